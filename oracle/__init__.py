@@ -1,0 +1,6 @@
+"""CPU oracle (test infrastructure only; see kvc_oracle's header)."""
+from .kvc_oracle import (  # noqa: F401
+    bf16_to_f64, default_scale, group_logits, normalizers, scores, maxpool,
+    mandatory, select_head, select, gather, inverse_stability_budgets,
+    compress_layer, LayerResult,
+)
