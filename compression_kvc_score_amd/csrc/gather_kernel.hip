@@ -1,0 +1,40 @@
+// Gather of the retained cache (TideKV, Fig. 2 caption): the selected K and V
+// rows copied bit for bit into dense head-major blocks, and their absolute
+// positions. One thread moves one 16-byte chunk of K and the same chunk of V;
+// consecutive threads cover consecutive chunks of a row, so both the reads
+// (one contiguous row segment per key) and the writes are coalesced.
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+__global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
+  const int cpr = a.d / 8;  // 16-byte chunks per row
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.total_rows * cpr) return;
+  const int64_t row = t / cpr;
+  const int c = (int)(t % cpr);
+  int g = 0;
+  while (g + 1 < a.hkv && a.heads.offset[g + 1] <= row) ++g;
+  int64_t j = a.idx[row];
+  j = j < 0 ? 0 : (j >= a.s ? a.s - 1 : j);  // keep every read inside K and V
+  const uint4 kv = *reinterpret_cast<const uint4*>(a.k + j * a.k_tok + (int64_t)g * a.k_head + c * 8);
+  const uint4 vv = *reinterpret_cast<const uint4*>(a.v + j * a.v_tok + (int64_t)g * a.v_head + c * 8);
+  *reinterpret_cast<uint4*>(a.k_out + row * a.d + c * 8) = kv;
+  *reinterpret_cast<uint4*>(a.v_out + row * a.d + c * 8) = vv;
+  if (c == 0) a.pos_out[row] = (int32_t)(a.pos_offset + j);
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
+  if (a.total_rows == 0) return hipSuccess;
+  GatherArgs args = a;
+  void* kargs[] = {&args};
+  const int64_t threads = a.total_rows * (a.d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gather_kernel), grid, dim3(256), kargs, 0, st);
+}
+
+}  // namespace kvc

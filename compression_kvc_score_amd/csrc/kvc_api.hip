@@ -1,0 +1,447 @@
+// Host side of the C ABI: argument validation, workspace layout, launch
+// sequencing and error reporting. Nothing here touches device memory; every
+// check runs before the first launch of a call.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(kvc_strerror(status)) + ": " + buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int64_t kInt32Max = 2147483647LL;
+constexpr int64_t kMaxPrompt = 1LL << 30;  // keeps every 32-bit key offset in the kernels exact
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workgroups the scans aim for across all KV heads (two per CU on a
+// 256-CU part). Overridable for tuning sweeps.
+int score_wg_target() {
+  static const int v = [] {
+    const char* e = std::getenv("KVC_SCORE_WGS");
+    const int x = e ? std::atoi(e) : 0;
+    return x > 0 ? x : 512;
+  }();
+  return v;
+}
+
+int normalize(const kvc_layer_desc* d, Layer& L) {
+  if (d == nullptr) return fail(KVC_ERR_INVALID_ARG, "desc is NULL");
+  if (d->s < 1) return fail(KVC_ERR_INVALID_ARG, "s=%lld must be >= 1", (long long)d->s);
+  if (d->s > kMaxPrompt) return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^30", (long long)d->s);
+  if (d->w < 1 || d->w > d->s) return fail(KVC_ERR_INVALID_ARG, "w=%d outside [1, s]", d->w);
+  if (d->hq < 1 || d->hkv < 1) return fail(KVC_ERR_INVALID_ARG, "hq=%d hkv=%d must be >= 1", d->hq, d->hkv);
+  if (d->hkv > KVC_MAX_KV_HEADS) return fail(KVC_ERR_UNSUPPORTED, "hkv=%d > %d", d->hkv, KVC_MAX_KV_HEADS);
+  if (d->hq % d->hkv != 0) return fail(KVC_ERR_INVALID_ARG, "hq=%d not a multiple of hkv=%d", d->hq, d->hkv);
+  if (d->d < 1) return fail(KVC_ERR_INVALID_ARG, "d=%d must be >= 1", d->d);
+  if (d->d != 64 && d->d != 128) return fail(KVC_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", d->d);
+  if (d->block < 1) return fail(KVC_ERR_INVALID_ARG, "block=%d must be >= 1", d->block);
+  if (d->block % kKeyTile != 0 || d->block > 512)
+    return fail(KVC_ERR_UNSUPPORTED, "block=%d (supported: multiples of 32 up to 512)", d->block);
+  const int64_t g = d->hq / d->hkv;
+  if (g * d->w > KVC_MAX_ROWS)
+    return fail(KVC_ERR_UNSUPPORTED, "(hq/hkv)*w=%lld > %d query rows per KV head", (long long)(g * d->w), KVC_MAX_ROWS);
+  if (std::isnan(d->scale) || std::isinf(d->scale)) return fail(KVC_ERR_INVALID_ARG, "scale is not finite");
+  if (d->n_sink < 0 || d->n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink/n_recent must be >= 0");
+  if (d->pool < 1 || d->pool % 2 == 0) return fail(KVC_ERR_INVALID_ARG, "pool=%d must be odd and >= 1", d->pool);
+  if (d->pool > KVC_MAX_POOL) return fail(KVC_ERR_UNSUPPORTED, "pool=%d > %d", d->pool, KVC_MAX_POOL);
+  if (d->pos_offset < 0 || d->pos_offset + d->s > kInt32Max)
+    return fail(KVC_ERR_INVALID_ARG, "pos_offset=%lld: positions must fit in int32", (long long)d->pos_offset);
+
+  const int64_t strides[6] = {d->q_tok_stride, d->q_head_stride, d->k_tok_stride,
+                              d->k_head_stride, d->v_tok_stride, d->v_head_stride};
+  for (int i = 0; i < 6; ++i) {
+    if (strides[i] < 0) return fail(KVC_ERR_INVALID_ARG, "negative stride");
+    if (strides[i] % 8 != 0) return fail(KVC_ERR_ALIGN, "stride %lld is not a multiple of 8 elements", (long long)strides[i]);
+  }
+
+  L.s = d->s;
+  L.w = d->w;
+  L.hq = d->hq;
+  L.hkv = d->hkv;
+  L.d = d->d;
+  L.g = (int)g;
+  L.block = d->block;
+  L.rows = (int)(g * d->w);
+  L.row_tiles = (L.rows + kRowTile - 1) / kRowTile;
+  L.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->d));
+  L.n_sink = d->n_sink;
+  L.n_recent = d->n_recent;
+  L.pool = d->pool;
+  L.pos_offset = d->pos_offset;
+  L.q_tok = d->q_tok_stride ? d->q_tok_stride : (int64_t)d->hq * d->d;
+  L.q_head = d->q_head_stride ? d->q_head_stride : d->d;
+  L.k_tok = d->k_tok_stride ? d->k_tok_stride : (int64_t)d->hkv * d->d;
+  L.k_head = d->k_head_stride ? d->k_head_stride : d->d;
+  L.v_tok = d->v_tok_stride ? d->v_tok_stride : (int64_t)d->hkv * d->d;
+  L.v_head = d->v_head_stride ? d->v_head_stride : d->d;
+
+  // Partition the key blocks of each head over at most kMaxSplit workgroups.
+  L.n_blocks = (int)((L.s + L.block - 1) / L.block);
+  const int64_t min_bpw = (L.n_blocks + kMaxSplit - 1) / kMaxSplit;
+  const int64_t want_bpw = ((int64_t)L.n_blocks * L.hkv + score_wg_target() - 1) / score_wg_target();
+  L.blocks_per_wg = (int)std::max<int64_t>(1, std::max(min_bpw, want_bpw));
+  L.n_split = (L.n_blocks + L.blocks_per_wg - 1) / L.blocks_per_wg;
+  return KVC_OK;
+}
+
+int64_t mandatory_count(int64_t s, int n_sink, int n_recent) {
+  const int64_t sink_end = std::min<int64_t>(n_sink, s);
+  const int64_t rec_begin = std::max<int64_t>(s - n_recent, sink_end);
+  return sink_end + (s - rec_begin);
+}
+
+int head_table(const Layer& L, const int32_t* budgets, HeadTable& t) {
+  if (budgets == nullptr) return fail(KVC_ERR_INVALID_ARG, "budgets is NULL");
+  const int64_t n_mand = mandatory_count(L.s, L.n_sink, L.n_recent);
+  std::memset(&t, 0, sizeof t);
+  int64_t off = 0;
+  for (int g = 0; g < L.hkv; ++g) {
+    const int64_t b = budgets[g];
+    if (b < 0) return fail(KVC_ERR_INVALID_ARG, "budgets[%d]=%lld < 0", g, (long long)b);
+    if (b < L.s && b < n_mand)
+      return fail(KVC_ERR_INVALID_ARG, "budgets[%d]=%lld below the %lld mandatory keys", g, (long long)b, (long long)n_mand);
+    t.budget[g] = (int32_t)b;
+    t.offset[g] = off;
+    off += std::min<int64_t>(b, L.s);
+  }
+  t.offset[L.hkv] = off;
+  return KVC_OK;
+}
+
+struct WsLayout {
+  size_t part, m, z, scores, pooled, total;
+};
+
+WsLayout ws_layout(const Layer& L) {
+  WsLayout w{};
+  size_t off = 0;
+  w.part = off;
+  off += align_up((size_t)L.hkv * kMaxSplit * L.row_tiles * kRowTile * sizeof(float2), 256);
+  w.m = off;
+  off += align_up((size_t)L.hq * L.w * sizeof(float), 256);
+  w.z = off;
+  off += align_up((size_t)L.hq * L.w * sizeof(float), 256);
+  w.scores = off;
+  off += align_up((size_t)L.hkv * L.s * sizeof(float), 256);
+  w.pooled = off;
+  if (L.pool > 1) off += align_up((size_t)L.hkv * L.s * sizeof(float), 256);
+  w.total = off;
+  return w;
+}
+
+int check_ws(const Layer& L, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_layout(L).total;
+  if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (ws_bytes < need) return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
+  return KVC_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (p == nullptr) return fail(KVC_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(KVC_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return KVC_OK;
+}
+
+#define KVC_TRY(x)                 \
+  do {                             \
+    const int _st = (x);           \
+    if (_st != KVC_OK) return _st; \
+  } while (0)
+
+// Device LDS limit per workgroup, cached per device.
+int check_lds(const Layer& L) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int lim = (dev >= 0 && dev < 64) ? __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) : 0;
+  if (lim == 0) {
+    e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], lim, __ATOMIC_RELAXED);
+  }
+  const size_t need = std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
+  if (need > (size_t)lim)
+    return fail(KVC_ERR_UNSUPPORTED, "scan needs %zu bytes of LDS, device allows %d", need, lim);
+  return KVC_OK;
+}
+
+ScoreArgs score_args(const Layer& L, const void* q, const void* k) {
+  ScoreArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.q_tok = L.q_tok;
+  a.q_head = L.q_head;
+  a.k_tok = L.k_tok;
+  a.k_head = L.k_head;
+  a.s = (int)L.s;
+  a.w = L.w;
+  a.g = L.g;
+  a.rows = L.rows;
+  a.block = L.block;
+  a.n_blocks = L.n_blocks;
+  a.blocks_per_wg = L.blocks_per_wg;
+  a.n_split = L.n_split;
+  a.scale = L.scale;
+  a.c = (float)((double)L.scale * 1.4426950408889634);
+  return a;
+}
+
+int run_pass1(const Layer& L, const void* q, const void* k, float* m_out, float* z_out,
+              void* ws, hipStream_t st) {
+  ScoreArgs a = score_args(L, q, k);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(L).part);
+  a.m_out = m_out;
+  a.z_out = z_out;
+  hipError_t e = launch_pass1(L, a, st);
+  if (e != hipSuccess) return hip_fail(e, "pass-1 launch");
+  e = launch_combine(L, a, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return KVC_OK;
+}
+
+int run_pass2(const Layer& L, const void* q, const void* k, const float* m, const float* z,
+              float* scores, hipStream_t st) {
+  ScoreArgs a = score_args(L, q, k);
+  a.m_in = m;
+  a.z_in = z;
+  a.scores = scores;
+  const hipError_t e = launch_pass2(L, a, st);
+  if (e != hipSuccess) return hip_fail(e, "pass-2 launch");
+  return KVC_OK;
+}
+
+int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
+               void* ws, hipStream_t st) {
+  const float* vals = scores;
+  if (L.pool > 1) {
+    PoolArgs p{};
+    p.in = scores;
+    p.out = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(L).pooled);
+    p.s = L.s;
+    p.total = (int64_t)L.hkv * L.s;
+    p.radius = L.pool / 2;
+    const hipError_t e = launch_pool(p, st);
+    if (e != hipSuccess) return hip_fail(e, "pool launch");
+    vals = p.out;
+  }
+  SelectArgs a{};
+  a.vals = vals;
+  a.idx_out = idx_out;
+  a.s = L.s;
+  a.n_sink = L.n_sink;
+  a.n_recent = L.n_recent;
+  a.heads = ht;
+  const hipError_t e = launch_select(L, a, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return KVC_OK;
+}
+
+int run_gather(const Layer& L, const void* k, const void* v, const int32_t* idx,
+               const HeadTable& ht, void* k_out, void* v_out, int32_t* pos_out, hipStream_t st) {
+  GatherArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_tok = L.k_tok;
+  a.k_head = L.k_head;
+  a.v_tok = L.v_tok;
+  a.v_head = L.v_head;
+  a.idx = idx;
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  a.pos_out = pos_out;
+  a.total_rows = ht.offset[L.hkv];
+  a.s = L.s;
+  a.pos_offset = L.pos_offset;
+  a.hkv = L.hkv;
+  a.d = L.d;
+  a.heads = ht;
+  const hipError_t e = launch_gather(a, st);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_strerror(int status) {
+  switch (status) {
+    case KVC_OK: return "KVC_OK";
+    case KVC_ERR_INVALID_ARG: return "KVC_ERR_INVALID_ARG";
+    case KVC_ERR_UNSUPPORTED: return "KVC_ERR_UNSUPPORTED";
+    case KVC_ERR_WORKSPACE: return "KVC_ERR_WORKSPACE";
+    case KVC_ERR_ALIGN: return "KVC_ERR_ALIGN";
+    case KVC_ERR_HIP: return "KVC_ERR_HIP";
+    default: return "KVC_ERR_UNKNOWN";
+  }
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+size_t kvc_workspace_size(const kvc_layer_desc* desc) {
+  Layer L;
+  if (normalize(desc, L) != KVC_OK) return 0;
+  return ws_layout(L).total;
+}
+
+int kvc_retained_offsets(const kvc_layer_desc* desc, const int32_t* budgets, int64_t* offsets) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  if (offsets == nullptr) return fail(KVC_ERR_INVALID_ARG, "offsets is NULL");
+  HeadTable t;
+  KVC_TRY(head_table(L, budgets, t));
+  for (int g = 0; g <= L.hkv; ++g) offsets[g] = t.offset[g];
+  return KVC_OK;
+}
+
+int kvc_budgets_inverse_stability(const double* s_stable, int32_t hkv, int64_t total,
+                                  int32_t* budgets) {
+  if (s_stable == nullptr || budgets == nullptr) return fail(KVC_ERR_INVALID_ARG, "NULL array");
+  if (hkv < 1) return fail(KVC_ERR_INVALID_ARG, "hkv=%d must be >= 1", hkv);
+  if (total < 0 || total > kInt32Max) return fail(KVC_ERR_INVALID_ARG, "total=%lld outside [0, 2^31-1]", (long long)total);
+  std::vector<double> w(hkv), frac(hkv);
+  std::vector<int64_t> base(hkv);
+  for (int h = 0; h < hkv; ++h) {
+    const double x = s_stable[h];
+    if (!(x > 0.0) || std::isinf(x)) return fail(KVC_ERR_INVALID_ARG, "s_stable[%d] must be finite and > 0", h);
+    w[h] = 1.0 / x;
+  }
+  double wsum = 0.0;
+  for (int h = 0; h < hkv; ++h) wsum += w[h];
+  int64_t used = 0;
+  for (int h = 0; h < hkv; ++h) {
+    const double exact = (double)total * w[h] / wsum;
+    base[h] = (int64_t)std::floor(exact);
+    frac[h] = exact - (double)base[h];
+    used += base[h];
+  }
+  std::vector<int> order(hkv);
+  for (int h = 0; h < hkv; ++h) order[h] = h;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return frac[a] > frac[b]; });
+  const int64_t rem = total - used;
+  for (int64_t r = 0; r < rem && r < hkv; ++r) base[order[r]] += 1;
+  for (int h = 0; h < hkv; ++h) budgets[h] = (int32_t)base[h];
+  return KVC_OK;
+}
+
+int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k, float* m_out,
+                    float* z_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(m_out, 4, "m_out"));
+  KVC_TRY(check_ptr(z_out, 4, "z_out"));
+  KVC_TRY(check_ws(L, ws, ws_bytes));
+  KVC_TRY(check_lds(L));
+  return run_pass1(L, q_win, k, m_out, z_out, ws, static_cast<hipStream_t>(stream));
+}
+
+int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k, const float* m,
+                    const float* z, float* scores, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(m, 4, "m"));
+  KVC_TRY(check_ptr(z, 4, "z"));
+  KVC_TRY(check_ptr(scores, 4, "scores"));
+  KVC_TRY(check_lds(L));
+  return run_pass2(L, q_win, k, m, z, scores, static_cast<hipStream_t>(stream));
+}
+
+int kvc_select_topk(const kvc_layer_desc* desc, const float* scores, const int32_t* budgets,
+                    int32_t* idx_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(scores, 4, "scores"));
+  KVC_TRY(check_ptr(idx_out, 4, "idx_out"));
+  HeadTable ht;
+  KVC_TRY(head_table(L, budgets, ht));
+  KVC_TRY(check_ws(L, ws, ws_bytes));
+  return run_select(L, scores, ht, idx_out, ws, static_cast<hipStream_t>(stream));
+}
+
+int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* budgets, void* k_out, void* v_out,
+                        int32_t* pos_out, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(v, 16, "v"));
+  KVC_TRY(check_ptr(idx, 4, "idx"));
+  KVC_TRY(check_ptr(k_out, 16, "k_out"));
+  KVC_TRY(check_ptr(v_out, 16, "v_out"));
+  KVC_TRY(check_ptr(pos_out, 4, "pos_out"));
+  HeadTable ht;
+  KVC_TRY(head_table(L, budgets, ht));
+  return run_gather(L, k, v, idx, ht, k_out, v_out, pos_out, static_cast<hipStream_t>(stream));
+}
+
+int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void* k, const void* v,
+                       const int32_t* budgets, float* m_out, float* z_out, float* scores_out,
+                       int32_t* idx_out, void* k_out, void* v_out, int32_t* pos_out, void* ws,
+                       size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(v, 16, "v"));
+  KVC_TRY(check_ptr(idx_out, 4, "idx_out"));
+  KVC_TRY(check_ptr(k_out, 16, "k_out"));
+  KVC_TRY(check_ptr(v_out, 16, "v_out"));
+  KVC_TRY(check_ptr(pos_out, 4, "pos_out"));
+  if (m_out) KVC_TRY(check_ptr(m_out, 4, "m_out"));
+  if (z_out) KVC_TRY(check_ptr(z_out, 4, "z_out"));
+  if (scores_out) KVC_TRY(check_ptr(scores_out, 4, "scores_out"));
+  HeadTable ht;
+  KVC_TRY(head_table(L, budgets, ht));
+  KVC_TRY(check_ws(L, ws, ws_bytes));
+  KVC_TRY(check_lds(L));
+
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
+  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
+  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, st));
+  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, st));
+  KVC_TRY(run_select(L, sc, ht, idx_out, ws, st));
+  KVC_TRY(run_gather(L, k, v, idx_out, ht, k_out, v_out, pos_out, st));
+  return KVC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal types shared by the host API and the gfx950 kernels of libkvc.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kKeyTile = 32;     // keys per wave per block (one 32x32 MFMA tile)
+constexpr int kRowTile = 32;     // query rows per MFMA tile
+constexpr int kMaxSplit = 128;   // max workgroups per KV head in the scans
+constexpr int kMaxRowTiles = KVC_MAX_ROWS / kRowTile;
+constexpr int kSelectThreads = 1024;
+
+// Descriptor after validation, with defaults resolved.
+struct Layer {
+  int64_t s;
+  int w, hq, hkv, d, g, block;
+  int rows;        // g * w query rows per KV head, ordered (head-in-group, window index)
+  int row_tiles;   // ceil(rows / 32)
+  float scale;
+  int n_sink, n_recent, pool;
+  int64_t pos_offset;
+  int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
+  int n_blocks;       // ceil(s / block)
+  int blocks_per_wg;  // consecutive key blocks scanned by one workgroup
+  int n_split;        // workgroups per KV head
+};
+
+// Arguments of the two scans and the split combine (passed by value).
+struct ScoreArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_tok, q_head, k_tok, k_head;
+  int s, w, g, rows;
+  int block;        // keys per block (a multiple of 32 * wavefronts per workgroup)
+  int n_blocks, blocks_per_wg, n_split;
+  float c;          // scale * log2(e): raw dot products to base-2 logits
+  float scale;
+  float* part;      // [hkv][n_split][row_tiles * 32] x (m_raw, z) split partials
+  const float* m_in;  // [hq][w] natural-log row max (pass 2 input)
+  const float* z_in;  // [hq][w]
+  float* m_out;     // [hq][w]
+  float* z_out;     // [hq][w]
+  float* scores;    // [hkv][s]
+};
+
+struct HeadTable {
+  int32_t budget[KVC_MAX_KV_HEADS];
+  int64_t offset[KVC_MAX_KV_HEADS + 1];  // packed row offsets of the retained outputs
+};
+
+struct PoolArgs {
+  const float* in;
+  float* out;
+  int64_t s;
+  int64_t total;  // hkv * s
+  int radius;
+};
+
+struct SelectArgs {
+  const float* vals;  // [hkv][s] ranking values (scores or pooled scores)
+  int32_t* idx_out;
+  int64_t s;
+  int n_sink, n_recent;
+  HeadTable heads;
+};
+
+struct GatherArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_tok, k_head, v_tok, v_head;
+  const int32_t* idx;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int32_t* pos_out;
+  int64_t total_rows;
+  int64_t s;
+  int64_t pos_offset;
+  int hkv, d;
+  HeadTable heads;
+};
+
+// Launchers (kernels in the .hip files). Each returns the launch status.
+hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_combine(const Layer& L, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
+hipError_t launch_select(const Layer& L, const SelectArgs& a, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
+// Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;
+// larger blocks give each wavefront block / 256 tiles per block.
+constexpr int kMaxScanWaves = 8;
+inline int scan_waves(const Layer& L) {
+  const int t = L.block / kKeyTile;
+  return t < kMaxScanWaves ? t : kMaxScanWaves;
+}
+
+// Dynamic LDS bytes of the scans.
+size_t pass1_lds_bytes(const Layer& L);
+size_t pass2_lds_bytes(const Layer& L);
+
+}  // namespace kvc

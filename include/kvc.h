@@ -1,0 +1,216 @@
+/*
+ * kvc.h -- C ABI of the layer-end KV-eviction compressor for AMD MI355X (gfx950).
+ *
+ * One call compresses one Transformer layer's full-prompt KV cache into a
+ * retained cache, as TideKV does at each layer boundary (TideKV, Fig. 2
+ * caption: layer-major delayed eviction; Fig. 3 caption: memory-controlled
+ * two-pass blockwise scoring). With grouped-query attention (G = hq / hkv
+ * query heads per KV head, query head h reads KV head h / G):
+ *
+ *   pass 1  the last W prompt queries (positions S-W .. S-1, causal) scan the
+ *           S prefix keys block by block and build per-query log-sum-exp
+ *           normalisers (m, Z): m = max_j l_j, Z = sum_j exp(l_j - m), with
+ *           logits l_j = scale * <q, k_j> (natural-log units);
+ *   pass 2  a second scan forms the normalised weights exp(l_j - m) / Z and
+ *           sums them over the W window queries and the G query heads of each
+ *           KV head into one score per (KV head, key);
+ *   select  per KV head, the mandatory keys -- the first n_sink and the last
+ *           n_recent -- plus the K_h - |mandatory| best other keys by
+ *           (score descending, index ascending), listed in ascending order;
+ *           an optional centred max-pool of odd width over the scores is
+ *           applied before ranking;
+ *   gather  the retained K and V rows, copied bit for bit, and their absolute
+ *           positions pos_offset + index.
+ *
+ * Per-head budgets K_h may differ (HeteroCache summary, Methodology, Phase 2:
+ * budgets weighted by inverse head stability); kvc_budgets_inverse_stability
+ * computes them.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are bf16 (passed as pointers to 16-bit patterns) or fp32/int32.
+ *    Default layouts: Q_win [W][hq][D], K and V [S][hkv][D]; D is contiguous
+ *    and other strides are given in elements in kvc_layer_desc.
+ *  - Device pointers must point to memory on the current HIP device; all work
+ *    is enqueued asynchronously on `stream` (a hipStream_t, 0 = null stream).
+ *    No entry point synchronises the host or allocates device memory; the
+ *    caller owns every buffer, including the workspace `ws`.
+ *  - Every argument is validated on the host before anything is enqueued: a
+ *    call that fails validation has enqueued nothing and written nothing. A
+ *    KVC_ERR_HIP failure of a later launch may leave earlier launches of the
+ *    same call enqueued.
+ *  - Inputs must be finite. Results are deterministic: the same inputs and
+ *    descriptor give bitwise-identical outputs.
+ *  - Functions are thread-safe; calls that share output or workspace buffers
+ *    must be ordered by the caller (same stream or events).
+ *  - Status codes are the kvc_status values; kvc_strerror names them and
+ *    kvc_last_error returns a message about the calling thread's last failure.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+#define KVC_MAX_KV_HEADS 64    /* hkv limit */
+#define KVC_MAX_ROWS 256       /* limit on G * W (query rows per KV head) */
+#define KVC_MAX_POOL 31        /* largest max-pool width */
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = -1,  /* null pointer, bad size, budget below the mandatory set, ... */
+  KVC_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels implement (D, block, G*W) */
+  KVC_ERR_WORKSPACE = -3,    /* workspace null or smaller than kvc_workspace_size() */
+  KVC_ERR_ALIGN = -4,        /* pointer or stride not 16-byte aligned */
+  KVC_ERR_HIP = -5           /* the HIP runtime reported an error (message in kvc_last_error) */
+} kvc_status;
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
+typedef void* kvc_stream_t;
+
+/*
+ * Shape and options of one layer's compression.
+ *  s            prompt length = number of keys scored, 1 <= s <= 2^30
+ *  w            observation window: the last w prompt queries, 1 <= w <= s
+ *  hq, hkv      query and KV heads, hq % hkv == 0, 1 <= hkv <= KVC_MAX_KV_HEADS,
+ *               (hq / hkv) * w <= KVC_MAX_ROWS
+ *  d            head dimension: 64 or 128
+ *  block        key block size b_s of the blockwise scan: a multiple of 32 in
+ *               [32, 512]; results do not depend on it beyond fp32 rounding
+ *  scale        logit scale; a value <= 0 selects 1 / sqrt(d)
+ *  n_sink       mandatory leading keys, >= 0
+ *  n_recent     mandatory trailing keys, >= 0
+ *  pool         odd max-pool width over scores before selection, 1 = none,
+ *               <= KVC_MAX_POOL; the window is truncated at both ends
+ *  pos_offset   added to retained key indices to form positions;
+ *               0 <= pos_offset and pos_offset + s <= 2^31 - 1
+ *  *_tok_stride, *_head_stride
+ *               element strides between tokens and between heads of Q_win, K
+ *               and V; 0 selects the default dense layout; non-zero strides
+ *               must be multiples of 8 elements (16 bytes)
+ */
+typedef struct kvc_layer_desc {
+  int64_t s;
+  int32_t w;
+  int32_t hq;
+  int32_t hkv;
+  int32_t d;
+  int32_t block;
+  float scale;
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t pool;
+  int32_t reserved0;
+  int64_t pos_offset;
+  int64_t q_tok_stride, q_head_stride;
+  int64_t k_tok_stride, k_head_stride;
+  int64_t v_tok_stride, v_head_stride;
+} kvc_layer_desc;
+
+/* KVC_ABI_VERSION of the built library. */
+int kvc_version(void);
+
+/* Static name of a status code ("KVC_OK", ...); never NULL. */
+const char* kvc_strerror(int status);
+
+/* Message about the calling thread's most recent failed call ("" if none).
+ * The pointer stays valid until the thread's next failing call. */
+const char* kvc_last_error(void);
+
+/*
+ * Workspace bytes that every entry point below accepts for this descriptor
+ * (the largest need, reached by kvc_compress_layer with all optional outputs
+ * NULL). Pure host function. Apart from the fp32 score and pooled-score
+ * vectors (4 * hkv * s bytes each), it does not grow with s, following the
+ * S-independent temporary bound of TideKV's Fig. 3 caption.
+ * Returns 0 if the descriptor is invalid.
+ */
+size_t kvc_workspace_size(const kvc_layer_desc* desc);
+
+/*
+ * Rows retained per KV head: min(budgets[g], s). Writes the exclusive prefix
+ * sums to offsets[0 .. hkv] (host array of hkv + 1 entries), so head g's rows
+ * in the packed outputs are [offsets[g], offsets[g + 1]). Validates budgets
+ * like kvc_select_topk. Pure host function.
+ */
+int kvc_retained_offsets(const kvc_layer_desc* desc, const int32_t* budgets, int64_t* offsets);
+
+/*
+ * Heterogeneous budgets (HeteroCache summary, Methodology, Phase 2): weight
+ * w_g = 1 / s_stable[g]; budgets[g] = floor(total * w_g / sum w) and the
+ * remaining total - sum floor slots go one each to the heads with the largest
+ * fractional parts, lower head index first among equals. Sums run in head
+ * order, in double precision. s_stable: host array of hkv finite values > 0;
+ * budgets: host output of hkv entries; 0 <= total <= 2^31 - 1. Pure host.
+ */
+int kvc_budgets_inverse_stability(const double* s_stable, int32_t hkv, int64_t total,
+                                  int32_t* budgets);
+
+/*
+ * Pass 1 (TideKV, Fig. 3 caption: first scan, stable log-sum-exp normalisers).
+ *  q_win  device, bf16 [W][hq][D] (strided)       k  device, bf16 [S][hkv][D]
+ *  m_out, z_out  device, fp32 [hq][W]: row max of the scaled logits (natural
+ *         units) and sum_j exp(l_j - m) for query head h, window query i
+ *  ws     device workspace of ws_bytes >= kvc_workspace_size(desc)
+ */
+int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k,
+                    float* m_out, float* z_out, void* ws, size_t ws_bytes,
+                    kvc_stream_t stream);
+
+/*
+ * Pass 2 (TideKV, Fig. 3 caption: second scan, normalised weights pooled per
+ * key). m, z as written by kvc_score_pass1. scores: device fp32 [hkv][S],
+ * scores[g][j] = sum over window queries i and query heads h of group g of
+ * exp(l - m[h][i]) / z[h][i] (0 where key j is after query i). Each head's
+ * scores sum to W * G up to rounding. Needs no workspace.
+ */
+int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k,
+                    const float* m, const float* z, float* scores,
+                    kvc_stream_t stream);
+
+/*
+ * Selection (TideKV, Fig. 3 caption: top K_l - |R_mand| non-mandatory keys
+ * plus the mandatory sink/recent set). scores: device fp32 [hkv][S], finite
+ * and >= 0 (as pass 2 writes them); if desc->pool > 1 ranking uses the
+ * max-pooled scores. budgets: HOST int32 [hkv]; each budgets[g] >= 0 and,
+ * when below s, at least the size of the mandatory set
+ * [0, n_sink) U [s - n_recent, s). idx_out: device int32, packed head-major
+ * at kvc_retained_offsets; each head's indices ascending.
+ */
+int kvc_select_topk(const kvc_layer_desc* desc, const float* scores, const int32_t* budgets,
+                    int32_t* idx_out, void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * Gather (TideKV, Fig. 2 caption: retained KV and absolute positions).
+ * idx: device int32 packed as kvc_select_topk writes it, entries in [0, s)
+ * (the device clamps out-of-range entries into [0, s) so reads stay inside K
+ * and V; such rows are not meaningful). budgets: HOST int32 [hkv] as given to
+ * the selection. k_out, v_out: device bf16 [rows][D] dense, rows packed as
+ * idx; pos_out: device int32 [rows] = pos_offset + idx.
+ */
+int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* budgets,
+                        void* k_out, void* v_out, int32_t* pos_out,
+                        kvc_stream_t stream);
+
+/*
+ * The whole layer: pass 1, pass 2, (pool), select, gather, enqueued in that
+ * order on one stream. m_out, z_out, scores_out and idx_out may be NULL (they
+ * then live in the workspace); k_out, v_out and pos_out are required.
+ * Results equal those of the four staged calls bit for bit.
+ */
+int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void* k,
+                       const void* v, const int32_t* budgets,
+                       float* m_out, float* z_out, float* scores_out, int32_t* idx_out,
+                       void* k_out, void* v_out, int32_t* pos_out,
+                       void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

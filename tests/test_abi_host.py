@@ -1,0 +1,168 @@
+"""Host side of the C ABI (no GPU needed): the library loads and exports every
+declared symbol, descriptors and budgets are validated before any launch,
+the workspace bound, and the heterogeneous-budget host function against the
+oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compression_kvc_score_amd as kvc
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvc.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kvc.h but not exported"
+    assert kvc.kvc_version() == 1
+
+
+def test_strerror_names():
+    assert kvc.kvc_strerror(0) == "KVC_OK"
+    assert kvc.kvc_strerror(-3) == "KVC_ERR_WORKSPACE"
+    assert kvc.kvc_strerror(12345) == "KVC_ERR_UNKNOWN"
+
+
+def base_desc(**kw):
+    args = dict(s=4096, w=32, hq=32, hkv=8, d=128, block=256, n_sink=4, n_recent=32)
+    args.update(kw)
+    return kvc.make_desc(**args)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("s", 0, kvc.KVC_ERR_INVALID_ARG),
+    ("w", 0, kvc.KVC_ERR_INVALID_ARG),
+    ("w", 5000, kvc.KVC_ERR_INVALID_ARG),
+    ("hq", 30, kvc.KVC_ERR_INVALID_ARG),
+    ("hkv", 0, kvc.KVC_ERR_INVALID_ARG),
+    ("hkv", 65, kvc.KVC_ERR_UNSUPPORTED),
+    ("d", 96, kvc.KVC_ERR_UNSUPPORTED),
+    ("d", 0, kvc.KVC_ERR_INVALID_ARG),
+    ("block", 48, kvc.KVC_ERR_UNSUPPORTED),
+    ("block", 1024, kvc.KVC_ERR_UNSUPPORTED),
+    ("block", 0, kvc.KVC_ERR_INVALID_ARG),
+    ("w", 65, kvc.KVC_ERR_UNSUPPORTED),       # G * W = 260 > 256 rows
+    ("n_sink", -1, kvc.KVC_ERR_INVALID_ARG),
+    ("pool", 4, kvc.KVC_ERR_INVALID_ARG),
+    ("pool", 33, kvc.KVC_ERR_UNSUPPORTED),
+    ("pos_offset", 2**31 - 100, kvc.KVC_ERR_INVALID_ARG),
+    ("scale", float("nan"), kvc.KVC_ERR_INVALID_ARG),
+    ("k_tok_stride", 1028, kvc.KVC_ERR_ALIGN),
+    ("q_head_stride", -8, kvc.KVC_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(field, value, status):
+    d = base_desc()
+    setattr(d, field, value)
+    lib = kvc.lib()
+    assert lib.kvc_workspace_size(ctypes.byref(d)) == 0
+    off = np.zeros(d.hkv + 1 if 0 < d.hkv <= 64 else 66, dtype=np.int64)
+    b = np.full(max(d.hkv, 1), 100, dtype=np.int32)
+    st = lib.kvc_retained_offsets(ctypes.byref(d), b.ctypes.data_as(ctypes.c_void_p),
+                                  off.ctypes.data_as(ctypes.c_void_p))
+    assert st == status, (st, lib.kvc_last_error())
+
+
+def test_budget_validation_and_offsets():
+    d = base_desc()
+    off = kvc.kvc_retained_offsets(d, [4096] * 8)
+    assert list(off) == [4096 * g for g in range(9)]
+    # a budget of at least S keeps S rows
+    off = kvc.kvc_retained_offsets(d, [5000] + [36] * 7)
+    assert off[1] == 4096 and off[-1] == 4096 + 7 * 36
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_retained_offsets(d, [35] + [100] * 7)  # below the 36 mandatory keys
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_retained_offsets(d, [-1] + [100] * 7)
+    # overlapping sink/recent ranges count once
+    d2 = base_desc(s=40, w=8, n_sink=30, n_recent=30)
+    assert kvc.kvc_retained_offsets(d2, [40] * 8)[-1] == 320
+
+
+def test_workspace_grows_only_with_the_score_vectors():
+    """Temporary memory independent of S apart from the fp32 score vector (and
+    the pooled copy when pooling), as the blockwise scan requires."""
+    for pool, nvec in [(1, 1), (7, 2)]:
+        sizes = []
+        for s in [4096, 16384, 65536, 131072]:
+            d = base_desc(s=s, pool=pool)
+            sizes.append(kvc.kvc_workspace_size(d) - nvec * 4 * 8 * s)
+        assert len(set(sizes)) == 1, sizes
+        assert sizes[0] < 4 << 20  # the S-independent part stays a few MiB
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_device_entry_points_reject_bad_arguments_before_launch():
+    """Every check precedes the first HIP call, so these run without a GPU."""
+    lib = kvc.lib()
+    d = base_desc()
+    ws_n = kvc.kvc_workspace_size(d)
+    P = _fake(0x10000)
+    b = np.full(8, 4096, dtype=np.int32)
+    bp = b.ctypes.data_as(ctypes.c_void_p)
+    dd = ctypes.byref(d)
+    S = kvc
+    # pass 1
+    assert lib.kvc_score_pass1(dd, None, P, P, P, P, ws_n, None) == S.KVC_ERR_INVALID_ARG
+    assert lib.kvc_score_pass1(dd, _fake(0x10008), P, P, P, P, ws_n, None) == S.KVC_ERR_ALIGN
+    assert lib.kvc_score_pass1(dd, P, P, P, P, P, ws_n - 1, None) == S.KVC_ERR_WORKSPACE
+    assert lib.kvc_score_pass1(dd, P, P, P, P, None, ws_n, None) == S.KVC_ERR_WORKSPACE
+    assert lib.kvc_score_pass1(dd, P, P, P, P, _fake(0x10010), ws_n, None) == S.KVC_ERR_ALIGN
+    assert lib.kvc_score_pass1(None, P, P, P, P, P, ws_n, None) == S.KVC_ERR_INVALID_ARG
+    # pass 2
+    assert lib.kvc_score_pass2(dd, P, P, P, P, None, None) == S.KVC_ERR_INVALID_ARG
+    assert lib.kvc_score_pass2(dd, P, P, _fake(0x10002), P, P, None) == S.KVC_ERR_ALIGN
+    # select
+    assert lib.kvc_select_topk(dd, P, None, P, P, ws_n, None) == S.KVC_ERR_INVALID_ARG
+    bad = np.full(8, 10, dtype=np.int32)
+    assert lib.kvc_select_topk(dd, P, bad.ctypes.data_as(ctypes.c_void_p), P, P, ws_n, None) == S.KVC_ERR_INVALID_ARG
+    assert lib.kvc_select_topk(dd, P, bp, P, P, 0, None) == S.KVC_ERR_WORKSPACE
+    # gather
+    assert lib.kvc_gather_retained(dd, P, P, P, bp, P, _fake(0x10004), P, None) == S.KVC_ERR_ALIGN
+    assert lib.kvc_gather_retained(dd, P, P, None, bp, P, P, P, None) == S.KVC_ERR_INVALID_ARG
+    # whole layer: idx/k_out/v_out/pos_out required, intermediates optional
+    args = [dd, P, P, P, bp, None, None, None, P, P, P, P, P, ws_n, None]
+    a2 = list(args); a2[8] = None
+    assert lib.kvc_compress_layer(*a2) == S.KVC_ERR_INVALID_ARG
+    a3 = list(args); a3[11] = None
+    assert lib.kvc_compress_layer(*a3) == S.KVC_ERR_INVALID_ARG
+    a4 = list(args); a4[13] = ws_n - 256
+    assert lib.kvc_compress_layer(*a4) == S.KVC_ERR_WORKSPACE
+    msg = lib.kvc_last_error().decode()
+    assert msg.startswith("KVC_ERR_WORKSPACE")
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_budgets_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.integers(1, 17))
+    st = rng.uniform(0.2, 0.9, size=hkv)
+    total = int(rng.integers(0, 100000))
+    got = kvc.kvc_budgets_inverse_stability(st, total)
+    want = oracle.inverse_stability_budgets(st, total)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_budgets_ties_and_errors():
+    np.testing.assert_array_equal(kvc.kvc_budgets_inverse_stability([0.3] * 3, 10), [4, 3, 3])
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_budgets_inverse_stability([0.5, 0.0], 10)
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_budgets_inverse_stability([0.5, float("inf")], 10)
