@@ -8,7 +8,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kvc_internal.h"
@@ -35,7 +37,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647LL;
-constexpr int64_t kMaxPrompt = 1LL << 30;  // keeps every 32-bit key offset in the kernels exact
+constexpr int64_t kMaxPrompt = 1LL << 25;  // bounds the selection's per-chunk tables in LDS
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -55,7 +57,7 @@ int score_wg_target() {
 int normalize(const kvc_layer_desc* d, Layer& L) {
   if (d == nullptr) return fail(KVC_ERR_INVALID_ARG, "desc is NULL");
   if (d->s < 1) return fail(KVC_ERR_INVALID_ARG, "s=%lld must be >= 1", (long long)d->s);
-  if (d->s > kMaxPrompt) return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^30", (long long)d->s);
+  if (d->s > kMaxPrompt) return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^25", (long long)d->s);
   if (d->w < 1 || d->w > d->s) return fail(KVC_ERR_INVALID_ARG, "w=%d outside [1, s]", d->w);
   if (d->hq < 1 || d->hkv < 1) return fail(KVC_ERR_INVALID_ARG, "hq=%d hkv=%d must be >= 1", d->hq, d->hkv);
   if (d->hkv > KVC_MAX_KV_HEADS) return fail(KVC_ERR_UNSUPPORTED, "hkv=%d > %d", d->hkv, KVC_MAX_KV_HEADS);
@@ -136,13 +138,30 @@ int head_table(const Layer& L, const int32_t* budgets, HeadTable& t) {
   return KVC_OK;
 }
 
+int n_chunks(const Layer& L) { return (int)((L.s + kSelectChunk - 1) / kSelectChunk); }
+
 struct WsLayout {
-  size_t part, m, z, scores, pooled, total;
+  size_t part, m, z, scores, pooled;
+  size_t hist, cand_count, cand, chunk_above, chunk_range, head_out;
+  size_t total;
 };
 
 WsLayout ws_layout(const Layer& L) {
   WsLayout w{};
   size_t off = 0;
+  const size_t nc = (size_t)n_chunks(L);
+  w.hist = off;
+  off += align_up((size_t)L.hkv * kHistBins * 4, 256);
+  w.cand_count = off;
+  off += align_up((size_t)L.hkv * 4, 256);
+  w.cand = off;
+  off += align_up((size_t)L.hkv * kCandCap * 8, 256);
+  w.chunk_above = off;
+  off += align_up((size_t)L.hkv * nc * 4, 256);
+  w.chunk_range = off;
+  off += align_up((size_t)L.hkv * nc * 16, 256);
+  w.head_out = off;
+  off += align_up((size_t)L.hkv * sizeof(SelectHead), 256);
   w.part = off;
   off += align_up((size_t)L.hkv * kMaxSplit * L.row_tiles * kRowTile * sizeof(float2), 256);
   w.m = off;
@@ -189,9 +208,10 @@ int check_lds(const Layer& L) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], lim, __ATOMIC_RELAXED);
   }
-  const size_t need = std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
+  const size_t need = std::max(std::max(pass1_lds_bytes(L), pass2_lds_bytes(L)),
+                               resolve_lds_bytes(n_chunks(L)) + 8192);
   if (need > (size_t)lim)
-    return fail(KVC_ERR_UNSUPPORTED, "scan needs %zu bytes of LDS, device allows %d", need, lim);
+    return fail(KVC_ERR_UNSUPPORTED, "kernels need %zu bytes of LDS, device allows %d", need, lim);
   return KVC_OK;
 }
 
@@ -213,13 +233,23 @@ ScoreArgs score_args(const Layer& L, const void* q, const void* k) {
   a.n_split = L.n_split;
   a.scale = L.scale;
   a.c = (float)((double)L.scale * 1.4426950408889634);
+  const int64_t sink_end = std::min<int64_t>(L.n_sink, L.s);
+  a.sink_end = (int)sink_end;
+  a.rec_begin = (int)std::max<int64_t>(L.s - L.n_recent, sink_end);
   return a;
 }
 
+// with_hist: also clear the selection histogram that pass 2 will fill.
 int run_pass1(const Layer& L, const void* q, const void* k, float* m_out, float* z_out,
-              void* ws, hipStream_t st) {
+              void* ws, bool with_hist, hipStream_t st) {
   ScoreArgs a = score_args(L, q, k);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(L).part);
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float*>(wsb + lay.part);
+  if (with_hist) {
+    a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+    a.cand_count = reinterpret_cast<uint32_t*>(wsb + lay.cand_count);
+  }
   a.m_out = m_out;
   a.z_out = z_out;
   hipError_t e = launch_pass1(L, a, st);
@@ -229,9 +259,11 @@ int run_pass1(const Layer& L, const void* q, const void* k, float* m_out, float*
   return KVC_OK;
 }
 
+// ws != nullptr: also build the selection histogram (cleared by pass 1).
 int run_pass2(const Layer& L, const void* q, const void* k, const float* m, const float* z,
-              float* scores, hipStream_t st) {
+              float* scores, void* ws, hipStream_t st) {
   ScoreArgs a = score_args(L, q, k);
+  if (ws != nullptr) a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + ws_layout(L).hist);
   a.m_in = m;
   a.z_in = z;
   a.scores = scores;
@@ -240,28 +272,30 @@ int run_pass2(const Layer& L, const void* q, const void* k, const float* m, cons
   return KVC_OK;
 }
 
+// need_hist: the selection clears and builds its own histogram (and pooled
+// values); otherwise pass 2 of the same call has built it.
 int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
-               void* ws, hipStream_t st) {
-  const float* vals = scores;
-  if (L.pool > 1) {
-    PoolArgs p{};
-    p.in = scores;
-    p.out = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_layout(L).pooled);
-    p.s = L.s;
-    p.total = (int64_t)L.hkv * L.s;
-    p.radius = L.pool / 2;
-    const hipError_t e = launch_pool(p, st);
-    if (e != hipSuccess) return hip_fail(e, "pool launch");
-    vals = p.out;
-  }
+               void* ws, bool need_hist, hipStream_t st) {
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
   SelectArgs a{};
-  a.vals = vals;
+  a.scores = scores;
+  a.pooled = L.pool > 1 ? reinterpret_cast<float*>(wsb + lay.pooled) : nullptr;
+  a.vals = L.pool > 1 ? a.pooled : scores;
+  a.pool_radius = L.pool / 2;
   a.idx_out = idx_out;
   a.s = L.s;
   a.n_sink = L.n_sink;
   a.n_recent = L.n_recent;
+  a.n_chunks = n_chunks(L);
+  a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+  a.cand_count = reinterpret_cast<uint32_t*>(wsb + lay.cand_count);
+  a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+  a.chunk_above = reinterpret_cast<uint32_t*>(wsb + lay.chunk_above);
+  a.chunk_range = reinterpret_cast<int64_t*>(wsb + lay.chunk_range);
+  a.head_out = reinterpret_cast<SelectHead*>(wsb + lay.head_out);
   a.heads = ht;
-  const hipError_t e = launch_select(L, a, st);
+  const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return KVC_OK;
 }
@@ -291,6 +325,22 @@ int run_gather(const Layer& L, const void* k, const void* v, const int32_t* idx,
 }
 
 }  // namespace
+
+namespace kvc {
+
+hipError_t ensure_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = done.find(fn);
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[fn] = bytes;
+  return e;
+}
+
+}  // namespace kvc
 
 extern "C" {
 
@@ -366,7 +416,7 @@ int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k
   KVC_TRY(check_ptr(z_out, 4, "z_out"));
   KVC_TRY(check_ws(L, ws, ws_bytes));
   KVC_TRY(check_lds(L));
-  return run_pass1(L, q_win, k, m_out, z_out, ws, static_cast<hipStream_t>(stream));
+  return run_pass1(L, q_win, k, m_out, z_out, ws, false, static_cast<hipStream_t>(stream));
 }
 
 int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k, const float* m,
@@ -379,7 +429,7 @@ int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k
   KVC_TRY(check_ptr(z, 4, "z"));
   KVC_TRY(check_ptr(scores, 4, "scores"));
   KVC_TRY(check_lds(L));
-  return run_pass2(L, q_win, k, m, z, scores, static_cast<hipStream_t>(stream));
+  return run_pass2(L, q_win, k, m, z, scores, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int kvc_select_topk(const kvc_layer_desc* desc, const float* scores, const int32_t* budgets,
@@ -391,7 +441,8 @@ int kvc_select_topk(const kvc_layer_desc* desc, const float* scores, const int32
   HeadTable ht;
   KVC_TRY(head_table(L, budgets, ht));
   KVC_TRY(check_ws(L, ws, ws_bytes));
-  return run_select(L, scores, ht, idx_out, ws, static_cast<hipStream_t>(stream));
+  KVC_TRY(check_lds(L));
+  return run_select(L, scores, ht, idx_out, ws, true, static_cast<hipStream_t>(stream));
 }
 
 int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v,
@@ -437,9 +488,11 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
   float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
   float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, st));
-  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, st));
-  KVC_TRY(run_select(L, sc, ht, idx_out, ws, st));
+  // pass 2 builds the selection histogram unless ranking uses pooled values
+  const bool hist_in_pass2 = L.pool == 1;
+  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
+  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
+  KVC_TRY(run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st));
   KVC_TRY(run_gather(L, k, v, idx_out, ht, k_out, v_out, pos_out, st));
   return KVC_OK;
 }

@@ -14,6 +14,9 @@ constexpr int kRowTile = 32;     // query rows per MFMA tile
 constexpr int kMaxSplit = 128;   // max workgroups per KV head in the scans
 constexpr int kMaxRowTiles = KVC_MAX_ROWS / kRowTile;
 constexpr int kSelectThreads = 1024;
+constexpr int kSelectChunk = 4 * kSelectThreads;  // keys per selection workgroup
+constexpr int kHistBins = 4096;   // top-bits histogram of candidate scores (bits 30..19)
+constexpr int kCandCap = 16384;   // listed candidates per head inside the threshold bin
 
 // Descriptor after validation, with defaults resolved.
 struct Layer {
@@ -46,6 +49,9 @@ struct ScoreArgs {
   float* m_out;     // [hq][w]
   float* z_out;     // [hq][w]
   float* scores;    // [hkv][s]
+  uint32_t* hist;   // [hkv][kHistBins]: pass 1 clears it, pass 2 fills it (null: skip)
+  uint32_t* cand_count;  // [hkv], cleared with hist
+  int sink_end, rec_begin;  // candidate keys [sink_end, rec_begin) for the histogram
 };
 
 struct HeadTable {
@@ -53,19 +59,26 @@ struct HeadTable {
   int64_t offset[KVC_MAX_KV_HEADS + 1];  // packed row offsets of the retained outputs
 };
 
-struct PoolArgs {
-  const float* in;
-  float* out;
-  int64_t s;
-  int64_t total;  // hkv * s
-  int radius;
+struct SelectHead {
+  uint32_t thr;      // bit pattern of the k-th best candidate value
+  uint32_t need_eq;  // candidates equal to thr that are kept (lowest indices)
 };
 
 struct SelectArgs {
-  const float* vals;  // [hkv][s] ranking values (scores or pooled scores)
+  const float* scores;   // [hkv][s] pass-2 scores
+  const float* vals;     // [hkv][s] ranking values (scores, or pooled scores)
+  float* pooled;         // pooled values written by the histogram pass (null: no pool)
+  int pool_radius;
   int32_t* idx_out;
   int64_t s;
   int n_sink, n_recent;
+  int n_chunks;          // ceil(s / kSelectChunk)
+  uint32_t* hist;        // [hkv][kHistBins]
+  uint32_t* cand_count;  // [hkv]
+  uint2* cand;           // [hkv][kCandCap] (value bits, key index)
+  uint32_t* chunk_above; // [hkv][n_chunks]
+  int64_t* chunk_range;  // [hkv][n_chunks][2]: output offset, equal-candidates before
+  SelectHead* head_out;  // [hkv]
   HeadTable heads;
 };
 
@@ -84,12 +97,17 @@ struct GatherArgs {
   HeadTable heads;
 };
 
+// Raise a kernel's dynamic-LDS limit to at least `bytes` (once per kernel).
+hipError_t ensure_lds(const void* fn, size_t bytes);
+
 // Launchers (kernels in the .hip files). Each returns the launch status.
 hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_combine(const Layer& L, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
-hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
-hipError_t launch_select(const Layer& L, const SelectArgs& a, hipStream_t st);
+// need_hist: clear and build the histogram (and pooled values) first;
+// otherwise pass 2 has built it.
+hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st);
+size_t resolve_lds_bytes(int n_chunks);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 
 // Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;

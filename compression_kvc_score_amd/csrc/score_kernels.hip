@@ -169,6 +169,12 @@ __global__ void __launch_bounds__(512) pass1_kernel(ScoreArgs a) {
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int head = work / a.n_split;
   const int split = work % a.n_split;
+  // The first workgroup of each head clears that head's selection histogram,
+  // which pass 2 fills after this kernel has finished.
+  if (a.hist != nullptr && split == 0) {
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) a.hist[(int64_t)head * kHistBins + i] = 0u;
+    if (threadIdx.x == 0) a.cand_count[head] = 0u;
+  }
   stage_queries<D>(a, head, ROWS_PAD, qs);
   __syncthreads();
 
@@ -267,7 +273,8 @@ __global__ void __launch_bounds__(256) combine_kernel(ScoreArgs a, int rows_pad)
 template <int D, int NRT, bool EDGE>
 __device__ __forceinline__ void pass2_tile(const ScoreArgs& a, const uint16_t* qs,
                                            const float* bias, const uint4 (&kf)[D / 16],
-                                           int kbase, int half, int l32, float* out) {
+                                           int kbase, int half, int l32, float* out,
+                                           uint32_t* lh) {
   constexpr int PITCH = D + 8;
   constexpr int NCH = D / 16;
   const int key = kbase + l32;
@@ -306,7 +313,11 @@ __device__ __forceinline__ void pass2_tile(const ScoreArgs& a, const uint16_t* q
   }
   float sum = s0 + s1;
   sum += __shfl_xor(sum, 32);
-  if (half == 0 && key < a.s) out[key] = sum;
+  if (half == 0 && key < a.s) {
+    out[key] = sum;
+    if (lh != nullptr && key >= a.sink_end && key < a.rec_begin)
+      atomicAdd(&lh[(__float_as_uint(sum) >> 19) & (kHistBins - 1)], 1u);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -320,6 +331,9 @@ __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
   constexpr int ROWS_PAD = NRT * kRowTile;
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
   float* bias = reinterpret_cast<float*>(smem + ROWS_PAD * PITCH * 2);
+  uint32_t* lh = a.hist != nullptr ? reinterpret_cast<uint32_t*>(bias + ROWS_PAD) : nullptr;
+  if (lh != nullptr)
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0u;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int head = work / a.n_split;
@@ -348,14 +362,20 @@ __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
   if (seq.clean > 0) load_key_frag<D>(a, head, seq.kbase(0) + l32, half, ka);
   for (int k = 0; k < seq.clean; k += 2) {
     if (k + 1 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 1) + l32, half, kb);
-    pass2_tile<D, NRT, false>(a, qs, bias, ka, seq.kbase(k), half, l32, out);
+    pass2_tile<D, NRT, false>(a, qs, bias, ka, seq.kbase(k), half, l32, out, lh);
     if (k + 1 >= seq.clean) break;
     if (k + 2 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 2) + l32, half, ka);
-    pass2_tile<D, NRT, false>(a, qs, bias, kb, seq.kbase(k + 1), half, l32, out);
+    pass2_tile<D, NRT, false>(a, qs, bias, kb, seq.kbase(k + 1), half, l32, out, lh);
   }
   for (int k = seq.clean; k < seq.n; ++k) {
     load_key_frag<D>(a, head, seq.kbase(k) + l32, half, ka);
-    pass2_tile<D, NRT, true>(a, qs, bias, ka, seq.kbase(k), half, l32, out);
+    pass2_tile<D, NRT, true>(a, qs, bias, ka, seq.kbase(k), half, l32, out, lh);
+  }
+  if (lh != nullptr) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (int64_t)head * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+      if (lh[i]) atomicAdd(&gh[i], lh[i]);
   }
 }
 
@@ -392,10 +412,8 @@ const void* pass2_fn(int nrt) {
 hipError_t launch_scan(const void* fn, const Layer& L, const ScoreArgs& a, size_t lds,
                        hipStream_t st) {
   if (fn == nullptr) return hipErrorInvalidValue;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = ensure_lds(fn, lds);
+  if (e != hipSuccess) return e;
   ScoreArgs args = a;
   void* kargs[] = {&args};
   const dim3 grid((unsigned)(L.hkv * L.n_split));
@@ -414,7 +432,7 @@ size_t pass1_lds_bytes(const Layer& L) {
 
 size_t pass2_lds_bytes(const Layer& L) {
   const size_t rows_pad = (size_t)L.row_tiles * kRowTile;
-  return rows_pad * (L.d + 8) * 2 + rows_pad * sizeof(float);
+  return rows_pad * (L.d + 8) * 2 + rows_pad * sizeof(float) + kHistBins * sizeof(uint32_t);
 }
 
 hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st) {

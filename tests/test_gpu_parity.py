@@ -197,6 +197,30 @@ def test_select_on_identical_values_is_exact(pool):
         np.testing.assert_array_equal(got[g], want, err_msg=f"head {g}")
 
 
+@pytest.mark.parametrize("case", ["all_equal", "tied_threshold_bin"])
+def test_select_heavy_ties_take_the_slow_path_exactly(case):
+    """More tied candidates than the threshold bin's list holds: the
+    selection falls back to a radix over the whole row, with the same result."""
+    rng = np.random.default_rng(11)
+    s, hkv = 40000, 2
+    if case == "all_equal":
+        vals = np.full((hkv, s), 0.25, dtype=np.float32)
+    else:
+        vals = rng.random((hkv, s)).astype(np.float32)
+        vals[:, 1000:30000] = np.float32(0.5)  # 29000 equal values around the threshold
+    budgets = np.array([5000, 20000])
+    desc = kvc.make_desc(s, 8, 8, hkv, 64, 64, n_sink=4, n_recent=32, pool=1)
+    scores = torch.from_numpy(vals).cuda()
+    ws = kvc.alloc_workspace(desc)
+    off = kvc.kvc_retained_offsets(desc, budgets)
+    idx = torch.empty(int(off[-1]), dtype=torch.int32, device="cuda")
+    kvc.kvc_select_topk(desc, scores, budgets, idx, ws)
+    got = split_heads(idx.cpu().numpy(), off)
+    for g in range(hkv):
+        want = oracle.select_head(vals[g].astype(np.float64), int(budgets[g]), 4, 32)
+        np.testing.assert_array_equal(got[g], want, err_msg=f"head {g}")
+
+
 def test_gather_given_indices_strided_and_offset():
     rng = np.random.default_rng(4)
     s, hkv, d = 3000, 4, 128
