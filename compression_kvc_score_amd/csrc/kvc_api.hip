@@ -37,7 +37,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647LL;
-constexpr int64_t kMaxPrompt = 1LL << 25;  // bounds the selection's per-chunk tables in LDS
+constexpr int64_t kMaxPrompt = 1LL << 23;  // bounds the selection's per-chunk tables in LDS
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -57,7 +57,7 @@ int score_wg_target() {
 int normalize(const kvc_layer_desc* d, Layer& L) {
   if (d == nullptr) return fail(KVC_ERR_INVALID_ARG, "desc is NULL");
   if (d->s < 1) return fail(KVC_ERR_INVALID_ARG, "s=%lld must be >= 1", (long long)d->s);
-  if (d->s > kMaxPrompt) return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^25", (long long)d->s);
+  if (d->s > kMaxPrompt) return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^23", (long long)d->s);
   if (d->w < 1 || d->w > d->s) return fail(KVC_ERR_INVALID_ARG, "w=%d outside [1, s]", d->w);
   if (d->hq < 1 || d->hkv < 1) return fail(KVC_ERR_INVALID_ARG, "hq=%d hkv=%d must be >= 1", d->hq, d->hkv);
   if (d->hkv > KVC_MAX_KV_HEADS) return fail(KVC_ERR_UNSUPPORTED, "hkv=%d > %d", d->hkv, KVC_MAX_KV_HEADS);
@@ -142,7 +142,7 @@ int n_chunks(const Layer& L) { return (int)((L.s + kSelectChunk - 1) / kSelectCh
 
 struct WsLayout {
   size_t part, m, z, scores, pooled;
-  size_t hist, cand_count, cand, chunk_above, chunk_range, head_out;
+  size_t hist, slots, chunk_in, chunk_above;
   size_t total;
 };
 
@@ -152,16 +152,12 @@ WsLayout ws_layout(const Layer& L) {
   const size_t nc = (size_t)n_chunks(L);
   w.hist = off;
   off += align_up((size_t)L.hkv * kHistBins * 4, 256);
-  w.cand_count = off;
-  off += align_up((size_t)L.hkv * 4, 256);
-  w.cand = off;
-  off += align_up((size_t)L.hkv * kCandCap * 8, 256);
+  w.slots = off;
+  off += align_up((size_t)L.hkv * nc * kSlotCap * 4, 256);
+  w.chunk_in = off;
+  off += align_up((size_t)L.hkv * nc * 4, 256);
   w.chunk_above = off;
   off += align_up((size_t)L.hkv * nc * 4, 256);
-  w.chunk_range = off;
-  off += align_up((size_t)L.hkv * nc * 16, 256);
-  w.head_out = off;
-  off += align_up((size_t)L.hkv * sizeof(SelectHead), 256);
   w.part = off;
   off += align_up((size_t)L.hkv * kMaxSplit * L.row_tiles * kRowTile * sizeof(float2), 256);
   w.m = off;
@@ -209,7 +205,7 @@ int check_lds(const Layer& L) {
     if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], lim, __ATOMIC_RELAXED);
   }
   const size_t need = std::max(std::max(pass1_lds_bytes(L), pass2_lds_bytes(L)),
-                               resolve_lds_bytes(n_chunks(L)) + 8192);
+                               select_lds_bytes(n_chunks(L)) + 8192);
   if (need > (size_t)lim)
     return fail(KVC_ERR_UNSUPPORTED, "kernels need %zu bytes of LDS, device allows %d", need, lim);
   return KVC_OK;
@@ -246,10 +242,7 @@ int run_pass1(const Layer& L, const void* q, const void* k, float* m_out, float*
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   a.part = reinterpret_cast<float*>(wsb + lay.part);
-  if (with_hist) {
-    a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
-    a.cand_count = reinterpret_cast<uint32_t*>(wsb + lay.cand_count);
-  }
+  if (with_hist) a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
   a.m_out = m_out;
   a.z_out = z_out;
   hipError_t e = launch_pass1(L, a, st);
@@ -289,11 +282,9 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
   a.n_recent = L.n_recent;
   a.n_chunks = n_chunks(L);
   a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
-  a.cand_count = reinterpret_cast<uint32_t*>(wsb + lay.cand_count);
-  a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+  a.slots = reinterpret_cast<uint32_t*>(wsb + lay.slots);
+  a.chunk_in = reinterpret_cast<uint32_t*>(wsb + lay.chunk_in);
   a.chunk_above = reinterpret_cast<uint32_t*>(wsb + lay.chunk_above);
-  a.chunk_range = reinterpret_cast<int64_t*>(wsb + lay.chunk_range);
-  a.head_out = reinterpret_cast<SelectHead*>(wsb + lay.head_out);
   a.heads = ht;
   const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");

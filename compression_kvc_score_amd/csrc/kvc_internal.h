@@ -17,6 +17,7 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSelectChunk = 4 * kSelectThreads;  // keys per selection workgroup
 constexpr int kHistBins = 4096;   // top-bits histogram of candidate scores (bits 30..19)
 constexpr int kCandCap = 16384;   // listed candidates per head inside the threshold bin
+constexpr int kSlotCap = 1024;    // listed candidates per 4096-key chunk
 
 // Descriptor after validation, with defaults resolved.
 struct Layer {
@@ -50,18 +51,12 @@ struct ScoreArgs {
   float* z_out;     // [hq][w]
   float* scores;    // [hkv][s]
   uint32_t* hist;   // [hkv][kHistBins]: pass 1 clears it, pass 2 fills it (null: skip)
-  uint32_t* cand_count;  // [hkv], cleared with hist
   int sink_end, rec_begin;  // candidate keys [sink_end, rec_begin) for the histogram
 };
 
 struct HeadTable {
   int32_t budget[KVC_MAX_KV_HEADS];
   int64_t offset[KVC_MAX_KV_HEADS + 1];  // packed row offsets of the retained outputs
-};
-
-struct SelectHead {
-  uint32_t thr;      // bit pattern of the k-th best candidate value
-  uint32_t need_eq;  // candidates equal to thr that are kept (lowest indices)
 };
 
 struct SelectArgs {
@@ -74,11 +69,9 @@ struct SelectArgs {
   int n_sink, n_recent;
   int n_chunks;          // ceil(s / kSelectChunk)
   uint32_t* hist;        // [hkv][kHistBins]
-  uint32_t* cand_count;  // [hkv]
-  uint2* cand;           // [hkv][kCandCap] (value bits, key index)
-  uint32_t* chunk_above; // [hkv][n_chunks]
-  int64_t* chunk_range;  // [hkv][n_chunks][2]: output offset, equal-candidates before
-  SelectHead* head_out;  // [hkv]
+  uint32_t* slots;       // [hkv][n_chunks][kSlotCap] listed patterns inside the threshold bin
+  uint32_t* chunk_in;    // [hkv][n_chunks] candidates inside the threshold bin
+  uint32_t* chunk_above; // [hkv][n_chunks] candidates above it
   HeadTable heads;
 };
 
@@ -107,7 +100,7 @@ hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
 // need_hist: clear and build the histogram (and pooled values) first;
 // otherwise pass 2 has built it.
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st);
-size_t resolve_lds_bytes(int n_chunks);
+size_t select_lds_bytes(int n_chunks);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 
 // Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;

@@ -173,7 +173,6 @@ __global__ void __launch_bounds__(512) pass1_kernel(ScoreArgs a) {
   // which pass 2 fills after this kernel has finished.
   if (a.hist != nullptr && split == 0) {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) a.hist[(int64_t)head * kHistBins + i] = 0u;
-    if (threadIdx.x == 0) a.cand_count[head] = 0u;
   }
   stage_queries<D>(a, head, ROWS_PAD, qs);
   __syncthreads();

@@ -13,19 +13,19 @@
 //           kernel also writes the pooled values.)
 //  filter   every chunk workgroup finds, from its head's histogram, the bin b*
 //           holding the k-th best candidate, counts its candidates above b*,
-//           and appends the candidates inside b* to a short per-head list.
-//  resolve  one workgroup per head radix-selects, among the listed
-//           candidates and in LDS, the exact pattern T of the k-th best and
-//           how many candidates equal to T are taken (the lowest indices:
-//           ties go to the lower index). From per-chunk counts it lays out
-//           every chunk's output range. If a bin holds more candidates than
-//           the list can take (heavily tied scores), it selects by a radix
-//           over the head's whole score row instead -- same result, slower.
-//  compact  every chunk workgroup writes its kept indices, ascending, to its
-//           range.
+//           and lists the patterns of its candidates inside b* in its own
+//           slot (no atomics).
+//  select   every chunk workgroup reads its head's short lists (a few
+//           thousand patterns), radix-selects in LDS the exact pattern T of
+//           the k-th best candidate and how many candidates equal to T are
+//           taken (the lowest indices: ties go to the lower index), derives
+//           its output offset from the counts of the chunks before it, and
+//           writes its kept indices in ascending order. If a slot or the
+//           lists overflow (heavily tied scores), it selects by a radix over
+//           the head's whole score row instead -- same result, slower.
 //
-// All counts are integers and the candidate list is only used as a multiset,
-// so the output does not depend on the order in which workgroups run.
+// All counts are integers, so the output does not depend on the order in
+// which workgroups run.
 
 #include "kvc_internal.h"
 
@@ -134,7 +134,6 @@ __device__ void find_bin(const uint32_t* hist, uint32_t k, uint32_t* scratch, ui
 __global__ void __launch_bounds__(256) init_kernel(SelectArgs a, int hkv) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < hkv * kHistBins) a.hist[i] = 0u;
-  if (i < hkv) a.cand_count[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -166,7 +165,8 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// filter: count candidates above b* per chunk, list the candidates inside b*.
+// filter: per chunk, count the candidates above b* and list, in key order,
+// the patterns of those inside b* (in the chunk's own slot: no atomics).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   __shared__ uint32_t scratch[kWaves + 1];
@@ -194,30 +194,22 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
       nin += in[e];
     }
   }
-  // wave-aggregated append of the in-bin candidates
-  const int lane = threadIdx.x & 63;
-  uint32_t incl = nin;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  const uint32_t wave_total = __shfl(incl, 63);
-  uint32_t base = 0;
-  if (lane == 63 && wave_total) base = atomicAdd(&a.cand_count[head], wave_total);
-  base = __shfl(base, 63);
-  uint32_t pos = base + incl - nin;
-  uint2* list = a.cand + (int64_t)head * kCandCap;
+  uint32_t n_in;
+  uint32_t pos = block_exclusive_scan(nin, scratch, n_in);
+  uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotCap;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (in[e]) {
-      if (pos < (uint32_t)kCandCap) list[pos] = make_uint2(bits[e], (uint32_t)(j0 + e));
+      if (pos < (uint32_t)kSlotCap) slot[pos] = bits[e];
       ++pos;
     }
   }
-  uint32_t tot;
-  block_exclusive_scan(above, scratch, tot);
-  if (threadIdx.x == 0) a.chunk_above[(int64_t)head * a.n_chunks + chunk] = tot;
+  uint32_t n_above;
+  block_exclusive_scan(above, scratch, n_above);
+  if (threadIdx.x == 0) {
+    a.chunk_above[(int64_t)head * a.n_chunks + chunk] = n_above;
+    a.chunk_in[(int64_t)head * a.n_chunks + chunk] = n_in;
+  }
 }
 
 // Mandatory keys inside chunk c.
@@ -230,11 +222,10 @@ __device__ __forceinline__ uint32_t chunk_mandatory(const HeadGeom& h, int64_t c
   return (uint32_t)(sink + rec);
 }
 
-// Slow path of resolve: k-th largest candidate pattern by a radix over the
-// whole score row of the head (8 bits per round from the top).
-__device__ uint32_t radix_over_row(const SelectArgs& a, const HeadGeom& h, const uint32_t* bits,
-                                   uint32_t k, uint32_t* hist256, uint32_t* scratch,
-                                   uint32_t& above) {
+// Slow path: k-th largest candidate pattern by a radix over the whole score
+// row of the head (8 bits per round from the top).
+__device__ uint32_t radix_over_row(const HeadGeom& h, const uint32_t* bits, uint32_t k,
+                                   uint32_t* hist256, uint32_t& above) {
   __shared__ uint32_t s_digit, s_rem;
   uint32_t prefix = 0u, mask = 0u, rem = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -278,124 +269,29 @@ __device__ uint32_t radix_over_row(const SelectArgs& a, const HeadGeom& h, const
   return prefix;
 }
 
-// ---------------------------------------------------------------------------
-// resolve: exact threshold per head and every chunk's output range.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) resolve_kernel(SelectArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* cbits = reinterpret_cast<uint32_t*>(smem);        // kCandCap
-  uint32_t* gt_c = cbits + kCandCap;                           // n_chunks
-  uint32_t* eq_c = gt_c + a.n_chunks;                          // n_chunks
-  __shared__ uint32_t hist[1024];
-  __shared__ uint32_t scratch[kWaves + 1];
-  __shared__ uint32_t s_digit, s_rem;
-
-  const int head = blockIdx.x;
-  const HeadGeom h = head_geom(a, head);
-  SelectHead* out = a.head_out + head;
-  int64_t* ranges = a.chunk_range + (int64_t)head * a.n_chunks * 2;
-  if (h.keep_all) return;  // compact writes 0..s-1 directly
-
-  for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) { gt_c[c] = 0u; eq_c[c] = 0u; }
-  uint32_t thr = 0xFFFFFFFFu, need_eq = 0u;  // k_sel == 0: choose no candidate
-  const uint32_t* rowbits = reinterpret_cast<const uint32_t*>(a.vals + (int64_t)head * h.s);
-  const uint32_t n_cand = h.k_sel ? a.cand_count[head] : 0u;
-  const bool overflow = n_cand > (uint32_t)kCandCap;
-  __syncthreads();
-
-  if (h.k_sel > 0 && !overflow) {
-    // candidates above b*, over all chunks
-    uint32_t above_local = 0;
-    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads)
-      above_local += a.chunk_above[(int64_t)head * a.n_chunks + c];
-    uint32_t above_all;
-    block_exclusive_scan(above_local, scratch, above_all);
-    uint32_t rem = h.k_sel - above_all;  // rank of the threshold inside the listed candidates
-    const uint2* list = a.cand + (int64_t)head * kCandCap;
-    for (uint32_t i = threadIdx.x; i < n_cand; i += kThreads) cbits[i] = list[i].x;
-    // the listed candidates share bits 30..19; radix over bits 18..9 then 8..0
-    uint32_t prefix = 0u, mask = 0u;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int shift = p == 0 ? 9 : 0;
-      const uint32_t nb = p == 0 ? 1024u : 512u;
-      for (uint32_t i = threadIdx.x; i < 1024u; i += kThreads) hist[i] = 0u;
-      __syncthreads();
-      for (uint32_t i = threadIdx.x; i < n_cand; i += kThreads) {
-        const uint32_t u = cbits[i] & 0x7FFFFu;
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      // descending scan over nb bins, one bin per thread
-      const uint32_t b = nb - 1 - threadIdx.x;
-      const uint32_t cnt = threadIdx.x < nb ? hist[b] : 0u;
-      uint32_t tot;
-      const uint32_t before = block_exclusive_scan(cnt, scratch, tot);
-      if (threadIdx.x < nb && before < rem && rem <= before + cnt) {
-        s_digit = b;
-        s_rem = rem - before;
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      mask |= (nb - 1) << shift;
-      rem = s_rem;
-      __syncthreads();
-    }
-    thr = (cbits[0] & ~0x7FFFFu) | prefix;  // listed candidates all carry b* in bits 31..19
-    need_eq = rem;
-    // per-chunk counts of listed candidates above / equal to the threshold
-    for (uint32_t i = threadIdx.x; i < n_cand; i += kThreads) {
-      const uint2 e = list[i];
-      const int64_t c = (int64_t)e.y / kChunk;
-      if (e.x > thr) atomicAdd(&gt_c[c], 1u);
-      else if (e.x == thr) atomicAdd(&eq_c[c], 1u);
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads)
-      gt_c[c] += a.chunk_above[(int64_t)head * a.n_chunks + c];
-    __syncthreads();
-  } else if (h.k_sel > 0) {
-    uint32_t above;
-    thr = radix_over_row(a, h, rowbits, h.k_sel, hist, scratch, above);
-    need_eq = h.k_sel - above;
-    for (int64_t j = h.sink_end + threadIdx.x; j < h.rec_begin; j += kThreads) {
-      const uint32_t u = rowbits[j];
-      if (u > thr) atomicAdd(&gt_c[j / kChunk], 1u);
-      else if (u == thr) atomicAdd(&eq_c[j / kChunk], 1u);
-    }
-    __syncthreads();
-  }
-
-  // chunk ranges: equal candidates are taken in index order until need_eq
-  uint32_t eq_run = 0, out_run = 0;
-  for (int base = 0; base < a.n_chunks; base += kThreads) {
-    const int c = base + threadIdx.x;
-    const uint32_t e = c < a.n_chunks ? eq_c[c] : 0u;
-    uint32_t etot;
-    const uint32_t eb = eq_run + block_exclusive_scan(e, scratch, etot);
-    uint32_t take = 0;
-    if (need_eq > eb) take = need_eq - eb < e ? need_eq - eb : e;
-    const uint32_t kept = c < a.n_chunks ? chunk_mandatory(h, c) + gt_c[c] + take : 0u;
-    uint32_t ktot;
-    const uint32_t ob = out_run + block_exclusive_scan(kept, scratch, ktot);
-    if (c < a.n_chunks) {
-      ranges[2 * c] = ob;
-      ranges[2 * c + 1] = eb;
-    }
-    eq_run += etot;
-    out_run += ktot;
-  }
-  if (threadIdx.x == 0) {
-    out->thr = thr;
-    out->need_eq = need_eq;
-  }
+// Sum over the workgroup of one value per thread (all threads get it).
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
+  uint32_t tot;
+  block_exclusive_scan(v, scratch, tot);
+  return tot;
 }
 
 // ---------------------------------------------------------------------------
-// compact: kept indices of one chunk, ascending, at the chunk's output range.
+// select: each chunk workgroup resolves its head's exact threshold from the
+// listed candidates (the same computation in every workgroup of the head),
+// derives its output offset from the counts of the chunks before it, and
+// writes its kept indices in ascending order.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) compact_kernel(SelectArgs a) {
+__global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* cbits = reinterpret_cast<uint32_t*>(smem);  // kCandCap listed patterns
+  uint32_t* coff = cbits + kCandCap;                    // n_chunks + 1 list offsets
+  uint32_t* gt_c = coff + a.n_chunks + 1;               // n_chunks
+  uint32_t* eq_c = gt_c + a.n_chunks;                   // n_chunks
+  __shared__ uint32_t hist[1024];
   __shared__ uint32_t scratch[kWaves + 1];
+  __shared__ uint32_t s_digit, s_rem, s_flag;
+
   const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
   const HeadGeom h = head_geom(a, head);
   int32_t* out = a.idx_out + a.heads.offset[head];
@@ -406,14 +302,113 @@ __global__ void __launch_bounds__(kThreads) compact_kernel(SelectArgs a) {
       if (j0 + e < h.s) out[j0 + e] = (int32_t)(j0 + e);
     return;
   }
-  const uint32_t thr = a.head_out[head].thr;
-  const uint32_t need_eq = a.head_out[head].need_eq;
-  const int64_t* rg = a.chunk_range + ((int64_t)head * a.n_chunks + chunk) * 2;
-  const int64_t out_base = rg[0];
-  const uint32_t eq_base = (uint32_t)rg[1];
   const float* vals = a.vals + (int64_t)head * h.s;
+  const uint32_t* rowbits = reinterpret_cast<const uint32_t*>(vals);
+  const int nc = a.n_chunks;
+  const uint32_t* c_in = a.chunk_in + (int64_t)head * nc;
+  const uint32_t* c_above = a.chunk_above + (int64_t)head * nc;
 
-  uint32_t flags[4];  // 1: definitely kept, 2: equal to the threshold
+  uint32_t thr = 0xFFFFFFFFu, need_eq = 0u;  // k_sel == 0: no candidate is chosen
+  // counts of the chunks before this one: kept = mandatory + above + taken equals
+  uint32_t prev_gt = 0, prev_eq = 0;
+  uint32_t eq_before = 0;  // equal candidates in chunks before this one
+  if (h.k_sel > 0) {
+    // list offsets; overflow if a chunk's slot or the whole list is too small
+    if (threadIdx.x == 0) s_flag = 0u;
+    __syncthreads();
+    uint32_t n_total = 0;
+    for (int base = 0; base < nc; base += kThreads) {
+      const int c = base + threadIdx.x;
+      const uint32_t n = c < nc ? c_in[c] : 0u;
+      if (n > (uint32_t)kSlotCap) s_flag = 1u;
+      uint32_t t;
+      const uint32_t o = n_total + block_exclusive_scan(n, scratch, t);
+      if (c < nc) coff[c] = o;
+      n_total += t;
+    }
+    if (threadIdx.x == 0) coff[nc] = n_total;
+    if (n_total > (uint32_t)kCandCap) s_flag = 1u;
+    __syncthreads();
+    const bool overflow = s_flag != 0u;
+
+    if (!overflow) {
+      uint32_t above_local = 0;
+      for (int c = threadIdx.x; c < nc; c += kThreads) above_local += c_above[c];
+      const uint32_t above_all = block_sum(above_local, scratch);
+      uint32_t rem = h.k_sel - above_all;  // rank of the threshold inside the list
+      // gather the listed patterns of all chunks, chunk by chunk
+      for (uint32_t i = threadIdx.x; i < n_total; i += kThreads) {
+        int lo = 0, hi = nc - 1;  // last chunk with coff[c] <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (coff[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        cbits[i] = a.slots[((int64_t)head * nc + lo) * kSlotCap + (i - coff[lo])];
+      }
+      // the listed patterns share bits 31..19; radix over bits 18..9, then 8..0
+      uint32_t prefix = 0u, mask = 0u;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int shift = p == 0 ? 9 : 0;
+        const uint32_t nb = p == 0 ? 1024u : 512u;
+        for (uint32_t i = threadIdx.x; i < 1024u; i += kThreads) hist[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n_total; i += kThreads) {
+          const uint32_t u = cbits[i] & 0x7FFFFu;
+          if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        const uint32_t b = nb - 1 - threadIdx.x;
+        const uint32_t cnt = threadIdx.x < nb ? hist[b] : 0u;
+        uint32_t tot;
+        const uint32_t before = block_exclusive_scan(cnt, scratch, tot);
+        if (threadIdx.x < nb && before < rem && rem <= before + cnt) {
+          s_digit = b;
+          s_rem = rem - before;
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        mask |= (nb - 1) << shift;
+        rem = s_rem;
+        __syncthreads();
+      }
+      thr = (cbits[0] & ~0x7FFFFu) | prefix;
+      need_eq = rem;
+      // above / equal counts of the listed entries of the chunks before this one
+      const uint32_t lim = coff[chunk];
+      uint32_t g = 0, q = 0;
+      for (uint32_t i = threadIdx.x; i < lim; i += kThreads) {
+        g += cbits[i] > thr;
+        q += cbits[i] == thr;
+      }
+      for (int c = threadIdx.x; c < chunk; c += kThreads) g += c_above[c];
+      prev_gt = block_sum(g, scratch);
+      prev_eq = block_sum(q, scratch);
+    } else {
+      uint32_t above;
+      thr = radix_over_row(h, rowbits, h.k_sel, hist, above);
+      need_eq = h.k_sel - above;
+      const int64_t lim = (int64_t)chunk * kChunk < h.rec_begin ? (int64_t)chunk * kChunk : h.rec_begin;
+      uint32_t g = 0, q = 0;
+      for (int64_t j = h.sink_end + threadIdx.x; j < lim; j += kThreads) {
+        const uint32_t u = rowbits[j];
+        g += u > thr;
+        q += u == thr;
+      }
+      prev_gt = block_sum(g, scratch);
+      prev_eq = block_sum(q, scratch);
+    }
+    eq_before = prev_eq;
+  }
+  // output offset of this chunk: mandatory keys, candidates above the
+  // threshold and the equal candidates taken, all in the chunks before it
+  uint32_t mand_before = 0;
+  for (int c = threadIdx.x; c < chunk; c += kThreads) mand_before += chunk_mandatory(h, c);
+  mand_before = block_sum(mand_before, scratch);
+  const uint32_t taken_before = need_eq < eq_before ? need_eq : eq_before;
+  const int64_t out_base = (int64_t)mand_before + prev_gt + taken_before;
+
+  uint32_t flags[4];  // 1: kept, 2: equal to the threshold (kept in index order)
   uint32_t neq = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -427,7 +422,7 @@ __global__ void __launch_bounds__(kThreads) compact_kernel(SelectArgs a) {
     else if (u == thr) { flags[e] = 2u; ++neq; }
   }
   uint32_t tot;
-  uint32_t eq_rank = eq_base + block_exclusive_scan(neq, scratch, tot);
+  uint32_t eq_rank = eq_before + block_exclusive_scan(neq, scratch, tot);
   uint32_t nkeep = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -451,8 +446,8 @@ __global__ void __launch_bounds__(kThreads) compact_kernel(SelectArgs a) {
 
 }  // namespace
 
-size_t resolve_lds_bytes(int n_chunks) {
-  return (size_t)kCandCap * 4 + (size_t)n_chunks * 8;
+size_t select_lds_bytes(int n_chunks) {
+  return (size_t)kCandCap * 4 + (size_t)(3 * n_chunks + 1) * 4;
 }
 
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
@@ -471,13 +466,10 @@ hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hi
   }
   e = hipLaunchKernel(reinterpret_cast<const void*>(&filter_kernel), chunks, dim3(kThreads), kargs, 0, st);
   if (e != hipSuccess) return e;
-  const size_t lds = resolve_lds_bytes(a.n_chunks);
-  e = ensure_lds(reinterpret_cast<const void*>(&resolve_kernel), lds);
+  const size_t lds = select_lds_bytes(a.n_chunks);
+  e = ensure_lds(reinterpret_cast<const void*>(&select_kernel), lds);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&resolve_kernel), dim3((unsigned)L.hkv),
-                      dim3(kThreads), kargs, lds, st);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&compact_kernel), chunks, dim3(kThreads), kargs, 0, st);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&select_kernel), chunks, dim3(kThreads), kargs, lds, st);
 }
 
 }  // namespace kvc

@@ -74,7 +74,7 @@ typedef void* kvc_stream_t;
 
 /*
  * Shape and options of one layer's compression.
- *  s            prompt length = number of keys scored, 1 <= s <= 2^25
+ *  s            prompt length = number of keys scored, 1 <= s <= 2^23
  *  w            observation window: the last w prompt queries, 1 <= w <= s
  *  hq, hkv      query and KV heads, hq % hkv == 0, 1 <= hkv <= KVC_MAX_KV_HEADS,
  *               (hq / hkv) * w <= KVC_MAX_ROWS
@@ -125,8 +125,8 @@ const char* kvc_last_error(void);
  * Workspace bytes that every entry point below accepts for this descriptor
  * (the largest need, reached by kvc_compress_layer with all optional outputs
  * NULL). Pure host function. Apart from the fp32 score and pooled-score
- * vectors (4 * hkv * s bytes each) and 20 bytes per KV head per 4096 keys of
- * selection bookkeeping, it does not grow with s, following the
+ * vectors (4 * hkv * s bytes each) and about 1 byte per key and KV head of
+ * selection bookkeeping (4104 bytes per 4096 keys), it does not grow with s, following the
  * S-independent temporary bound of TideKV's Fig. 3 caption.
  * Returns 0 if the descriptor is invalid.
  */
