@@ -1,11 +1,11 @@
 // Two-pass blockwise scoring on gfx950 (TideKV, Fig. 3 caption).
 //
-// Work decomposition (both passes): one workgroup = block/32 wavefronts scans
-// `blocks_per_wg` consecutive key blocks of one KV head; in every block each
-// wavefront owns one 32-key tile. The G*W query rows of the head (its
-// window queries) are staged once per workgroup in LDS and stay stationary;
-// K streams from HBM straight into VGPRs in the bf16 MFMA operand layout,
-// one tile ahead of the math.
+// Work decomposition (both passes): one workgroup of up to 8 wavefronts
+// scans `blocks_per_wg` consecutive key blocks of one KV head; in every block
+// each wavefront owns one or more 32-key tiles. The G*W query rows of the
+// head (its window queries) are staged once per workgroup in LDS and stay
+// stationary; K streams from HBM straight into VGPRs in the bf16 MFMA operand
+// layout, one tile ahead of the math.
 //
 // The contraction Q_win . K^T runs on v_mfma_f32_32x32x16_bf16. The k-index
 // of the MFMA is a sum index, so any assignment of head-dimension chunks to
@@ -20,6 +20,11 @@
 // that every lane owns one key and 16 query rows: the per-key pooling over
 // the group's window rows is an in-register sum plus one lane-half exchange.
 // exp runs in base 2 on v_exp_f32 with the scale folded into one FMA.
+//
+// Latency hiding: the next tile's loads are issued unconditionally before
+// the current tile is computed (so the compiler never waits on them early),
+// and within a tile the MFMAs of row tile t+1 are issued before the VALU
+// work of row tile t.
 
 #include "kvc_internal.h"
 
@@ -85,7 +90,8 @@ __device__ __forceinline__ void load_key_frag(const ScoreArgs& a, int head, int 
 // The 32-key tiles one wavefront visits: in each of the workgroup's blocks,
 // tiles wave, wave + nwaves, ... (block / 32 / nwaves of them), in increasing
 // key order. The first `clean` tiles hold only keys that every window query
-// sees; the rest (at the end of the prompt) need the causal mask.
+// sees; the rest (at the end of the prompt) need the causal mask. kbase(k)
+// of any k >= n names keys past the range, which loads clamp into it.
 struct TileSeq {
   int b0, block, nwaves, tpw, wave;
   int n, clean;
@@ -110,55 +116,78 @@ __device__ __forceinline__ TileSeq tile_seq(const ScoreArgs& a, int split, int w
   return q;
 }
 
-// One 32-key tile of pass 1 against every query row tile: updates the
-// lane-private online (max, sum-exp) state of the lane's query rows.
+// One row tile of the Q_win.K^T contraction for the lane's 32-key tile.
+// KROWS: the MFMA rows are the keys (pass 1: lane = one query row, 16 keys);
+// otherwise the rows are the query rows (pass 2: lane = one key, 16 rows).
+template <int D, bool KROWS>
+__device__ __forceinline__ f32x16_t contract_row_tile(const uint16_t* qs, const uint4 (&kf)[D / 16],
+                                                      int t, int half, int l32) {
+  constexpr int PITCH = D + 8;
+  constexpr int NCH = D / 16;
+  const uint16_t* qrow = qs + (t * kRowTile + l32) * PITCH + half * (D / 2);
+  f32x16_t acc = {};
+#pragma unroll
+  for (int st = 0; st < NCH; ++st) {
+    const uint4 qf = *reinterpret_cast<const uint4*>(qrow + st * 8);
+    acc = KROWS ? mfma32x32x16(kf[st], qf, acc) : mfma32x32x16(qf, kf[st], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  const float a = fmaxf(fmaxf(v[0], v[1]), v[2]);
+  const float b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float c = fmaxf(fmaxf(v[6], v[7]), v[8]);
+  const float d = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float e = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), v[15]));
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1
+// ---------------------------------------------------------------------------
+
+// Online (max, sum-exp) update of the lane's query row in one row tile with
+// the 16 logits it holds (keys kbase + 8*(e/4) + 4*half + e%4).
+template <bool EDGE>
+__device__ __forceinline__ void lse_update(const ScoreArgs& a, f32x16_t acc, int kbase, int half,
+                                           int qpos, float& mrun, float& zrun) {
+  if constexpr (EDGE) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kbase + 8 * (e >> 2) + 4 * half + (e & 3);
+      if (key >= a.s || key > qpos) acc[e] = -INFINITY;
+    }
+  }
+  const float mnew = fmaxf(mrun, max16(acc));
+  if (EDGE && mnew == -INFINITY) return;  // nothing visible to this row yet
+  const float mc = mnew * a.c;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    s0 += exp2_raw(fmaf(acc[e], a.c, -mc));
+    s1 += exp2_raw(fmaf(acc[e + 1], a.c, -mc));
+  }
+  zrun = zrun * exp2_raw((mrun - mnew) * a.c) + (s0 + s1);
+  mrun = mnew;
+}
+
 template <int D, int NRT, bool EDGE>
 __device__ __forceinline__ void pass1_tile(const ScoreArgs& a, const uint16_t* qs,
                                            const uint4 (&kf)[D / 16], int kbase, int half,
                                            int l32, const int (&qpos)[NRT],
                                            float (&mrun)[NRT], float (&zrun)[NRT]) {
-  constexpr int PITCH = D + 8;
-  constexpr int NCH = D / 16;
+  f32x16_t acc[2];
+  acc[0] = contract_row_tile<D, true>(qs, kf, 0, half, l32);
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
-    f32x16_t acc = {};
-    const uint16_t* qrow = qs + (t * kRowTile + l32) * PITCH + half * (D / 2);
-#pragma unroll
-    for (int st = 0; st < NCH; ++st) {
-      const uint4 qf = *reinterpret_cast<const uint4*>(qrow + st * 8);
-      acc = mfma32x32x16(kf[st], qf, acc);  // rows: keys, columns: query rows
-    }
-    // acc[e] is key kbase + 8*(e/4) + 4*half + e%4 against query row t*32 + l32.
-    if constexpr (EDGE) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kbase + 8 * (e >> 2) + 4 * half + (e & 3);
-        if (key >= a.s || key > qpos[t]) acc[e] = -INFINITY;
-      }
-    }
-    float tmax = acc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, acc[e]);
-    const float mnew = fmaxf(mrun[t], tmax);
-    if (mnew != -INFINITY) {
-      const float mc = mnew * a.c;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        s0 += exp2_raw(fmaf(acc[e], a.c, -mc));
-        s1 += exp2_raw(fmaf(acc[e + 1], a.c, -mc));
-      }
-      zrun[t] = zrun[t] * exp2_raw((mrun[t] - mnew) * a.c) + (s0 + s1);
-      mrun[t] = mnew;
-    }
-    // Keep one row tile's operands live at a time.
-    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < NRT) acc[(t + 1) & 1] = contract_row_tile<D, true>(qs, kf, t + 1, half, l32);
+    lse_update<EDGE>(a, acc[t & 1], kbase, half, qpos[t], mrun[t], zrun[t]);
+    __builtin_amdgcn_sched_barrier(0);  // at most two row tiles of operands live
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 1: split-local (max, sum-exp) per query row.
-// ---------------------------------------------------------------------------
+// Split-local (max, sum-exp) per query row.
 template <int D, int NRT>
 __global__ void __launch_bounds__(512) pass1_kernel(ScoreArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -174,13 +203,15 @@ __global__ void __launch_bounds__(512) pass1_kernel(ScoreArgs a) {
   if (a.hist != nullptr && split == 0) {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) a.hist[(int64_t)head * kHistBins + i] = 0u;
   }
-  stage_queries<D>(a, head, ROWS_PAD, qs);
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nwaves = blockDim.x >> 6;
   const int first_hidden = a.s - a.w + 1;  // keys from here on are after some window query
+  const TileSeq seq = tile_seq(a, split, wave, nwaves, first_hidden);
+  uint4 ka[NCH], kb[NCH];
+  load_key_frag<D>(a, head, seq.kbase(0) + l32, half, ka);  // streams in during staging
+  stage_queries<D>(a, head, ROWS_PAD, qs);
+  __syncthreads();
 
   float mrun[NRT], zrun[NRT];
   int qpos[NRT];  // prompt position of this lane's query row in tile t (-1: padding row)
@@ -192,19 +223,15 @@ __global__ void __launch_bounds__(512) pass1_kernel(ScoreArgs a) {
     qpos[t] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
   }
 
-  const TileSeq seq = tile_seq(a, split, wave, nwaves, first_hidden);
-  uint4 ka[NCH], kb[NCH];
-  if (seq.clean > 0) load_key_frag<D>(a, head, seq.kbase(0) + l32, half, ka);
-  // Two tiles per iteration so the prefetch alternates between two fragment
-  // sets without register copies.
-  for (int k = 0; k < seq.clean; k += 2) {
-    if (k + 1 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 1) + l32, half, kb);
+  int k = 0;
+  for (; k + 1 < seq.clean; k += 2) {
+    load_key_frag<D>(a, head, seq.kbase(k + 1) + l32, half, kb);
     pass1_tile<D, NRT, false>(a, qs, ka, seq.kbase(k), half, l32, qpos, mrun, zrun);
-    if (k + 1 >= seq.clean) break;
-    if (k + 2 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 2) + l32, half, ka);
+    load_key_frag<D>(a, head, seq.kbase(k + 2) + l32, half, ka);
     pass1_tile<D, NRT, false>(a, qs, kb, seq.kbase(k + 1), half, l32, qpos, mrun, zrun);
   }
-  for (int k = seq.clean; k < seq.n; ++k) {
+  if (k < seq.clean) pass1_tile<D, NRT, false>(a, qs, ka, seq.kbase(k), half, l32, qpos, mrun, zrun);
+  for (k = seq.clean; k < seq.n; ++k) {
     load_key_frag<D>(a, head, seq.kbase(k) + l32, half, ka);
     pass1_tile<D, NRT, true>(a, qs, ka, seq.kbase(k), half, l32, qpos, mrun, zrun);
   }
@@ -267,6 +294,34 @@ __global__ void __launch_bounds__(256) combine_kernel(ScoreArgs a, int rows_pad)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pass 2
+// ---------------------------------------------------------------------------
+
+// Add the lane key's normalised weights of row tile t (rows
+// t*32 + 8*(e/4) + 4*half + e%4) to the running sums.
+template <bool EDGE>
+__device__ __forceinline__ void weight_sum(const ScoreArgs& a, const f32x16_t& acc,
+                                           const float* bias, int t, int key, int half,
+                                           float& s0, float& s1) {
+  const float* bt = bias + t * kRowTile + 4 * half;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float4 bq = *reinterpret_cast<const float4*>(bt + 8 * q4);
+    const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      float p = exp2_raw(fmaf(acc[4 * q4 + e4], a.c, -bb[e4]));
+      if constexpr (EDGE) {
+        const int r = t * kRowTile + 8 * q4 + 4 * half + e4;
+        const int qp = a.s - a.w + (r % a.w);
+        if (key >= a.s || r >= a.rows || key > qp) p = 0.f;
+      }
+      if (e4 & 1) s1 += p; else s0 += p;
+    }
+  }
+}
+
 // One 32-key tile of pass 2: the lane's key collects exp(l - m)/Z over all
 // query rows of the head; lanes l and l+32 then add their row halves.
 template <int D, int NRT, bool EDGE>
@@ -274,40 +329,17 @@ __device__ __forceinline__ void pass2_tile(const ScoreArgs& a, const uint16_t* q
                                            const float* bias, const uint4 (&kf)[D / 16],
                                            int kbase, int half, int l32, float* out,
                                            uint32_t* lh) {
-  constexpr int PITCH = D + 8;
-  constexpr int NCH = D / 16;
   const int key = kbase + l32;
   float s0 = 0.f, s1 = 0.f;
   // With many row tiles, re-read the per-row bias from LDS for every tile
   // rather than letting it be hoisted into registers for the whole scan.
   if constexpr (NRT > 4) asm volatile("" ::: "memory");
+  f32x16_t acc[2];
+  acc[0] = contract_row_tile<D, false>(qs, kf, 0, half, l32);
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
-    f32x16_t acc = {};
-    const uint16_t* qrow = qs + (t * kRowTile + l32) * PITCH + half * (D / 2);
-#pragma unroll
-    for (int st = 0; st < NCH; ++st) {
-      const uint4 qf = *reinterpret_cast<const uint4*>(qrow + st * 8);
-      acc = mfma32x32x16(qf, kf[st], acc);  // rows: query rows, columns: keys
-    }
-    // acc[e] is query row t*32 + 8*(e/4) + 4*half + e%4 against key kbase + l32.
-    const float* bt = bias + t * kRowTile + 4 * half;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 bq = *reinterpret_cast<const float4*>(bt + 8 * q4);
-      const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int e = 4 * q4 + e4;
-        float p = exp2_raw(fmaf(acc[e], a.c, -bb[e4]));
-        if constexpr (EDGE) {
-          const int r = t * kRowTile + 8 * q4 + 4 * half + e4;
-          const int qp = a.s - a.w + (r % a.w);
-          if (key >= a.s || r >= a.rows || key > qp) p = 0.f;
-        }
-        if (e4 & 1) s1 += p; else s0 += p;
-      }
-    }
+    if (t + 1 < NRT) acc[(t + 1) & 1] = contract_row_tile<D, false>(qs, kf, t + 1, half, l32);
+    weight_sum<EDGE>(a, acc[t & 1], bias, t, key, half, s0, s1);
     __builtin_amdgcn_sched_barrier(0);
   }
   float sum = s0 + s1;
@@ -319,9 +351,7 @@ __device__ __forceinline__ void pass2_tile(const ScoreArgs& a, const uint16_t* q
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 2: normalised weights summed per key over the group's window rows.
-// ---------------------------------------------------------------------------
+// Normalised weights summed per key over the group's window rows.
 template <int D, int NRT>
 __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -331,12 +361,20 @@ __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
   float* bias = reinterpret_cast<float*>(smem + ROWS_PAD * PITCH * 2);
   uint32_t* lh = a.hist != nullptr ? reinterpret_cast<uint32_t*>(bias + ROWS_PAD) : nullptr;
-  if (lh != nullptr)
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0u;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int head = work / a.n_split;
   const int split = work % a.n_split;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nwaves = blockDim.x >> 6;
+  const int first_hidden = a.s - a.w + 1;
+  const TileSeq seq = tile_seq(a, split, wave, nwaves, first_hidden);
+  uint4 ka[NCH], kb[NCH];
+  load_key_frag<D>(a, head, seq.kbase(0) + l32, half, ka);  // streams in during staging
+
+  if (lh != nullptr)
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0u;
   stage_queries<D>(a, head, ROWS_PAD, qs);
   // p = exp(l - m) / Z = 2^(dot * c - (m * log2 e + log2 Z)); padding rows get +inf (p = 0).
   for (int r = threadIdx.x; r < ROWS_PAD; r += blockDim.x) {
@@ -350,23 +388,16 @@ __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int nwaves = blockDim.x >> 6;
-  const int first_hidden = a.s - a.w + 1;
-
-  const TileSeq seq = tile_seq(a, split, wave, nwaves, first_hidden);
   float* out = a.scores + (int64_t)head * a.s;
-  uint4 ka[NCH], kb[NCH];
-  if (seq.clean > 0) load_key_frag<D>(a, head, seq.kbase(0) + l32, half, ka);
-  for (int k = 0; k < seq.clean; k += 2) {
-    if (k + 1 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 1) + l32, half, kb);
+  int k = 0;
+  for (; k + 1 < seq.clean; k += 2) {
+    load_key_frag<D>(a, head, seq.kbase(k + 1) + l32, half, kb);
     pass2_tile<D, NRT, false>(a, qs, bias, ka, seq.kbase(k), half, l32, out, lh);
-    if (k + 1 >= seq.clean) break;
-    if (k + 2 < seq.clean) load_key_frag<D>(a, head, seq.kbase(k + 2) + l32, half, ka);
+    load_key_frag<D>(a, head, seq.kbase(k + 2) + l32, half, ka);
     pass2_tile<D, NRT, false>(a, qs, bias, kb, seq.kbase(k + 1), half, l32, out, lh);
   }
-  for (int k = seq.clean; k < seq.n; ++k) {
+  if (k < seq.clean) pass2_tile<D, NRT, false>(a, qs, bias, ka, seq.kbase(k), half, l32, out, lh);
+  for (k = seq.clean; k < seq.n; ++k) {
     load_key_frag<D>(a, head, seq.kbase(k) + l32, half, ka);
     pass2_tile<D, NRT, true>(a, qs, bias, ka, seq.kbase(k), half, l32, out, lh);
   }

@@ -286,8 +286,6 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* cbits = reinterpret_cast<uint32_t*>(smem);  // kCandCap listed patterns
   uint32_t* coff = cbits + kCandCap;                    // n_chunks + 1 list offsets
-  uint32_t* gt_c = coff + a.n_chunks + 1;               // n_chunks
-  uint32_t* eq_c = gt_c + a.n_chunks;                   // n_chunks
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t scratch[kWaves + 1];
   __shared__ uint32_t s_digit, s_rem, s_flag;
@@ -447,7 +445,7 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
 }  // namespace
 
 size_t select_lds_bytes(int n_chunks) {
-  return (size_t)kCandCap * 4 + (size_t)(3 * n_chunks + 1) * 4;
+  return (size_t)kCandCap * 4 + (size_t)(n_chunks + 1) * 4;
 }
 
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
