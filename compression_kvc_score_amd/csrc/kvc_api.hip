@@ -54,6 +54,25 @@ int score_wg_target() {
   return v;
 }
 
+// Workgroups the streaming scans aim for (one per CU: each uses most of the LDS).
+int stream_wg_target() {
+  static const int v = [] {
+    const char* e = std::getenv("KVC_STREAM_WGS");
+    const int x = e ? std::atoi(e) : 0;
+    return x > 0 ? x : 256;
+  }();
+  return v;
+}
+
+// KVC_STREAM=0 selects the per-head scans everywhere (for comparisons).
+bool stream_scans_enabled() {
+  static const bool v = [] {
+    const char* e = std::getenv("KVC_STREAM");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+
 int normalize(const kvc_layer_desc* d, Layer& L) {
   if (d == nullptr) return fail(KVC_ERR_INVALID_ARG, "desc is NULL");
   if (d->s < 1) return fail(KVC_ERR_INVALID_ARG, "s=%lld must be >= 1", (long long)d->s);
@@ -105,10 +124,19 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   L.v_tok = d->v_tok_stride ? d->v_tok_stride : (int64_t)d->hkv * d->d;
   L.v_head = d->v_head_stride ? d->v_head_stride : d->d;
 
-  // Partition the key blocks of each head over at most kMaxSplit workgroups.
-  L.n_blocks = (int)((L.s + L.block - 1) / L.block);
+  // Streaming scans when each wavefront can hold its head's query rows in
+  // registers; head pairs when the KV heads pair up.
+  L.stream_hg = 0;
+  if (L.row_tiles <= 4 && stream_scans_enabled()) L.stream_hg = L.hkv % 2 == 0 ? 2 : 1;
+
+  // Partition the key blocks (streaming: stages) of each head (group) over at
+  // most kMaxSplit workgroups.
+  const int unit = L.stream_hg ? stream_tokens(L.stream_hg) : L.block;
+  const int groups = L.stream_hg ? L.hkv / L.stream_hg : L.hkv;
+  const int target = L.stream_hg ? stream_wg_target() : score_wg_target();
+  L.n_blocks = (int)((L.s + unit - 1) / unit);
   const int64_t min_bpw = (L.n_blocks + kMaxSplit - 1) / kMaxSplit;
-  const int64_t want_bpw = ((int64_t)L.n_blocks * L.hkv + score_wg_target() - 1) / score_wg_target();
+  const int64_t want_bpw = ((int64_t)L.n_blocks * groups + target - 1) / target;
   L.blocks_per_wg = (int)std::max<int64_t>(1, std::max(min_bpw, want_bpw));
   L.n_split = (L.n_blocks + L.blocks_per_wg - 1) / L.blocks_per_wg;
   return KVC_OK;
@@ -204,8 +232,9 @@ int check_lds(const Layer& L) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], lim, __ATOMIC_RELAXED);
   }
-  const size_t need = std::max(std::max(pass1_lds_bytes(L), pass2_lds_bytes(L)),
-                               select_lds_bytes(n_chunks(L)) + 8192);
+  const size_t scan = L.stream_hg ? std::max(pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L))
+                                  : std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
+  const size_t need = std::max(scan, select_lds_bytes(n_chunks(L)) + 8192);
   if (need > (size_t)lim)
     return fail(KVC_ERR_UNSUPPORTED, "kernels need %zu bytes of LDS, device allows %d", need, lim);
   return KVC_OK;
@@ -245,7 +274,7 @@ int run_pass1(const Layer& L, const void* q, const void* k, float* m_out, float*
   if (with_hist) a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
   a.m_out = m_out;
   a.z_out = z_out;
-  hipError_t e = launch_pass1(L, a, st);
+  hipError_t e = L.stream_hg ? launch_stream(true, L, a, st) : launch_pass1(L, a, st);
   if (e != hipSuccess) return hip_fail(e, "pass-1 launch");
   e = launch_combine(L, a, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -260,7 +289,7 @@ int run_pass2(const Layer& L, const void* q, const void* k, const float* m, cons
   a.m_in = m;
   a.z_in = z;
   a.scores = scores;
-  const hipError_t e = launch_pass2(L, a, st);
+  const hipError_t e = L.stream_hg ? launch_stream(false, L, a, st) : launch_pass2(L, a, st);
   if (e != hipSuccess) return hip_fail(e, "pass-2 launch");
   return KVC_OK;
 }

@@ -29,9 +29,10 @@ struct Layer {
   int n_sink, n_recent, pool;
   int64_t pos_offset;
   int64_t q_tok, q_head, k_tok, k_head, v_tok, v_head;
-  int n_blocks;       // ceil(s / block)
-  int blocks_per_wg;  // consecutive key blocks scanned by one workgroup
-  int n_split;        // workgroups per KV head
+  int n_blocks;       // ceil(s / block), or stages of the streaming scans
+  int blocks_per_wg;  // consecutive key blocks (stages) scanned by one workgroup
+  int n_split;        // workgroups per KV head (per head group when streaming)
+  int stream_hg;      // 0: per-head scans; 1 or 2: streaming scans with this many heads per workgroup
 };
 
 // Arguments of the two scans and the split combine (passed by value).
@@ -110,6 +111,12 @@ inline int scan_waves(const Layer& L) {
   const int t = L.block / kKeyTile;
   return t < kMaxScanWaves ? t : kMaxScanWaves;
 }
+
+// Streaming scans (G*W <= 128): head-group workgroups with K staged in LDS.
+int stream_tokens(int hg);
+size_t pass1_stream_lds_bytes(const Layer& L);
+size_t pass2_stream_lds_bytes(const Layer& L);
+hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStream_t st);
 
 // Dynamic LDS bytes of the scans.
 size_t pass1_lds_bytes(const Layer& L);
