@@ -124,14 +124,17 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   L.v_tok = d->v_tok_stride ? d->v_tok_stride : (int64_t)d->hkv * d->d;
   L.v_head = d->v_head_stride ? d->v_head_stride : d->d;
 
-  // Streaming scans when each wavefront can hold its head's query rows in
-  // registers; head pairs when the KV heads pair up.
+  // Streaming scans for up to four query-row tiles per KV head; head pairs
+  // when the KV heads pair up and a slot's copy offsets stay in 32 bits.
   L.stream_hg = 0;
-  if (L.row_tiles <= 4 && stream_scans_enabled()) L.stream_hg = L.hkv % 2 == 0 ? 2 : 1;
+  if (L.row_tiles <= 4 && stream_scans_enabled()) {
+    if (L.hkv % 2 == 0 && stream_offsets_fit(L, 2)) L.stream_hg = 2;
+    else if (stream_offsets_fit(L, 1)) L.stream_hg = 1;
+  }
 
   // Partition the key blocks (streaming: stages) of each head (group) over at
   // most kMaxSplit workgroups.
-  const int unit = L.stream_hg ? stream_tokens(L.stream_hg) : L.block;
+  const int unit = L.stream_hg ? stream_tokens(L.d, L.stream_hg) : L.block;
   const int groups = L.stream_hg ? L.hkv / L.stream_hg : L.hkv;
   const int target = L.stream_hg ? stream_wg_target() : score_wg_target();
   L.n_blocks = (int)((L.s + unit - 1) / unit);

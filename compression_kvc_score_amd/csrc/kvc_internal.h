@@ -113,7 +113,8 @@ inline int scan_waves(const Layer& L) {
 }
 
 // Streaming scans (G*W <= 128): head-group workgroups with K staged in LDS.
-int stream_tokens(int hg);
+int stream_tokens(int d, int hg);                  // tokens per ring slot of the streaming scans
+bool stream_offsets_fit(const Layer& L, int hg);  // a slot's copy offsets fit in 32 bits
 size_t pass1_stream_lds_bytes(const Layer& L);
 size_t pass2_stream_lds_bytes(const Layer& L);
 hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStream_t st);

@@ -2,15 +2,20 @@
 // counts G*W <= 128: used whenever its register budget allows.
 //
 // A workgroup of 8 wavefronts owns HG KV heads (a head pair when Hkv is even)
-// and a contiguous token range. K flows through a two-stage LDS ring with
-// direct global->LDS loads: a stage holds TOK tokens x HG heads, and every
-// load instruction moves 1 KiB made of whole HG*256-byte token segments, so
-// DRAM sees long contiguous runs even though K is token-major. Each wavefront
-// keeps its head's G*W window-query rows in VGPRs (the MFMA operand layout,
-// loaded once) and takes one 32-key tile of its head from every stage.
+// and a contiguous token range. K flows through a ring of kRingSlots LDS
+// slots filled by direct global->LDS loads: a slot holds TOKS tokens x HG
+// heads (32 KiB), and every load instruction moves 1 KiB made of whole
+// HG*D*2-byte token segments, so DRAM sees long contiguous runs even though K
+// is token-major. Up to kRingSlots-1 slots are in flight while one is
+// consumed; one LDS-only barrier per slot recycles the slot consumed before.
 //
-// LDS layout of a stage: token r occupies R16 16-byte slots; logical chunk
-// (head h, chunk c) sits in slot (h*CPH + c) XOR (r mod 16), so the 32 lanes
+// The wavefronts of a head split a slot's key tiles and, when a slot holds
+// fewer tiles than that, the head's query-row tiles as well (RS row groups):
+// a wavefront keeps only its own row tiles of Q_win in VGPRs (MFMA operand
+// layout, loaded once) and contracts them with its 32-key tile of every slot.
+//
+// LDS layout of a slot: token r occupies R16 16-byte chunks; logical chunk
+// (head h, chunk c) sits in chunk (h*CPH + c) XOR (r mod XS), so the 32 lanes
 // that read one chunk column of 32 tokens hit distinct banks.
 //
 // The MFMA k-slot assignment matches the per-head scans: at step st, lane
@@ -23,9 +28,13 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSlotBytes = 32768;      // one ring slot
+constexpr int kRingSlots = 4;          // slots in the ring
+constexpr int kRingBytes = kSlotBytes * kRingSlots;
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -34,23 +43,33 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
 
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  if ((nb & 7) != 0) return bid;
+  return (bid & 7) * (nb >> 3) + (bid >> 3);
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& z, float m2, float z2, float c) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  z = z * exp2_raw((m - mn) * c) + z2 * exp2_raw((m2 - mn) * c);
+  m = mn;
+}
+
 // Workgroup barrier that orders LDS traffic only. __syncthreads(), and even a
 // workgroup fence restricted to LDS, also drains every outstanding
-// global->LDS copy, the next stage's included, and so serialises the ring;
-// those copies are waited for explicitly (wait_stage) by the wavefront that
+// global->LDS copy, the later slots' included, and so serialises the ring;
+// those copies are waited for explicitly (wait_slots) by the wavefront that
 // issued them. The memory clobber keeps the compiler from moving memory
 // operations across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// LDS reads inside the ring loop are issued as inline assembly. For a plain
-// LDS load the compiler cannot tell which ring stage it touches, so it waits
-// for every outstanding global->LDS copy, the stage still being filled
-// included; these reads rely on the stage's explicit wait and the barrier
-// instead, and lds_settle() orders their results before any use.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
+// LDS accesses inside the ring loop are issued as inline assembly. For a
+// plain LDS access the compiler cannot tell which ring slot it touches, so it
+// waits for every outstanding global->LDS copy first; these rely on the
+// slot's explicit wait and the barrier instead, and lds_settle() orders their
+// results before any use.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -61,10 +80,24 @@ __device__ __forceinline__ u32x4_t lds_read_b128(const void* p) {
   return v;
 }
 
+__device__ __forceinline__ float lds_read_f32(const void* p) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void lds_write_f32(void* p, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
 // Wait for this wavefront's LDS reads; every value passed through here is
 // read only after the wait.
-template <int N>
-__device__ __forceinline__ void lds_settle(u32x4_t (&v)[N]) {
+template <typename T, int N>
+__device__ __forceinline__ void lds_settle(T (&v)[N]) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
@@ -72,9 +105,9 @@ __device__ __forceinline__ void lds_settle(u32x4_t (&v)[N]) {
 
 // Wait for every outstanding global load of this wavefront and re-define the
 // given registers after the wait. Without this the compiler cannot prove, in
-// the ring loop, that the query registers loaded before it have arrived (the
+// the ring loop, that registers loaded before it have arrived (the
 // global->LDS copies issued since share their counter) and waits for all
-// loads, the next stage's included, before the first MFMA of every stage.
+// copies before their first use in every iteration.
 template <int N, int M>
 __device__ __forceinline__ void vm_settle(uint4 (&q)[N][M]) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -90,105 +123,169 @@ __device__ __forceinline__ void vm_settle(uint4 (&q)[N][M]) {
 
 __device__ __forceinline__ void vm_settle(float& x) { asm volatile("" : "+v"(x)); }
 
-// LDS atomic add without return, as inline assembly for the same reason as
-// the reads above (a plain LDS atomic would first drain the ring's copies).
-__device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
-  asm volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+template <int NI, int K>
+__device__ __forceinline__ void wait_slots(int later);
+
+// As vm_settle, but the `later` slots of ring copies issued after the
+// registers' loads may stay in flight.
+template <int NI, int N, int M>
+__device__ __forceinline__ void vm_settle_after(uint4 (&q)[N][M], int later) {
+  wait_slots<NI, kRingSlots - 1>(later);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      u32x4_t v = __builtin_bit_cast(u32x4_t, q[i][j]);
+      asm volatile("" : "+v"(v));
+      q[i][j] = __builtin_bit_cast(uint4, v);
+    }
 }
 
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
-  if ((nb & 7) != 0) return bid;
-  return (bid & 7) * (nb >> 3) + (bid >> 3);
+// s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& z, float m2, float z2, float c) {
-  const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;
-  z = z * exp2_raw((m - mn) * c) + z2 * exp2_raw((m2 - mn) * c);
-  m = mn;
+// Wait until at most `later` slots' copies (NI instructions each) are still
+// in flight for this wavefront; `later` is wavefront-uniform.
+template <int NI, int K>
+__device__ __forceinline__ void wait_slots(int later) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= K) wait_vmcnt<K * NI>();
+    else wait_slots<NI, K - 1>(later);
+  }
 }
 
 template <int D, int HG>
-struct Cfg {
-  static constexpr int WPH = 8 / HG;              // wavefronts per head
-  static constexpr int TOK = kKeyTile * WPH;      // tokens per stage
-  static constexpr int CPH = D / 8;               // 16-byte chunks per head row
-  static constexpr int R16 = HG * CPH;            // 16-byte slots per token in a stage
-  static constexpr int XS = R16 < 16 ? R16 : 16;  // swizzle span
-  static constexpr int STAGE = TOK * R16 * 16;    // bytes per stage
-  static constexpr int NI = STAGE / (1024 * 8);   // load instructions per wave per stage
-  static constexpr int NCH = D / 16;              // MFMA k-steps
+struct Ring {
+  static constexpr int WAVES = 8;                       // wavefronts per workgroup
+  static constexpr int CPH = D / 8;                     // 16-byte chunks per head row
+  static constexpr int R16 = HG * CPH;                  // chunks per token in a slot
+  static constexpr int XS = R16 < 16 ? R16 : 16;        // swizzle span
+  static constexpr int TOKS = kSlotBytes / (R16 * 16);  // tokens per slot
+  static constexpr int KT = TOKS / kKeyTile;            // key tiles per head per slot
+  static constexpr int WPH = WAVES / HG;                // wavefronts per head
+  static constexpr int RS = WPH / KT;                   // row groups sharing a key tile
+  static constexpr int NI = kSlotBytes / (WAVES * 1024);   // copies per wavefront per slot
+  static_assert(KT >= 1 && WPH % KT == 0 && RS >= 1, "slot geometry");
+  static_assert(kSlotBytes % (WAVES * 1024) == 0, "whole copy instructions per wavefront");
+  static_assert(64 % R16 == 0, "a copy instruction covers whole tokens");
+};
+
+// Wavefront roles: head within the group, key tile within a slot, and row
+// group (row tiles rg, rg + RS, ...).
+struct Role {
+  int hl, kt, rg;
 };
 
 template <int D, int HG>
-__device__ __forceinline__ int slot_of(int r, int h, int c) {
-  using C = Cfg<D, HG>;
-  return r * C::R16 + ((h * C::CPH + c) ^ (r & (C::XS - 1)));
+__device__ __forceinline__ Role role_of(int wave) {
+  using R = Ring<D, HG>;
+  const int sub = wave % R::WPH;
+  return Role{wave / R::WPH, sub % R::KT, sub / R::KT};
 }
 
-// This wavefront's share of one stage's loads (tokens from tok0; tokens past
-// the prompt are clamped to its last key and masked by the consumer).
+// Per-lane byte offsets of this wavefront's copies within a full slot,
+// relative to (first token of the slot, first head of the group); the host
+// only picks this path when they fit in 32 bits.
 template <int D, int HG>
-__device__ __forceinline__ void stage_issue(const ScoreArgs& a, int h0, int tok0, int wave, int lane,
-                                            unsigned char* dst) {
-  using C = Cfg<D, HG>;
+__device__ __forceinline__ void copy_offsets(const ScoreArgs& a, int wave, int lane,
+                                             uint32_t (&off)[Ring<D, HG>::NI]) {
+  using R = Ring<D, HG>;
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-    const int p = (wave * C::NI + j) * 64 + lane;  // slot this lane fills
-    const int r = p / C::R16, q = p % C::R16;
-    const int lc = q ^ (r & (C::XS - 1));
-    const int h = lc / C::CPH, c = lc % C::CPH;
-    int tok = tok0 + r;
-    tok = tok < a.s ? tok : a.s - 1;
-    const uint16_t* src = a.k + (int64_t)tok * a.k_tok + (int64_t)(h0 + h) * a.k_head + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (wave * C::NI + j) * 1024), 16, 0, 0);
+  for (int j = 0; j < R::NI; ++j) {
+    const int p = (wave * R::NI + j) * 64 + lane;
+    const int r = p / R::R16, q = p % R::R16;
+    const int lc = q ^ (r & (R::XS - 1));
+    const int h = lc / R::CPH, c = lc % R::CPH;
+    off[j] = (uint32_t)(((int64_t)r * a.k_tok + (int64_t)h * a.k_head + c * 8) * 2);
   }
 }
 
-// Wait until this wavefront's loads of the stage being consumed have landed:
-// at most `ahead` later stages' loads may still be in flight.
-template <int NI>
-__device__ __forceinline__ void wait_stage(bool next_in_flight) {
-  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8
-  if (next_in_flight) __builtin_amdgcn_s_waitcnt(0x0F70 | (NI & 15) | ((NI >> 4) << 14));
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
+// Copies of the slot that starts at token tok0 into the LDS buffer dst.
+// Tokens past the prompt are clamped to its last key and masked by the
+// consumer.
+template <int D, int HG>
+__device__ __forceinline__ void slot_issue(const ScoreArgs& a, int h0, int tok0, int wave, int lane,
+                                           const uint32_t* off, unsigned char* dst) {
+  using R = Ring<D, HG>;
+  if (tok0 + R::TOKS <= a.s) {
+    const char* base = reinterpret_cast<const char*>(a.k + (int64_t)tok0 * a.k_tok + (int64_t)h0 * a.k_head);
+#pragma unroll
+    for (int j = 0; j < R::NI; ++j)
+      __builtin_amdgcn_global_load_lds(base + off[j], (lds_void*)(dst + (wave * R::NI + j) * 1024), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < R::NI; ++j) {
+      const int p = (wave * R::NI + j) * 64 + lane;
+      const int r = p / R::R16, q = p % R::R16;
+      const int lc = q ^ (r & (R::XS - 1));
+      const int h = lc / R::CPH, c = lc % R::CPH;
+      int tok = tok0 + r;
+      tok = tok < a.s ? tok : a.s - 1;
+      const uint16_t* src = a.k + (int64_t)tok * a.k_tok + (int64_t)(h0 + h) * a.k_head + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (wave * R::NI + j) * 1024), 16, 0, 0);
+    }
+  }
 }
 
-// The wavefront's head rows of Q_win in MFMA operand layout: row tile t, step st.
-template <int D, int NRT>
-__device__ __forceinline__ void load_query_regs(const ScoreArgs& a, int head, int half, int l32,
-                                                uint4 (&qr)[NRT][D / 16]) {
+// The wavefront's row tiles (rg, rg + RS, ...) of its head's Q_win rows in
+// MFMA operand layout; rows past G*W (and tiles past nrt) are zero.
+template <int D, int NRTW, int RS>
+__device__ __forceinline__ void load_query_regs(const ScoreArgs& a, int head, int rg, int nrt, int half,
+                                                int l32, uint4 (&qr)[NRTW][D / 16]) {
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) {
+  for (int i = 0; i < NRTW; ++i) {
+    const int t = rg + RS * i;
     const int r = t * kRowTile + l32;
-    const bool ok = r < a.rows;
-    const int hh = ok ? r / a.w : 0, i = ok ? r % a.w : 0;
-    const uint16_t* src = a.q + (int64_t)i * a.q_tok + (int64_t)(head * a.g + hh) * a.q_head;
+    const bool ok = t < nrt && r < a.rows;
+    const int hh = ok ? r / a.w : 0, wi = ok ? r % a.w : 0;
+    const uint16_t* src = a.q + (int64_t)wi * a.q_tok + (int64_t)(head * a.g + hh) * a.q_head;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
-      qr[t][st] = ok ? *reinterpret_cast<const uint4*>(src + (2 * st + half) * 8) : make_uint4(0u, 0u, 0u, 0u);
+      qr[i][st] = ok ? *reinterpret_cast<const uint4*>(src + (2 * st + half) * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
+// This lane's MFMA operand chunks of key tile kt of head hl in a slot. The
+// reads are only issued here; key_settle() waits for them.
 template <int D, int HG>
-__device__ __forceinline__ void load_key_regs(const unsigned char* stage, int hl, int kt, int half,
-                                              int l32, uint4 (&kf)[D / 16]) {
+__device__ __forceinline__ void key_issue(const unsigned char* slot, int hl, int kt, int half, int l32,
+                                          u32x4_t (&raw)[D / 16]) {
+  using R = Ring<D, HG>;
   const int r = kt * kKeyTile + l32;
-  u32x4_t raw[D / 16];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) raw[st] = lds_read_b128(stage + slot_of<D, HG>(r, hl, 2 * st + half) * 16);
-  lds_settle(raw);
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) kf[st] = make_uint4(raw[st][0], raw[st][1], raw[st][2], raw[st][3]);
+  for (int st = 0; st < D / 16; ++st) {
+    const int chunk = r * R::R16 + ((hl * R::CPH + 2 * st + half) ^ (r & (R::XS - 1)));
+    raw[st] = lds_read_b128(slot + chunk * 16);
+  }
 }
 
-template <int D, int NRT, bool KROWS>
-__device__ __forceinline__ f32x16_t contract(const uint4 (&qr)[NRT][D / 16], const uint4 (&kf)[D / 16],
-                                             int t) {
+template <int D>
+__device__ __forceinline__ void key_settle(u32x4_t (&raw)[D / 16], uint4 (&kf)[D / 16]) {
+  lds_settle(raw);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) kf[st] = __builtin_bit_cast(uint4, raw[st]);
+}
+
+template <int D, int HG>
+__device__ __forceinline__ void load_key_regs(const unsigned char* slot, int hl, int kt, int half, int l32,
+                                              uint4 (&kf)[D / 16]) {
+  u32x4_t raw[D / 16];
+  key_issue<D, HG>(slot, hl, kt, half, l32, raw);
+  key_settle<D>(raw, kf);
+}
+
+template <int D, int NRTW, bool KROWS>
+__device__ __forceinline__ f32x16_t contract(const uint4 (&qr)[NRTW][D / 16], const uint4 (&kf)[D / 16], int i) {
   f32x16_t acc = {};
 #pragma unroll
   for (int st = 0; st < D / 16; ++st)
-    acc = KROWS ? mfma32x32x16(kf[st], qr[t][st], acc) : mfma32x32x16(qr[t][st], kf[st], acc);
+    acc = KROWS ? mfma32x32x16(kf[st], qr[i][st], acc) : mfma32x32x16(qr[i][st], kf[st], acc);
   return acc;
 }
 
@@ -202,24 +299,50 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
 }
 
 struct Range {
-  int t0, nst;  // first token, stages
+  int t0, nst;  // first token, slots
 };
 
-__device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int tok_per_stage) {
+__device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int toks) {
   Range r;
-  r.t0 = split * a.blocks_per_wg * tok_per_stage;
-  int t1 = r.t0 + a.blocks_per_wg * tok_per_stage;
+  r.t0 = split * a.blocks_per_wg * toks;
+  int t1 = r.t0 + a.blocks_per_wg * toks;
   t1 = t1 < a.s ? t1 : a.s;
-  r.nst = (t1 - r.t0 + tok_per_stage - 1) / tok_per_stage;
+  r.nst = (t1 - r.t0 + toks - 1) / toks;
   return r;
+}
+
+// Ring prologue: copies of slots 0 .. kRingSlots-2.
+template <int D, int HG>
+__device__ __forceinline__ void ring_fill(const ScoreArgs& a, int h0, const Range& rg, int wave, int lane,
+                                          const uint32_t* off, unsigned char* smem) {
+  using R = Ring<D, HG>;
+#pragma unroll
+  for (int n = 0; n < kRingSlots - 1; ++n)
+    if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.t0 + n * R::TOKS, wave, lane, off, smem + n * kSlotBytes);
+}
+
+// Top of ring iteration n: slot n has landed for the whole workgroup, and
+// every wavefront is done with slot n-1, whose buffer then takes slot
+// n + kRingSlots - 1.
+template <int D, int HG>
+__device__ __forceinline__ void ring_advance(const ScoreArgs& a, int h0, const Range& rg, int n, int wave,
+                                             int lane, const uint32_t* off,
+                                             unsigned char* smem) {
+  using R = Ring<D, HG>;
+  const int later = min(kRingSlots - 2, rg.nst - 1 - n);
+  wait_slots<R::NI, kRingSlots - 2>(later);
+  lds_barrier();
+  const int nn = n + kRingSlots - 1;
+  if (nn < rg.nst)
+    slot_issue<D, HG>(a, h0, rg.t0 + nn * R::TOKS, wave, lane, off, smem + (nn % kRingSlots) * kSlotBytes);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 1
 // ---------------------------------------------------------------------------
 template <bool EDGE>
-__device__ __forceinline__ void lse_update(const ScoreArgs& a, f32x16_t acc, int kbase, int half,
-                                           int qpos, float& mrun, float& zrun) {
+__device__ __forceinline__ void lse_update(const ScoreArgs& a, f32x16_t acc, int kbase, int half, int qpos,
+                                           float& mrun, float& zrun) {
   if constexpr (EDGE) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -240,102 +363,185 @@ __device__ __forceinline__ void lse_update(const ScoreArgs& a, f32x16_t acc, int
   mrun = mnew;
 }
 
-template <int D, int NRT, bool EDGE>
-__device__ __forceinline__ void pass1_tile(const ScoreArgs& a, const uint4 (&qr)[NRT][D / 16],
-                                           const uint4 (&kf)[D / 16], int kbase, int half,
-                                           const int (&qpos)[NRT], float (&mrun)[NRT],
-                                           float (&zrun)[NRT]) {
-  if constexpr (NRT <= 2) {
-    // software-pipelined: the MFMAs of row tile t+1 overlap the VALU of t
-    f32x16_t acc[2];
-    acc[0] = contract<D, NRT, true>(qr, kf, 0);
+// Pass-1 update of one (slot, row tile) job whose dot products are in acc,
+// with the MFMA chain of the next job (keys kf, query rows q) woven in: one
+// MFMA, then the exponentials of 16 / (D / 16) logits, so that the matrix
+// pipe and the VALU work side by side. Returns the next job's dot products.
+template <int D, bool EDGE>
+__device__ __forceinline__ f32x16_t lse_update_mfma(const ScoreArgs& a, f32x16_t acc, int kbase, int half,
+                                                    int qpos, float& mrun, float& zrun, const uint4 (&kf)[D / 16],
+                                                    const uint4 (&q)[D / 16]) {
+  constexpr int NST = D / 16, PER = 16 / NST;
+  if constexpr (EDGE) {
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      if (t + 1 < NRT) acc[(t + 1) & 1] = contract<D, NRT, true>(qr, kf, t + 1);
-      lse_update<EDGE>(a, acc[t & 1], kbase, half, qpos[t], mrun[t], zrun[t]);
+    for (int e = 0; e < 16; ++e) {
+      const int key = kbase + 8 * (e >> 2) + 4 * half + (e & 3);
+      if (key >= a.s || key > qpos) acc[e] = -INFINITY;
+    }
+  }
+  const float mnew = fmaxf(mrun, max16(acc));
+  const bool dead = EDGE && mnew == -INFINITY;  // every key masked: contributes nothing
+  const float mc = dead ? 0.f : mnew * a.c;
+  f32x16_t nxt = {};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    nxt = mfma32x32x16(kf[st], q[st], nxt);
+#pragma unroll
+    for (int e = st * PER; e < (st + 1) * PER; e += 2) {
+      s0 += exp2_raw(fmaf(acc[e], a.c, -mc));
+      s1 += exp2_raw(fmaf(acc[e + 1], a.c, -mc));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!dead) {
+    zrun = zrun * exp2_raw((mrun - mnew) * a.c) + (s0 + s1);
+    mrun = mnew;
+  }
+  return nxt;
+}
+
+// ntile: row tiles this wavefront owns (wavefront-uniform, <= NRTW); FULL:
+// every wavefront owns NRTW (known at compile time).
+template <int D, int NRTW, bool FULL, bool EDGE>
+__device__ __forceinline__ void pass1_tile(const ScoreArgs& a, const uint4 (&qr)[NRTW][D / 16],
+                                           const uint4 (&kf)[D / 16], int kbase, int half, int ntile,
+                                           const int (&qpos)[NRTW], float (&mrun)[NRTW], float (&zrun)[NRTW]) {
+  if constexpr (NRTW <= 2) {
+    // software-pipelined: the MFMAs of row tile i+1 overlap the VALU of i
+    f32x16_t acc[2];
+    acc[0] = contract<D, NRTW, true>(qr, kf, 0);
+#pragma unroll
+    for (int i = 0; i < NRTW; ++i) {
+      const bool next = i + 1 < NRTW && (FULL || i + 1 < ntile);
+      if (next) acc[(i + 1) & 1] = contract<D, NRTW, true>(qr, kf, i + 1);
+      if (FULL || i < ntile) lse_update<EDGE>(a, acc[i & 1], kbase, half, qpos[i], mrun[i], zrun[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    // register budget: one accumulator; the second wavefront on the SIMD
+    // register budget: one accumulator; the other wavefront on the SIMD
     // overlaps its MFMAs with this one's VALU
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      lse_update<EDGE>(a, contract<D, NRT, true>(qr, kf, t), kbase, half, qpos[t], mrun[t], zrun[t]);
+    for (int i = 0; i < NRTW; ++i) {
+      if (i < ntile) lse_update<EDGE>(a, contract<D, NRTW, true>(qr, kf, i), kbase, half, qpos[i], mrun[i], zrun[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 template <int D, int NRT, int HG>
-__global__ void __launch_bounds__(512) pass1_stream_kernel(ScoreArgs a) {
-  using C = Cfg<D, HG>;
-  extern __shared__ __align__(16) unsigned char smem[];
+__global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
   constexpr int ROWS_PAD = NRT * kRowTile;
+  extern __shared__ __align__(16) unsigned char smem[];
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = work / a.n_split, split = work % a.n_split;
   const int h0 = grp * HG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront-uniform: SGPRs
   const int half = lane >> 5, l32 = lane & 31;
-  const int hl = wave / C::WPH, kt = wave % C::WPH;
-  const int head = h0 + hl;
+  const Role ro = role_of<D, HG>(wave);
+  const int head = h0 + ro.hl;
+  const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;  // the last row groups may own one fewer
   const int first_hidden = a.s - a.w + 1;
-  const Range rg = wg_range(a, split, C::TOK);
+  const Range rg = wg_range(a, split, R::TOKS);
 
   if (a.hist != nullptr && split == 0)
     for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x) a.hist[(int64_t)h0 * kHistBins + i] = 0u;
 
-  stage_issue<D, HG>(a, h0, rg.t0, wave, lane, smem);
-  uint4 qr[NRT][D / 16];
-  load_query_regs<D, NRT>(a, head, half, l32, qr);
-  vm_settle(qr);
-  if (rg.nst > 1) stage_issue<D, HG>(a, h0, rg.t0 + C::TOK, wave, lane, smem + C::STAGE);
+  uint32_t off[R::NI];
+  copy_offsets<D, HG>(a, wave, lane, off);
+  uint4 qr[NRTW][D / 16];
+  load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem);
+  vm_settle_after<R::NI>(qr, min(rg.nst, kRingSlots - 1));
 
-  float mrun[NRT], zrun[NRT];
-  int qpos[NRT];
+  float mrun[NRTW], zrun[NRTW];
+  int qpos[NRTW];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    mrun[t] = -INFINITY;
-    zrun[t] = 0.f;
-    const int r = t * kRowTile + l32;
-    qpos[t] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
+  for (int i = 0; i < NRTW; ++i) {
+    mrun[i] = -INFINITY;
+    zrun[i] = 0.f;
+    const int r = (ro.rg + R::RS * i) * kRowTile + l32;
+    qpos[i] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
   }
 
-  for (int st = 0; st < rg.nst; ++st) {
-    wait_stage<C::NI>(st + 1 < rg.nst);
-    lds_barrier();
-    const unsigned char* stage = smem + (st & 1) * C::STAGE;
-    const int kbase = rg.t0 + st * C::TOK + kt * kKeyTile;
-    if (kbase < a.s) {
-      uint4 kf[D / 16];
-      load_key_regs<D, HG>(stage, hl, kt, half, l32, kf);
-      if (kbase + kKeyTile <= first_hidden)
-        pass1_tile<D, NRT, false>(a, qr, kf, kbase, half, qpos, mrun, zrun);
-      else
-        pass1_tile<D, NRT, true>(a, qr, kf, kbase, half, qpos, mrun, zrun);
+  constexpr bool PIPE = NRT % R::RS == 0;
+  if constexpr (PIPE) {
+    // Jobs (slot n, row tile i) in order; the MFMAs of each job run beside
+    // the VALU work of the one before, across slot boundaries too. Jobs past
+    // the prompt compute on clamped keys and are masked out.
+    constexpr int LAST = NRTW - 1;
+    const int kt_off = ro.kt * kKeyTile;
+    uint4 kf[D / 16];
+    f32x16_t A;
+    if (rg.nst > 0) {
+      ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
+      load_key_regs<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
+      A = contract<D, NRTW, true>(qr, kf, 0);
     }
-    lds_barrier();
-    if (st + 2 < rg.nst) stage_issue<D, HG>(a, h0, rg.t0 + (st + 2) * C::TOK, wave, lane, smem + (st & 1) * C::STAGE);
+    for (int n = 0; n < rg.nst; ++n) {
+      const int kbase = rg.t0 + n * R::TOKS + kt_off;
+      const bool edge = kbase + kKeyTile > first_hidden;
+      const bool more = n + 1 < rg.nst;
+      // the next slot's key reads overlap this slot's remaining jobs
+      u32x4_t raw[D / 16];
+      if (more) {
+        ring_advance<D, HG>(a, h0, rg, n + 1, wave, lane, off, smem);
+        key_issue<D, HG>(smem + ((n + 1) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, raw);
+      }
+#pragma unroll
+      for (int i = 0; i < LAST; ++i)
+        A = edge ? lse_update_mfma<D, true>(a, A, kbase, half, qpos[i], mrun[i], zrun[i], kf, qr[i + 1])
+                 : lse_update_mfma<D, false>(a, A, kbase, half, qpos[i], mrun[i], zrun[i], kf, qr[i + 1]);
+      if (more) {
+        key_settle<D>(raw, kf);
+        A = edge ? lse_update_mfma<D, true>(a, A, kbase, half, qpos[LAST], mrun[LAST], zrun[LAST], kf, qr[0])
+                 : lse_update_mfma<D, false>(a, A, kbase, half, qpos[LAST], mrun[LAST], zrun[LAST], kf, qr[0]);
+      } else {
+        if (edge) lse_update<true>(a, A, kbase, half, qpos[LAST], mrun[LAST], zrun[LAST]);
+        else lse_update<false>(a, A, kbase, half, qpos[LAST], mrun[LAST], zrun[LAST]);
+      }
+    }
+  } else {
+    for (int n = 0; n < rg.nst; ++n) {
+      ring_advance<D, HG>(a, h0, rg, n, wave, lane, off, smem);
+      const unsigned char* slot = smem + (n % kRingSlots) * kSlotBytes;
+      const int kbase = rg.t0 + n * R::TOKS + ro.kt * kKeyTile;
+      if (kbase < a.s) {
+        uint4 kf[D / 16];
+        load_key_regs<D, HG>(slot, ro.hl, ro.kt, half, l32, kf);
+        if (kbase + kKeyTile <= first_hidden)
+          pass1_tile<D, NRTW, NRT % R::RS == 0, false>(a, qr, kf, kbase, half, ntile, qpos, mrun, zrun);
+        else
+          pass1_tile<D, NRTW, NRT % R::RS == 0, true>(a, qr, kf, kbase, half, ntile, qpos, mrun, zrun);
+      }
+    }
   }
 
-  // lanes l and l+32 share a query row; then the WPH wavefronts of a head
+  // lanes l and l+32 share a query row; then the KT wavefronts of a head
+  // that own the same rows
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    const float mo = __shfl_xor(mrun[t], 32);
-    const float zo = __shfl_xor(zrun[t], 32);
-    lse_merge(mrun[t], zrun[t], mo, zo, a.c);
+  for (int i = 0; i < NRTW; ++i) {
+    const float mo = __shfl_xor(mrun[i], 32);
+    const float zo = __shfl_xor(zrun[i], 32);
+    lse_merge(mrun[i], zrun[i], mo, zo, a.c);
   }
-  float2* red = reinterpret_cast<float2*>(smem);  // the ring is idle now
+  __syncthreads();  // the ring is idle now: every copy was waited for
+  float2* red = reinterpret_cast<float2*>(smem);  // [HG][KT][ROWS_PAD]
   if (half == 0) {
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) red[wave * ROWS_PAD + t * kRowTile + l32] = make_float2(mrun[t], zrun[t]);
+    for (int i = 0; i < NRTW; ++i)
+      if (i < ntile)
+        red[(ro.hl * R::KT + ro.kt) * ROWS_PAD + (ro.rg + R::RS * i) * kRowTile + l32] = make_float2(mrun[i], zrun[i]);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < HG * a.rows; idx += blockDim.x) {
     const int h = idx / a.rows, r = idx % a.rows;
     float m = -INFINITY, z = 0.f;
-    for (int k = 0; k < C::WPH; ++k) {
-      const float2 p = red[(h * C::WPH + k) * ROWS_PAD + r];
+    for (int k = 0; k < R::KT; ++k) {
+      const float2 p = red[(h * R::KT + k) * ROWS_PAD + r];
       lse_merge(m, z, p.x, p.y, a.c);
     }
     reinterpret_cast<float2*>(a.part)[((int64_t)(h0 + h) * a.n_split + split) * ROWS_PAD + r] = make_float2(m, z);
@@ -345,54 +551,57 @@ __global__ void __launch_bounds__(512) pass1_stream_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Pass 2
 // ---------------------------------------------------------------------------
-// qpos: per row, the prompt position of its query (-1 for padding rows),
-// read from LDS inside the loop so that nothing per row lives in registers.
+// bias / qpos: per row of the head, log2 of the normaliser and the prompt
+// position of its query (-1 for padding rows), read from LDS inside the loop
+// so that nothing per row lives in registers.
 template <bool EDGE>
 __device__ __forceinline__ void weight_sum(const ScoreArgs& a, const f32x16_t& acc, const float* bias,
-                                           const int* qpos, int t, int key, int half, float& s0,
-                                           float& s1) {
+                                           const int* qpos, int t, int key, int half, float& s0, float& s1) {
   const int o = t * kRowTile + 4 * half;
-  u32x4_t bq[4];
+  // two rounds of 8 rows keep the register footprint small
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) bq[q4] = lds_read_b128(bias + o + 8 * q4);
-  lds_settle(bq);
+  for (int q2 = 0; q2 < 4; q2 += 2) {
+    u32x4_t bq[2] = {lds_read_b128(bias + o + 8 * q2), lds_read_b128(bias + o + 8 * q2 + 8)};
+    lds_settle(bq);
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    u32x4_t qv = {0u, 0u, 0u, 0u};
-    if constexpr (EDGE) {
-      u32x4_t q1[1] = {lds_read_b128(qpos + o + 8 * q4)};
-      lds_settle(q1);
-      qv = q1[0];
-    }
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      float p = exp2_raw(fmaf(acc[4 * q4 + e4], a.c, -__uint_as_float(bq[q4][e4])));
+    for (int q1 = 0; q1 < 2; ++q1) {
+      const int q4 = q2 + q1;
+      u32x4_t qv = {0u, 0u, 0u, 0u};
       if constexpr (EDGE) {
-        if (key >= a.s || key > (int)qv[e4]) p = 0.f;
+        u32x4_t qq[1] = {lds_read_b128(qpos + o + 8 * q4)};
+        lds_settle(qq);
+        qv = qq[0];
       }
-      if (e4 & 1) s1 += p; else s0 += p;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        float p = exp2_raw(fmaf(acc[4 * q4 + e4], a.c, -__uint_as_float(bq[q1][e4])));
+        if constexpr (EDGE) {
+          if (key >= a.s || key > (int)qv[e4]) p = 0.f;
+        }
+        if (e4 & 1) s1 += p; else s0 += p;
+      }
     }
   }
 }
 
-template <int D, int NRT, bool EDGE>
-__device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr)[NRT][D / 16],
-                                            const uint4 (&kf)[D / 16], const float* bias,
-                                            const int* qpos, int key, int half) {
+template <int D, int NRTW, int RS, bool EDGE>
+__device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr)[NRTW][D / 16],
+                                            const uint4 (&kf)[D / 16], const float* bias, const int* qpos,
+                                            int key, int half, int rg, int ntile) {
   float s0 = 0.f, s1 = 0.f;
-  if constexpr (NRT <= 2) {
+  if constexpr (NRTW <= 2) {
     f32x16_t acc[2];
-    acc[0] = contract<D, NRT, false>(qr, kf, 0);
+    acc[0] = contract<D, NRTW, false>(qr, kf, 0);
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      if (t + 1 < NRT) acc[(t + 1) & 1] = contract<D, NRT, false>(qr, kf, t + 1);
-      weight_sum<EDGE>(a, acc[t & 1], bias, qpos, t, key, half, s0, s1);
+    for (int i = 0; i < NRTW; ++i) {
+      if (i + 1 < NRTW && i + 1 < ntile) acc[(i + 1) & 1] = contract<D, NRTW, false>(qr, kf, i + 1);
+      if (i < ntile) weight_sum<EDGE>(a, acc[i & 1], bias, qpos, rg + RS * i, key, half, s0, s1);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      weight_sum<EDGE>(a, contract<D, NRT, false>(qr, kf, t), bias, qpos, t, key, half, s0, s1);
+    for (int i = 0; i < NRTW; ++i) {
+      if (i < ntile) weight_sum<EDGE>(a, contract<D, NRTW, false>(qr, kf, i), bias, qpos, rg + RS * i, key, half, s0, s1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -400,14 +609,26 @@ __device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr
   return s + __shfl_xor(s, 32);
 }
 
+// Store a key's score and count it in the head's LDS histogram.
+__device__ __forceinline__ void emit_score(const ScoreArgs& a, float* out, uint32_t* lh, bool with_hist, int key,
+                                           float sum) {
+  out[key] = sum;
+  if (with_hist && key >= a.sink_end && key < a.rec_begin) {
+    const uint32_t b = (__float_as_uint(sum) >> 19) & (kHistBins - 1);
+    lds_add_u32(&lh[b >> 1], 1u << ((b & 1) * 16));
+  }
+}
+
 template <int D, int NRT, int HG>
-__global__ void __launch_bounds__(512) pass2_stream_kernel(ScoreArgs a) {
-  using C = Cfg<D, HG>;
-  extern __shared__ __align__(16) unsigned char smem[];
+__global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
   constexpr int ROWS_PAD = NRT * kRowTile;
-  float* bias_all = reinterpret_cast<float*>(smem + 2 * C::STAGE);          // [HG][ROWS_PAD]
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* bias_all = reinterpret_cast<float*>(smem + kRingBytes);            // [HG][ROWS_PAD]
   int* qpos_all = reinterpret_cast<int*>(bias_all + HG * ROWS_PAD);         // [HG][ROWS_PAD]
   uint32_t* hist2 = reinterpret_cast<uint32_t*>(qpos_all + HG * ROWS_PAD);  // [HG][kHistBins/2], u16 pairs
+  float* psum = reinterpret_cast<float*>(hist2 + HG * (kHistBins / 2));     // [2][HG][KT][RS][32]
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = work / a.n_split, split = work % a.n_split;
@@ -415,16 +636,18 @@ __global__ void __launch_bounds__(512) pass2_stream_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront-uniform: SGPRs
   const int half = lane >> 5, l32 = lane & 31;
-  const int hl = wave / C::WPH, kt = wave % C::WPH;
-  const int head = h0 + hl;
+  const Role ro = role_of<D, HG>(wave);
+  const int head = h0 + ro.hl;
+  const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;
   const int first_hidden = a.s - a.w + 1;
-  const Range rg = wg_range(a, split, C::TOK);
+  const Range rg = wg_range(a, split, R::TOKS);
 
-  stage_issue<D, HG>(a, h0, rg.t0, wave, lane, smem);
-  uint4 qr[NRT][D / 16];
-  load_query_regs<D, NRT>(a, head, half, l32, qr);
+  uint32_t off[R::NI];
+  copy_offsets<D, HG>(a, wave, lane, off);
+  uint4 qr[NRTW][D / 16];
+  load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
   // this thread's normaliser (one bias entry per thread)
-  static_assert(HG * ROWS_PAD <= 512, "one bias entry per thread");
+  static_assert(HG * ROWS_PAD <= R::WAVES * kWave, "one bias entry per thread");
   const int bidx = threadIdx.x;
   float mv = 0.f, zv = 1.f;
   bool real_row = false;
@@ -437,7 +660,8 @@ __global__ void __launch_bounds__(512) pass2_stream_kernel(ScoreArgs a) {
       real_row = true;
     }
   }
-  vm_settle(qr);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem);
+  vm_settle_after<R::NI>(qr, min(rg.nst, kRingSlots - 1));
   vm_settle(mv);
   vm_settle(zv);
 
@@ -449,34 +673,54 @@ __global__ void __launch_bounds__(512) pass2_stream_kernel(ScoreArgs a) {
   const bool with_hist = a.hist != nullptr;
   if (with_hist)
     for (int i = threadIdx.x; i < HG * kHistBins / 2; i += blockDim.x) hist2[i] = 0u;
-  if (rg.nst > 1) stage_issue<D, HG>(a, h0, rg.t0 + C::TOK, wave, lane, smem + C::STAGE);
-  const float* bias = bias_all + hl * ROWS_PAD;
-  const int* qpos = qpos_all + hl * ROWS_PAD;
-  uint32_t* lh = hist2 + hl * (kHistBins / 2);
-  float* out = a.scores + (int64_t)head * a.s;
 
-  for (int st = 0; st < rg.nst; ++st) {
-    wait_stage<C::NI>(st + 1 < rg.nst);
-    lds_barrier();
-    const unsigned char* stage = smem + (st & 1) * C::STAGE;
-    const int kbase = rg.t0 + st * C::TOK + kt * kKeyTile;
+  const float* bias = bias_all + ro.hl * ROWS_PAD;
+  const int* qpos = qpos_all + ro.hl * ROWS_PAD;
+  uint32_t* lh = hist2 + ro.hl * (kHistBins / 2);
+  float* out = a.scores + (int64_t)head * a.s;
+  // row-group partial sums of slot n: psum[n & 1][hl][kt][rg][key]
+  auto psum_at = [&](int n, int g) {
+    return psum + ((((n & 1) * HG + ro.hl) * R::KT + ro.kt) * R::RS + g) * kKeyTile + l32;
+  };
+  // the first row group adds the partials of slot n in a fixed order
+  auto finish = [&](int n) {
+    const int key = rg.t0 + n * R::TOKS + ro.kt * kKeyTile + l32;
+    if (ro.rg == 0 && half == 0 && key < a.s) {
+      float v[R::RS];
+#pragma unroll
+      for (int g = 0; g < R::RS; ++g) v[g] = lds_read_f32(psum_at(n, g));
+      lds_settle(v);
+      float sum = v[0];
+#pragma unroll
+      for (int g = 1; g < R::RS; ++g) sum += v[g];
+      emit_score(a, out, lh, with_hist, key, sum);
+    }
+  };
+
+  for (int n = 0; n < rg.nst; ++n) {
+    ring_advance<D, HG>(a, h0, rg, n, wave, lane, off, smem);
+    if constexpr (R::RS > 1) {
+      if (n > 0) finish(n - 1);
+    }
+    const unsigned char* slot = smem + (n % kRingSlots) * kSlotBytes;
+    const int kbase = rg.t0 + n * R::TOKS + ro.kt * kKeyTile;
     if (kbase < a.s) {
       uint4 kf[D / 16];
-      load_key_regs<D, HG>(stage, hl, kt, half, l32, kf);
+      load_key_regs<D, HG>(slot, ro.hl, ro.kt, half, l32, kf);
       const int key = kbase + l32;
       const float sum = kbase + kKeyTile <= first_hidden
-                            ? pass2_tile<D, NRT, false>(a, qr, kf, bias, qpos, key, half)
-                            : pass2_tile<D, NRT, true>(a, qr, kf, bias, qpos, key, half);
-      if (half == 0 && key < a.s) {
-        out[key] = sum;
-        if (with_hist && key >= a.sink_end && key < a.rec_begin) {
-          const uint32_t b = (__float_as_uint(sum) >> 19) & (kHistBins - 1);
-          lds_add_u32(&lh[b >> 1], 1u << ((b & 1) * 16));
-        }
+                            ? pass2_tile<D, NRTW, R::RS, false>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile)
+                            : pass2_tile<D, NRTW, R::RS, true>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile);
+      if constexpr (R::RS > 1) {
+        if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
+      } else {
+        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum);
       }
     }
+  }
+  if constexpr (R::RS > 1) {
     lds_barrier();
-    if (st + 2 < rg.nst) stage_issue<D, HG>(a, h0, rg.t0 + (st + 2) * C::TOK, wave, lane, smem + (st & 1) * C::STAGE);
+    if (rg.nst > 0) finish(rg.nst - 1);
   }
   if (with_hist) {
     __syncthreads();
@@ -522,25 +766,31 @@ const void* stream_fn(bool pass1, const Layer& L) {
   return pass1 ? pass1_stream_fn<64, 1>(L.row_tiles) : pass2_stream_fn<64, 1>(L.row_tiles);
 }
 
-size_t stage_bytes(const Layer& L) {
-  const int tok = kKeyTile * 8 / L.stream_hg;
-  return (size_t)tok * L.stream_hg * (L.d / 8) * 16;
+int slot_key_tiles(const Layer& L) {
+  if (L.d == 128) return L.stream_hg == 2 ? Ring<128, 2>::KT : Ring<128, 1>::KT;
+  return L.stream_hg == 2 ? Ring<64, 2>::KT : Ring<64, 1>::KT;
 }
 
 }  // namespace
 
-int stream_tokens(int hg) { return kKeyTile * 8 / hg; }
+int stream_tokens(int d, int hg) { return kSlotBytes / (hg * d * 2); }
+
+bool stream_offsets_fit(const Layer& L, int hg) {
+  const int64_t toks = stream_tokens(L.d, hg);
+  const int64_t span = ((toks - 1) * L.k_tok + (int64_t)(hg - 1) * L.k_head + L.d) * 2;
+  return span < (1LL << 32);
+}
 
 size_t pass1_stream_lds_bytes(const Layer& L) {
-  const size_t ring = 2 * stage_bytes(L);
-  const size_t red = (size_t)8 * L.row_tiles * kRowTile * sizeof(float2);
-  return ring > red ? ring : red;
+  const size_t red = (size_t)L.stream_hg * slot_key_tiles(L) * L.row_tiles * kRowTile * sizeof(float2);
+  return red > (size_t)kRingBytes ? red : (size_t)kRingBytes;
 }
 
 size_t pass2_stream_lds_bytes(const Layer& L) {
   const size_t rows_pad = (size_t)L.row_tiles * kRowTile;
-  return 2 * stage_bytes(L) + L.stream_hg * rows_pad * (sizeof(float) + sizeof(int)) +
-         (size_t)L.stream_hg * (kHistBins / 2) * sizeof(uint32_t);
+  const size_t psum = (size_t)2 * 8 * kKeyTile * sizeof(float);  // [2][HG][KT][RS][32]
+  return kRingBytes + L.stream_hg * rows_pad * (sizeof(float) + sizeof(int)) +
+         (size_t)L.stream_hg * (kHistBins / 2) * sizeof(uint32_t) + psum;
 }
 
 hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStream_t st) {
