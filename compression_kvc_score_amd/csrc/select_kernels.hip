@@ -28,6 +28,7 @@
 // which workgroups run.
 
 #include "kvc_internal.h"
+#include "wave_ops.h"
 
 namespace kvc {
 namespace {
@@ -42,30 +43,19 @@ __device__ __forceinline__ uint32_t bin_of(uint32_t bits) { return (bits >> 19) 
 // returns the total. Uses `scratch` (kWaves + 1 entries) in LDS.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_inclusive_sum(v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t w = lane < kWaves ? scratch[lane] : 0u;
-    uint32_t wi = w;
+  uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int off = 1; off < kWaves; off <<= 1) {
-      const uint32_t o = __shfl_up(wi, off);
-      if (lane >= off) wi += o;
-    }
-    if (lane < kWaves) scratch[lane] = wi - w;  // exclusive wave offsets
-    if (lane == kWaves - 1) scratch[kWaves] = wi;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = scratch[w];
+    before += w < wave ? t : 0u;
+    all += t;
   }
+  total = all;
   __syncthreads();
-  const uint32_t res = scratch[wave] + incl - v;
-  total = scratch[kWaves];
-  __syncthreads();
-  return res;
+  return before + incl - v;
 }
 
 struct HeadGeom {
@@ -173,21 +163,26 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
   const HeadGeom h = head_geom(a, head);
   if (h.keep_all || h.k_sel == 0) return;
+  // this thread's four values, loaded before the histogram scan so that the
+  // two memory round trips overlap
+  const float* vals = a.vals + (int64_t)head * h.s;
+  const int64_t j0 = (int64_t)chunk * kChunk + 4 * threadIdx.x;
+  uint32_t bits[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t j = j0 + e;
+    bits[e] = (j < h.s && j >= h.sink_end && j < h.rec_begin) ? __float_as_uint(vals[j]) : 0u;
+  }
   uint32_t bstar, above_all;
   find_bin(a.hist + (int64_t)head * kHistBins, h.k_sel, scratch, bstar, above_all);
 
-  const float* vals = a.vals + (int64_t)head * h.s;
-  const int64_t j0 = (int64_t)chunk * kChunk + 4 * threadIdx.x;
   uint32_t above = 0, nin = 0;
-  uint32_t bits[4];
   bool in[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t j = j0 + e;
     in[e] = false;
-    bits[e] = 0u;
     if (j < h.s && j >= h.sink_end && j < h.rec_begin) {
-      bits[e] = __float_as_uint(vals[j]);
       const uint32_t b = bin_of(bits[e]);
       above += b > bstar;
       in[e] = b == bstar;
@@ -241,12 +236,7 @@ __device__ uint32_t radix_over_row(const HeadGeom& h, const uint32_t* bits, uint
       uint32_t c[4], loc = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) { c[q] = hist256[255 - 4 * l - q]; loc += c[q]; }
-      uint32_t incl = loc;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (l >= off) incl += o;
-      }
+      const uint32_t incl = wave_inclusive_sum(loc);
       uint32_t before = incl - loc;
       if (before < rem && rem <= incl) {
 #pragma unroll
@@ -305,6 +295,13 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
   const int nc = a.n_chunks;
   const uint32_t* c_in = a.chunk_in + (int64_t)head * nc;
   const uint32_t* c_above = a.chunk_above + (int64_t)head * nc;
+  // this thread's four values, needed last, are loaded first
+  uint32_t vbits[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t j = j0 + e;
+    vbits[e] = (h.k_sel > 0 && j < h.s && j >= h.sink_end && j < h.rec_begin) ? __float_as_uint(vals[j]) : 0u;
+  }
 
   uint32_t thr = 0xFFFFFFFFu, need_eq = 0u;  // k_sel == 0: no candidate is chosen
   // counts of the chunks before this one: kept = mandatory + above + taken equals
@@ -315,6 +312,8 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
     if (threadIdx.x == 0) s_flag = 0u;
     __syncthreads();
     uint32_t n_total = 0;
+    uint32_t above_local = 0;
+    for (int c = threadIdx.x; c < nc; c += kThreads) above_local += c_above[c];
     for (int base = 0; base < nc; base += kThreads) {
       const int c = base + threadIdx.x;
       const uint32_t n = c < nc ? c_in[c] : 0u;
@@ -330,8 +329,6 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
     const bool overflow = s_flag != 0u;
 
     if (!overflow) {
-      uint32_t above_local = 0;
-      for (int c = threadIdx.x; c < nc; c += kThreads) above_local += c_above[c];
       const uint32_t above_all = block_sum(above_local, scratch);
       uint32_t rem = h.k_sel - above_all;  // rank of the threshold inside the list
       // gather the listed patterns of all chunks, chunk by chunk
@@ -415,7 +412,7 @@ __global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
     if (j >= h.s) continue;
     if (j < h.sink_end || j >= h.rec_begin) { flags[e] = 1u; continue; }
     if (h.k_sel == 0) continue;
-    const uint32_t u = __float_as_uint(vals[j]);
+    const uint32_t u = vbits[e];
     if (u > thr) flags[e] = 1u;
     else if (u == thr) { flags[e] = 2u; ++neq; }
   }
