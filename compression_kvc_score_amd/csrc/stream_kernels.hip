@@ -300,14 +300,20 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
 
 struct Range {
   int t0, nst;  // first token, slots
+  int toks;     // tokens per slot
+  bool rev;     // slots visited from the last one down
+  // first token of the n-th slot visited
+  __device__ __forceinline__ int tok(int n) const { return t0 + (rev ? nst - 1 - n : n) * toks; }
 };
 
-__device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int toks) {
+__device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int toks, bool rev) {
   Range r;
   r.t0 = split * a.blocks_per_wg * toks;
   int t1 = r.t0 + a.blocks_per_wg * toks;
   t1 = t1 < a.s ? t1 : a.s;
   r.nst = (t1 - r.t0 + toks - 1) / toks;
+  r.toks = toks;
+  r.rev = rev;
   return r;
 }
 
@@ -318,7 +324,7 @@ __device__ __forceinline__ void ring_fill(const ScoreArgs& a, int h0, const Rang
   using R = Ring<D, HG>;
 #pragma unroll
   for (int n = 0; n < kRingSlots - 1; ++n)
-    if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.t0 + n * R::TOKS, wave, lane, off, smem + n * kSlotBytes);
+    if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
 }
 
 // Top of ring iteration n: slot n has landed for the whole workgroup, and
@@ -334,7 +340,7 @@ __device__ __forceinline__ void ring_advance(const ScoreArgs& a, int h0, const R
   lds_barrier();
   const int nn = n + kRingSlots - 1;
   if (nn < rg.nst)
-    slot_issue<D, HG>(a, h0, rg.t0 + nn * R::TOKS, wave, lane, off, smem + (nn % kRingSlots) * kSlotBytes);
+    slot_issue<D, HG>(a, h0, rg.tok(nn), wave, lane, off, smem + (nn % kRingSlots) * kSlotBytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -445,7 +451,7 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
   const int head = h0 + ro.hl;
   const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;  // the last row groups may own one fewer
   const int first_hidden = a.s - a.w + 1;
-  const Range rg = wg_range(a, split, R::TOKS);
+  const Range rg = wg_range(a, split, R::TOKS, false);
 
   if (a.hist != nullptr && split == 0)
     for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x) a.hist[(int64_t)h0 * kHistBins + i] = 0u;
@@ -482,7 +488,7 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
       A = contract<D, NRTW, true>(qr, kf, 0);
     }
     for (int n = 0; n < rg.nst; ++n) {
-      const int kbase = rg.t0 + n * R::TOKS + kt_off;
+      const int kbase = rg.tok(n) + kt_off;
       const bool edge = kbase + kKeyTile > first_hidden;
       const bool more = n + 1 < rg.nst;
       // the next slot's key reads overlap this slot's remaining jobs
@@ -508,7 +514,7 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
     for (int n = 0; n < rg.nst; ++n) {
       ring_advance<D, HG>(a, h0, rg, n, wave, lane, off, smem);
       const unsigned char* slot = smem + (n % kRingSlots) * kSlotBytes;
-      const int kbase = rg.t0 + n * R::TOKS + ro.kt * kKeyTile;
+      const int kbase = rg.tok(n) + ro.kt * kKeyTile;
       if (kbase < a.s) {
         uint4 kf[D / 16];
         load_key_regs<D, HG>(slot, ro.hl, ro.kt, half, l32, kf);
@@ -640,7 +646,8 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
   const int head = h0 + ro.hl;
   const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;
   const int first_hidden = a.s - a.w + 1;
-  const Range rg = wg_range(a, split, R::TOKS);
+  // the K that pass 1 read last (still in the memory-side cache) goes first
+  const Range rg = wg_range(a, split, R::TOKS, true);
 
   uint32_t off[R::NI];
   copy_offsets<D, HG>(a, wave, lane, off);
@@ -684,7 +691,7 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
   };
   // the first row group adds the partials of slot n in a fixed order
   auto finish = [&](int n) {
-    const int key = rg.t0 + n * R::TOKS + ro.kt * kKeyTile + l32;
+    const int key = rg.tok(n) + ro.kt * kKeyTile + l32;
     if (ro.rg == 0 && half == 0 && key < a.s) {
       float v[R::RS];
 #pragma unroll
@@ -703,7 +710,7 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
       if (n > 0) finish(n - 1);
     }
     const unsigned char* slot = smem + (n % kRingSlots) * kSlotBytes;
-    const int kbase = rg.t0 + n * R::TOKS + ro.kt * kKeyTile;
+    const int kbase = rg.tok(n) + ro.kt * kKeyTile;
     if (kbase < a.s) {
       uint4 kf[D / 16];
       load_key_regs<D, HG>(slot, ro.hl, ro.kt, half, l32, kf);
