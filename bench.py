@@ -261,7 +261,8 @@ def main(argv=None):
         traffic = None
     roofline = {
         "bound": "hbm",
-        "kernel": dominant,
+        "kernel": {"pass1": "pass 1 scan + split combine (one kvc_score_pass1 call)",
+                   "pass2": "pass 2 scan (one kvc_score_pass2 call)"}[dominant],
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
