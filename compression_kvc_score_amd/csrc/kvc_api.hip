@@ -37,7 +37,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kInt32Max = 2147483647LL;
-constexpr int64_t kMaxPrompt = 1LL << 23;  // bounds the selection's per-chunk tables in LDS
+constexpr int64_t kMaxPrompt = (int64_t)kMaxSubs * kSub;  // 2^23: sub-chunk tags fit in 13 bits
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -170,10 +170,11 @@ int head_table(const Layer& L, const int32_t* budgets, HeadTable& t) {
 }
 
 int n_chunks(const Layer& L) { return (int)((L.s + kSelectChunk - 1) / kSelectChunk); }
+int n_subs(const Layer& L) { return (int)((L.s + kSub - 1) / kSub); }
 
 struct WsLayout {
   size_t part, m, z, scores, pooled;
-  size_t hist, slots, chunk_in, chunk_above;
+  size_t hist, slots;
   size_t total;
 };
 
@@ -184,11 +185,7 @@ WsLayout ws_layout(const Layer& L) {
   w.hist = off;
   off += align_up((size_t)L.hkv * kHistBins * 4, 256);
   w.slots = off;
-  off += align_up((size_t)L.hkv * nc * kSlotCap * 4, 256);
-  w.chunk_in = off;
-  off += align_up((size_t)L.hkv * nc * 4, 256);
-  w.chunk_above = off;
-  off += align_up((size_t)L.hkv * nc * 4, 256);
+  off += align_up((size_t)L.hkv * nc * kSlotStride * 4, 256);
   w.part = off;
   off += align_up((size_t)L.hkv * kMaxSplit * L.row_tiles * kRowTile * sizeof(float2), 256);
   w.m = off;
@@ -237,7 +234,7 @@ int check_lds(const Layer& L) {
   }
   const size_t scan = L.stream_hg ? std::max(pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L))
                                   : std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
-  const size_t need = std::max(scan, select_lds_bytes(n_chunks(L)) + 8192);
+  const size_t need = std::max(scan, select_lds_bytes(n_chunks(L), n_subs(L)) + 16384);
   if (need > (size_t)lim)
     return fail(KVC_ERR_UNSUPPORTED, "kernels need %zu bytes of LDS, device allows %d", need, lim);
   return KVC_OK;
@@ -298,9 +295,12 @@ int run_pass2(const Layer& L, const void* q, const void* k, const float* m, cons
 }
 
 // need_hist: the selection clears and builds its own histogram (and pooled
-// values); otherwise pass 2 of the same call has built it.
+// values); otherwise pass 1 cleared it and pass 2 built it. k != nullptr: the
+// compaction also copies the retained K/V rows and writes their positions.
 int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
-               void* ws, bool need_hist, hipStream_t st) {
+               void* ws, bool need_hist, hipStream_t st, const void* k = nullptr,
+               const void* v = nullptr, void* k_out = nullptr, void* v_out = nullptr,
+               int32_t* pos_out = nullptr) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   SelectArgs a{};
@@ -313,11 +313,23 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
   a.n_sink = L.n_sink;
   a.n_recent = L.n_recent;
   a.n_chunks = n_chunks(L);
+  a.n_subs = n_subs(L);
   a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
   a.slots = reinterpret_cast<uint32_t*>(wsb + lay.slots);
-  a.chunk_in = reinterpret_cast<uint32_t*>(wsb + lay.chunk_in);
-  a.chunk_above = reinterpret_cast<uint32_t*>(wsb + lay.chunk_above);
   a.heads = ht;
+  if (k != nullptr) {
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.k_tok = L.k_tok;
+    a.k_head = L.k_head;
+    a.v_tok = L.v_tok;
+    a.v_head = L.v_head;
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.v_out = static_cast<uint16_t*>(v_out);
+    a.pos_out = pos_out;
+    a.pos_offset = L.pos_offset;
+    a.d = L.d;
+  }
   const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return KVC_OK;
@@ -515,8 +527,8 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
   const bool hist_in_pass2 = L.pool == 1;
   KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
   KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
-  KVC_TRY(run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st));
-  KVC_TRY(run_gather(L, k, v, idx_out, ht, k_out, v_out, pos_out, st));
+  // the compaction of the selection copies the retained rows as it goes
+  KVC_TRY(run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out));
   return KVC_OK;
 }
 

@@ -14,10 +14,16 @@ constexpr int kRowTile = 32;     // query rows per MFMA tile
 constexpr int kMaxSplit = 128;   // max workgroups per KV head in the scans
 constexpr int kMaxRowTiles = KVC_MAX_ROWS / kRowTile;
 constexpr int kSelectThreads = 1024;
-constexpr int kSelectChunk = 4 * kSelectThreads;  // keys per selection workgroup
+constexpr int kSelectChunk = 4 * kSelectThreads;  // keys per filter workgroup
+constexpr int kCompactThreads = 256;
+constexpr int kSub = 4 * kCompactThreads;         // keys per compaction workgroup (a sub-chunk)
+constexpr int kSubsPerChunk = kSelectChunk / kSub;
 constexpr int kHistBins = 4096;   // top-bits histogram of candidate scores (bits 30..19)
 constexpr int kCandCap = 16384;   // listed candidates per head inside the threshold bin
 constexpr int kSlotCap = 1024;    // listed candidates per 4096-key chunk
+constexpr int kSlotHdr = 16;      // header words of a chunk's slot (counts, b*)
+constexpr int kSlotStride = kSlotHdr + kSlotCap;
+constexpr int kMaxSubs = 8192;    // sub-chunk tags of listed candidates take 13 bits
 
 // Descriptor after validation, with defaults resolved.
 struct Layer {
@@ -69,11 +75,21 @@ struct SelectArgs {
   int64_t s;
   int n_sink, n_recent;
   int n_chunks;          // ceil(s / kSelectChunk)
+  int n_subs;            // ceil(s / kSub)
   uint32_t* hist;        // [hkv][kHistBins]
-  uint32_t* slots;       // [hkv][n_chunks][kSlotCap] listed patterns inside the threshold bin
-  uint32_t* chunk_in;    // [hkv][n_chunks] candidates inside the threshold bin
-  uint32_t* chunk_above; // [hkv][n_chunks] candidates above it
+  uint32_t* slots;       // [hkv][n_chunks][kSlotStride]: per chunk, the candidates inside and
+                         // above the threshold bin b* of each sub-chunk, b*, and the list of
+                         // those inside b* (sub-chunk << 19 | low 19 pattern bits, key order)
   HeadTable heads;
+  // retained rows copied by the compaction (k == nullptr: indices only)
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_tok, k_head, v_tok, v_head;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int32_t* pos_out;
+  int64_t pos_offset;
+  int d;
 };
 
 struct GatherArgs {
@@ -99,9 +115,10 @@ hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_combine(const Layer& L, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
 // need_hist: clear and build the histogram (and pooled values) first;
-// otherwise pass 2 has built it.
+// otherwise pass 2 has built it. a.k != nullptr: the compaction also copies
+// the retained K/V rows and positions.
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st);
-size_t select_lds_bytes(int n_chunks);
+size_t select_lds_bytes(int n_chunks, int n_subs);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 
 // Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;

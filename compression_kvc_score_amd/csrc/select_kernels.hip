@@ -1,6 +1,7 @@
 // Selection of the retained keys (TideKV, Fig. 3 caption): per KV head, the
 // mandatory sink and recent keys plus the top K_h - |mandatory| other keys by
-// (score descending, index ascending), written in ascending key order.
+// (score descending, index ascending), written in ascending key order; with
+// the gather (TideKV, Fig. 2 caption) the same pass copies their K and V rows.
 //
 // Scores are finite and >= +0, so their IEEE-754 bit patterns read as uint32
 // order the same way as the values. The selection spreads over every CU:
@@ -12,17 +13,18 @@
 //           same histogram while it writes the scores; with a max-pool this
 //           kernel also writes the pooled values.)
 //  filter   every chunk workgroup finds, from its head's histogram, the bin b*
-//           holding the k-th best candidate, counts its candidates above b*,
-//           and lists the patterns of its candidates inside b* in its own
-//           slot (no atomics).
-//  select   every chunk workgroup reads its head's short lists (a few
-//           thousand patterns), radix-selects in LDS the exact pattern T of
-//           the k-th best candidate and how many candidates equal to T are
-//           taken (the lowest indices: ties go to the lower index), derives
-//           its output offset from the counts of the chunks before it, and
-//           writes its kept indices in ascending order. If a slot or the
-//           lists overflow (heavily tied scores), it selects by a radix over
-//           the head's whole score row instead -- same result, slower.
+//           holding the k-th best candidate, counts per 1024-key sub-chunk its
+//           candidates above b* and inside b*, and lists the patterns of those
+//           inside b* in its own slot (no atomics).
+//  compact  a small workgroup per sub-chunk reads its head's short lists (a
+//           few thousand patterns, from L2), radix-selects in LDS the exact
+//           pattern T of the k-th best candidate and how many candidates equal
+//           to T are taken (the lowest indices: ties go to the lower index),
+//           derives its first output row from the counts of the keys before
+//           it, writes its kept indices (and positions) in ascending order and
+//           copies the kept keys' K and V rows. If a slot or the lists
+//           overflow (heavily tied scores), it selects by a radix over the
+//           head's whole score row instead -- same result, slower.
 //
 // All counts are integers, so the output does not depend on the order in
 // which workgroups run.
@@ -33,14 +35,20 @@
 namespace kvc {
 namespace {
 
-constexpr int kThreads = kSelectThreads;  // 1024
-constexpr int kWaves = kThreads / kWave;  // 16
-constexpr int kChunk = kSelectChunk;      // 4096 keys per chunk, 4 per thread
+constexpr int kThreads = kSelectThreads;          // 1024 per filter workgroup
+constexpr int kWaves = kThreads / kWave;          // 16
+constexpr int kChunk = kSelectChunk;              // 4096 keys per filter workgroup, 4 per thread
+constexpr int kWavesPerSub = kWaves / kSubsPerChunk;
+constexpr int kCWaves = kCompactThreads / kWave;  // 4 per compaction workgroup
+constexpr int kCopyUnroll = 8;                    // rows in flight per thread in the row copy
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t bin_of(uint32_t bits) { return (bits >> 19) & (kHistBins - 1); }
 
-// Exclusive prefix sum over the workgroup of one value per thread; also
-// returns the total. Uses `scratch` (kWaves + 1 entries) in LDS.
+// Exclusive prefix sum over a workgroup of NW wavefronts, one value per
+// thread; also returns the total. Uses `scratch` (NW entries) in LDS.
+template <int NW>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_inclusive_sum(v);
@@ -48,7 +56,7 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t t = scratch[w];
     before += w < wave ? t : 0u;
     all += t;
@@ -56,6 +64,27 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t
   total = all;
   __syncthreads();
   return before + incl - v;
+}
+
+// Sums over a workgroup of NW wavefronts of two values per thread (every
+// thread gets both). Uses `scratch` (2 * NW entries) in LDS.
+template <int NW>
+__device__ void block_sum2(uint32_t& x, uint32_t& y, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ix = wave_inclusive_sum(x), iy = wave_inclusive_sum(y);
+  if (lane == 63) {
+    scratch[wave] = ix;
+    scratch[NW + wave] = iy;
+  }
+  __syncthreads();
+  x = 0u;
+  y = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    x += scratch[w];
+    y += scratch[NW + w];
+  }
+  __syncthreads();
 }
 
 struct HeadGeom {
@@ -78,6 +107,20 @@ __device__ __forceinline__ HeadGeom head_geom(const SelectArgs& a, int head) {
   return h;
 }
 
+__device__ __forceinline__ bool is_candidate(const HeadGeom& h, int64_t j) {
+  return j >= h.sink_end && j < h.rec_begin;
+}
+
+// Mandatory keys in [lo, hi).
+__device__ __forceinline__ uint32_t mandatory_in(const HeadGeom& h, int64_t lo, int64_t hi) {
+  if (hi > h.s) hi = h.s;
+  if (lo >= hi) return 0u;
+  const int64_t sink = h.sink_end > lo ? (h.sink_end < hi ? h.sink_end : hi) - lo : 0;
+  const int64_t rb = h.rec_begin > lo ? h.rec_begin : lo;
+  const int64_t rec = hi > rb ? hi - rb : 0;
+  return (uint32_t)(sink + rec);
+}
+
 // Ranking value of key j: the score, or its centred max over [j - r, j + r].
 __device__ __forceinline__ float rank_value(const float* row, int64_t s, int64_t j, int r) {
   float m = row[j];
@@ -88,38 +131,35 @@ __device__ __forceinline__ float rank_value(const float* row, int64_t s, int64_t
   return m;
 }
 
-// Find the bin holding the k-th largest candidate from the head's histogram.
-// Returns b* and the number of candidates in higher bins. Uses `scratch`.
-__device__ void find_bin(const uint32_t* hist, uint32_t k, uint32_t* scratch, uint32_t& bstar,
-                         uint32_t& above) {
-  __shared__ uint32_t s_b, s_above;
-  // thread t owns bins 4095-4t .. 4092-4t (descending)
-  uint32_t c[4], loc = 0;
+// Run by one wavefront: among the NB bins of `hist` (counts), walked from the
+// highest bin down, find the bin d holding the rem-th element and the rank of
+// that element inside d; lane 0 of the bin's owner writes (d, rank) to out.
+template <int NB>
+__device__ void pick_digit_wave(const uint32_t* hist, uint32_t rem, uint32_t* out) {
+  constexpr int BPL = NB / kWave;  // bins per lane, consecutive and descending
+  const int lane = threadIdx.x & 63;
+  uint32_t c[BPL], loc = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c[q] = hist[kHistBins - 1 - 4 * threadIdx.x - q];
+  for (int q = 0; q < BPL; ++q) {
+    c[q] = hist[NB - 1 - BPL * lane - q];
     loc += c[q];
   }
-  uint32_t total;
-  uint32_t before = block_exclusive_scan(loc, scratch, total);
-  if (before < k && k <= before + loc) {
+  const uint32_t incl = wave_inclusive_sum(loc);
+  uint32_t before = incl - loc;
+  if (before < rem && rem <= incl) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (before < k && k <= before + c[q]) {
-        s_b = kHistBins - 1 - 4 * threadIdx.x - q;
-        s_above = before;
+    for (int q = 0; q < BPL; ++q) {
+      if (before < rem && rem <= before + c[q]) {
+        out[0] = (uint32_t)(NB - 1 - BPL * lane - q);
+        out[1] = rem - before;
       }
       before += c[q];
     }
   }
-  __syncthreads();
-  bstar = s_b;
-  above = s_above;
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// init: clear the per-head histograms and candidate counters.
+// init: clear the per-head histograms.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) init_kernel(SelectArgs a, int hkv) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -146,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
     if (j >= h.s) break;
     const float v = a.pool_radius > 0 ? rank_value(row, h.s, j, a.pool_radius) : row[j];
     if (prow) prow[j] = v;
-    if (j >= h.sink_end && j < h.rec_begin) atomicAdd(&lh[bin_of(__float_as_uint(v))], 1u);
+    if (is_candidate(h, j)) atomicAdd(&lh[bin_of(__float_as_uint(v))], 1u);
   }
   __syncthreads();
   uint32_t* gh = a.hist + (int64_t)head * kHistBins;
@@ -155,14 +195,18 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// filter: per chunk, count the candidates above b* and list, in key order,
-// the patterns of those inside b* (in the chunk's own slot: no atomics).
+// filter: per chunk, count per sub-chunk the candidates above b* and inside
+// it, and list, in key order, the patterns of those inside b* (in the chunk's
+// own slot: no atomics).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
-  __shared__ uint32_t scratch[kWaves + 1];
+  __shared__ uint32_t scratch[kWaves];
+  __shared__ uint32_t w_in[kWaves], w_above[kWaves];
+  __shared__ uint32_t s_b, s_hit;
   const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
   const HeadGeom h = head_geom(a, head);
   if (h.keep_all || h.k_sel == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // this thread's four values, loaded before the histogram scan so that the
   // two memory round trips overlap
   const float* vals = a.vals + (int64_t)head * h.s;
@@ -171,10 +215,28 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t j = j0 + e;
-    bits[e] = (j < h.s && j >= h.sink_end && j < h.rec_begin) ? __float_as_uint(vals[j]) : 0u;
+    bits[e] = (j < h.s && is_candidate(h, j)) ? __float_as_uint(vals[j]) : 0u;
   }
-  uint32_t bstar, above_all;
-  find_bin(a.hist + (int64_t)head * kHistBins, h.k_sel, scratch, bstar, above_all);
+  // b*: the bin holding the k-th best candidate (thread t owns bins
+  // 4095-4t .. 4092-4t, descending)
+  const uint32_t* hist = a.hist + (int64_t)head * kHistBins;
+  uint32_t c[4], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = hist[kHistBins - 1 - 4 * threadIdx.x - q];
+    loc += c[q];
+  }
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<kWaves>(loc, scratch, total);
+  if (before < h.k_sel && h.k_sel <= before + loc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (before < h.k_sel && h.k_sel <= before + c[q]) s_b = kHistBins - 1 - 4 * threadIdx.x - q;
+      before += c[q];
+    }
+  }
+  __syncthreads();
+  const uint32_t bstar = s_b;
 
   uint32_t above = 0, nin = 0;
   bool in[4];
@@ -182,267 +244,336 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   for (int e = 0; e < 4; ++e) {
     const int64_t j = j0 + e;
     in[e] = false;
-    if (j < h.s && j >= h.sink_end && j < h.rec_begin) {
+    if (j < h.s && is_candidate(h, j)) {
       const uint32_t b = bin_of(bits[e]);
       above += b > bstar;
       in[e] = b == bstar;
       nin += in[e];
     }
   }
-  uint32_t n_in;
-  uint32_t pos = block_exclusive_scan(nin, scratch, n_in);
-  uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotCap;
+  const uint32_t inc_in = wave_inclusive_sum(nin), inc_ab = wave_inclusive_sum(above);
+  if (lane == 63) {
+    w_in[wave] = inc_in;
+    w_above[wave] = inc_ab;
+  }
+  __syncthreads();
+  uint32_t pos = inc_in - nin;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) pos += w < wave ? w_in[w] : 0u;
+  // listed entries carry their sub-chunk: the patterns inside b* share bits
+  // 31..19, so the low 19 bits identify them
+  uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotStride;
+  const uint32_t tag = (uint32_t)(chunk * kSubsPerChunk + (int)threadIdx.x / (kSub / 4)) << 19;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (in[e]) {
-      if (pos < (uint32_t)kSlotCap) slot[pos] = bits[e];
+      if (pos < (uint32_t)kSlotCap) slot[kSlotHdr + pos] = tag | (bits[e] & 0x7FFFFu);
       ++pos;
     }
   }
-  uint32_t n_above;
-  block_exclusive_scan(above, scratch, n_above);
-  if (threadIdx.x == 0) {
-    a.chunk_above[(int64_t)head * a.n_chunks + chunk] = n_above;
-    a.chunk_in[(int64_t)head * a.n_chunks + chunk] = n_in;
-  }
-}
-
-// Mandatory keys inside chunk c.
-__device__ __forceinline__ uint32_t chunk_mandatory(const HeadGeom& h, int64_t c) {
-  const int64_t lo = c * kChunk;
-  int64_t hi = lo + kChunk;
-  if (hi > h.s) hi = h.s;
-  const int64_t sink = (h.sink_end > lo ? (h.sink_end < hi ? h.sink_end : hi) - lo : 0);
-  const int64_t rec = (hi > h.rec_begin ? hi - (h.rec_begin > lo ? h.rec_begin : lo) : 0);
-  return (uint32_t)(sink + rec);
-}
-
-// Slow path: k-th largest candidate pattern by a radix over the whole score
-// row of the head (8 bits per round from the top).
-__device__ uint32_t radix_over_row(const HeadGeom& h, const uint32_t* bits, uint32_t k,
-                                   uint32_t* hist256, uint32_t& above) {
-  __shared__ uint32_t s_digit, s_rem;
-  uint32_t prefix = 0u, mask = 0u, rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kThreads) hist256[i] = 0u;
-    __syncthreads();
-    for (int64_t j = h.sink_end + threadIdx.x; j < h.rec_begin; j += kThreads) {
-      const uint32_t u = bits[j];
-      if ((u & mask) == prefix) atomicAdd(&hist256[(u >> shift) & 255u], 1u);
+  // header: candidates inside b* and above it per sub-chunk, then b*
+  if (threadIdx.x < kSubsPerChunk) {
+    uint32_t ni = 0, na = 0;
+#pragma unroll
+    for (int q = 0; q < kWavesPerSub; ++q) {
+      ni += w_in[kWavesPerSub * threadIdx.x + q];
+      na += w_above[kWavesPerSub * threadIdx.x + q];
     }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int l = threadIdx.x;
-      uint32_t c[4], loc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { c[q] = hist256[255 - 4 * l - q]; loc += c[q]; }
-      const uint32_t incl = wave_inclusive_sum(loc);
-      uint32_t before = incl - loc;
-      if (before < rem && rem <= incl) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (before < rem && rem <= before + c[q]) {
-            s_digit = 255u - 4u * l - q;
-            s_rem = rem - before;
-          }
-          before += c[q];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    rem = s_rem;
-    __syncthreads();
+    slot[threadIdx.x] = ni;
+    slot[kSubsPerChunk + threadIdx.x] = na;
   }
-  above = k - rem;  // candidates strictly above the threshold pattern
-  return prefix;
+  if (threadIdx.x == 0) slot[2 * kSubsPerChunk] = bstar;
 }
 
-// Sum over the workgroup of one value per thread (all threads get it).
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
-  uint32_t tot;
-  block_exclusive_scan(v, scratch, tot);
-  return tot;
-}
+// Shared memory of a compaction workgroup while it resolves its head.
+struct ResolveLds {
+  uint32_t* cbits;    // kCandCap listed entries (any order)
+  uint32_t* hist1;    // 1024 radix bins (pattern bits 18..9)
+  uint32_t* hist2;    // 512 radix bins (pattern bits 8..0)
+  uint32_t* scratch;  // 2 * kCWaves
+  uint32_t* pick;     // 2: digit and rank from pick_digit_wave
+};
 
-// ---------------------------------------------------------------------------
-// select: each chunk workgroup resolves its head's exact threshold from the
-// listed candidates (the same computation in every workgroup of the head),
-// derives its output offset from the counts of the chunks before it, and
-// writes its kept indices in ascending order.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) select_kernel(SelectArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* cbits = reinterpret_cast<uint32_t*>(smem);  // kCandCap listed patterns
-  uint32_t* coff = cbits + kCandCap;                    // n_chunks + 1 list offsets
-  __shared__ uint32_t hist[1024];
-  __shared__ uint32_t scratch[kWaves + 1];
-  __shared__ uint32_t s_digit, s_rem, s_flag;
+constexpr int kGroupChunks = 4;             // chunk slots a wavefront reads per round trip
+constexpr int kSpecRounds = 4;              // 64-word reads per slot: header + 240 entries
+constexpr int kSpecEntries = kSpecRounds * kWave - kSlotHdr;
 
-  const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
-  const HeadGeom h = head_geom(a, head);
-  int32_t* out = a.idx_out + a.heads.offset[head];
-  const int64_t j0 = (int64_t)chunk * kChunk + 4 * threadIdx.x;
-  if (h.keep_all) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (j0 + e < h.s) out[j0 + e] = (int32_t)(j0 + e);
-    return;
-  }
-  const float* vals = a.vals + (int64_t)head * h.s;
-  const uint32_t* rowbits = reinterpret_cast<const uint32_t*>(vals);
+// Threshold of one head, resolved from the chunk lists: the pattern T of the
+// k-th best candidate, the number need_eq of candidates equal to T that are
+// kept, and, for the keys before sub-chunk `sub`, the candidates above T and
+// equal to T. One speculative read per slot brings its header and most of its
+// list. Returns false (nothing resolved) if a chunk's slot or the gathered
+// list overflowed.
+__device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int head, int sub,
+                                   const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
+                                   uint32_t& gt_before, uint32_t& eq_before) {
+  constexpr int NW = kCWaves;
+  __shared__ uint32_t s_count, s_flag, s_bstar;
   const int nc = a.n_chunks;
-  const uint32_t* c_in = a.chunk_in + (int64_t)head * nc;
-  const uint32_t* c_above = a.chunk_above + (int64_t)head * nc;
-  // this thread's four values, needed last, are loaded first
-  uint32_t vbits[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t* slots = a.slots + (int64_t)head * nc * kSlotStride;
+  if (threadIdx.x == 0) {
+    s_count = 0u;
+    s_flag = 0u;
+  }
+  uint32_t ab_all = 0, ab_before = 0;  // wavefront-uniform partial sums
+  for (int c0 = 0; c0 < nc; c0 += NW * kGroupChunks) {
+    // this wavefront's chunks of the group: c0 + wave * kGroupChunks + i
+    uint32_t v[kGroupChunks][kSpecRounds];
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = c0 + wave * kGroupChunks + i;
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r)
+        v[i][r] = c < nc ? slots[(int64_t)c * kSlotStride + r * kWave + lane] : 0u;
+    }
+    if (c0 == 0) __syncthreads();  // s_count and the radix bins are cleared
+    uint32_t n[kGroupChunks], tot = 0;
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      n[i] = 0u;
+#pragma unroll
+      for (int q = 0; q < kSubsPerChunk; ++q) {
+        const int c = c0 + wave * kGroupChunks + i;
+        n[i] += (uint32_t)__builtin_amdgcn_readlane((int)v[i][0], q);
+        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)v[i][0], kSubsPerChunk + q);
+        ab_all += ab;
+        ab_before += c * kSubsPerChunk + q < sub ? ab : 0u;
+      }
+      tot += n[i];
+    }
+    if (c0 == 0 && wave == 0 && lane == 2 * kSubsPerChunk) s_bstar = v[0][0];
+    // space in the LDS list for this wavefront's chunks
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&s_count, tot);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = c0 + wave * kGroupChunks + i;
+      if (n[i] > (uint32_t)kSlotCap || base + n[i] > (uint32_t)kCandCap) {
+        if (lane == 0) s_flag = 1u;
+      } else {
+#pragma unroll
+        for (int r = 0; r < kSpecRounds; ++r) {
+          const int e = r * kWave + lane - kSlotHdr;  // entry index of this word
+          if (e >= 0 && (uint32_t)e < n[i]) m.cbits[base + e] = v[i][r];
+        }
+        // rest of a long list
+        for (uint32_t e = kSpecEntries + lane; e < n[i]; e += kWave)
+          m.cbits[base + e] = slots[(int64_t)c * kSlotStride + kSlotHdr + e];
+      }
+      base += n[i];
+    }
+  }
+  if (lane != 0) {  // wavefront-uniform: count once per wavefront
+    ab_all = 0u;
+    ab_before = 0u;
+  }
+  block_sum2<NW>(ab_all, ab_before, m.scratch);
+  if (s_flag != 0u) return false;
+
+  // radix over pattern bits 18..9, then 8..0 (the listed patterns share the rest)
+  const uint32_t n_total = s_count;
+  uint32_t rem = h.k_sel - ab_all;  // rank of the threshold inside the list
+  for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads)
+    atomicAdd(&m.hist1[(m.cbits[i] >> 9) & 1023u], 1u);
+  __syncthreads();
+  if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
+  __syncthreads();
+  const uint32_t d1 = m.pick[0];
+  rem = m.pick[1];
+  for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads) {
+    const uint32_t e = m.cbits[i];
+    if (((e >> 9) & 1023u) == d1) atomicAdd(&m.hist2[e & 511u], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) pick_digit_wave<512>(m.hist2, rem, m.pick);
+  __syncthreads();
+  const uint32_t low = (d1 << 9) | m.pick[0];
+  need_eq = m.pick[1];
+  thr = (s_bstar << 19) | low;
+  // listed candidates of the sub-chunks before this one
+  uint32_t g = 0, q = 0;
+  for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads) {
+    const uint32_t e = m.cbits[i];
+    if ((int)(e >> 19) < sub) {
+      g += (e & 0x7FFFFu) > low;
+      q += (e & 0x7FFFFu) == low;
+    }
+  }
+  block_sum2<NW>(g, q, m.scratch);
+  gt_before = ab_before + g;
+  eq_before = q;
+  return true;
+}
+
+// Slow path: the same quantities by radix passes over the head's whole
+// score row (8 bits per round from the top).
+__device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int head, int sub,
+                                 const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
+                                 uint32_t& gt_before, uint32_t& eq_before) {
+  constexpr int NT = kCompactThreads, NW = kCWaves;
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(a.vals + (int64_t)head * h.s);
+  uint32_t prefix = 0u, mask = 0u, rem = h.k_sel;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += NT) m.hist1[i] = 0u;
+    __syncthreads();
+    for (int64_t j = h.sink_end + threadIdx.x; j < h.rec_begin; j += NT) {
+      const uint32_t u = bits[j];
+      if ((u & mask) == prefix) atomicAdd(&m.hist1[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) pick_digit_wave<256>(m.hist1, rem, m.pick);
+    __syncthreads();
+    prefix |= m.pick[0] << shift;
+    rem = m.pick[1];
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  thr = prefix;
+  need_eq = rem;
+  const int64_t s0 = (int64_t)sub * kSub;
+  const int64_t lim = s0 < h.rec_begin ? s0 : h.rec_begin;
+  uint32_t g = 0, q = 0;
+  for (int64_t j = h.sink_end + threadIdx.x; j < lim; j += NT) {
+    const uint32_t u = bits[j];
+    g += u > thr;
+    q += u == thr;
+  }
+  block_sum2<NW>(g, q, m.scratch);
+  gt_before = g;
+  eq_before = q;
+}
+
+// ---------------------------------------------------------------------------
+// compact: per sub-chunk, resolve the head's threshold, then write the kept
+// indices (and positions) in ascending order from the sub-chunk's first
+// output row; with GATHER also copy their K and V rows.
+// ---------------------------------------------------------------------------
+template <bool GATHER>
+__global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ uint32_t hist1[1024], hist2[512];
+  __shared__ uint32_t scratch[2 * kCWaves], pick[2];
+  __shared__ int32_t kept_keys[GATHER ? kSub : 1];
+  const int head = blockIdx.x / a.n_subs, sub = blockIdx.x % a.n_subs;
+  const HeadGeom h = head_geom(a, head);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t s0 = (int64_t)sub * kSub;
+  const int64_t j0 = s0 + 4 * threadIdx.x;
+  const bool ranked = !h.keep_all && h.k_sel > 0;
+  uint32_t vb[4] = {0u, 0u, 0u, 0u};
+  uint32_t thr = 0xFFFFFFFFu, quota = 0u, first;
+  if (ranked) {
+    const float* vals = a.vals + (int64_t)head * h.s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t j = j0 + e;
+      if (j < h.s && is_candidate(h, j)) vb[e] = __float_as_uint(vals[j]);
+    }
+    for (int i = threadIdx.x; i < 1024; i += kCompactThreads) hist1[i] = 0u;
+    for (int i = threadIdx.x; i < 512; i += kCompactThreads) hist2[i] = 0u;
+    ResolveLds m;
+    m.cbits = reinterpret_cast<uint32_t*>(smem);
+    m.hist1 = hist1;
+    m.hist2 = hist2;
+    m.scratch = scratch;
+    m.pick = pick;
+    uint32_t need_eq, gt_before, eq_before;
+    if (!resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before))
+      resolve_from_row(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
+    quota = need_eq > eq_before ? need_eq - eq_before : 0u;  // equal candidates this sub-chunk may take
+    first = mandatory_in(h, 0, s0) + gt_before + (need_eq < eq_before ? need_eq : eq_before);
+  } else {
+    first = h.keep_all ? (uint32_t)s0 : mandatory_in(h, 0, s0);
+  }
+  // 1: kept; 2: equal to T (taken in key order while the quota lasts)
+  uint32_t flag[4], n_kept = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t j = j0 + e;
-    vbits[e] = (h.k_sel > 0 && j < h.s && j >= h.sink_end && j < h.rec_begin) ? __float_as_uint(vals[j]) : 0u;
-  }
-
-  uint32_t thr = 0xFFFFFFFFu, need_eq = 0u;  // k_sel == 0: no candidate is chosen
-  // counts of the chunks before this one: kept = mandatory + above + taken equals
-  uint32_t prev_gt = 0, prev_eq = 0;
-  uint32_t eq_before = 0;  // equal candidates in chunks before this one
-  if (h.k_sel > 0) {
-    // list offsets; overflow if a chunk's slot or the whole list is too small
-    if (threadIdx.x == 0) s_flag = 0u;
-    __syncthreads();
-    uint32_t n_total = 0;
-    uint32_t above_local = 0;
-    for (int c = threadIdx.x; c < nc; c += kThreads) above_local += c_above[c];
-    for (int base = 0; base < nc; base += kThreads) {
-      const int c = base + threadIdx.x;
-      const uint32_t n = c < nc ? c_in[c] : 0u;
-      if (n > (uint32_t)kSlotCap) s_flag = 1u;
-      uint32_t t;
-      const uint32_t o = n_total + block_exclusive_scan(n, scratch, t);
-      if (c < nc) coff[c] = o;
-      n_total += t;
-    }
-    if (threadIdx.x == 0) coff[nc] = n_total;
-    if (n_total > (uint32_t)kCandCap) s_flag = 1u;
-    __syncthreads();
-    const bool overflow = s_flag != 0u;
-
-    if (!overflow) {
-      const uint32_t above_all = block_sum(above_local, scratch);
-      uint32_t rem = h.k_sel - above_all;  // rank of the threshold inside the list
-      // gather the listed patterns of all chunks, chunk by chunk
-      for (uint32_t i = threadIdx.x; i < n_total; i += kThreads) {
-        int lo = 0, hi = nc - 1;  // last chunk with coff[c] <= i
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (coff[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        cbits[i] = a.slots[((int64_t)head * nc + lo) * kSlotCap + (i - coff[lo])];
-      }
-      // the listed patterns share bits 31..19; radix over bits 18..9, then 8..0
-      uint32_t prefix = 0u, mask = 0u;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int shift = p == 0 ? 9 : 0;
-        const uint32_t nb = p == 0 ? 1024u : 512u;
-        for (uint32_t i = threadIdx.x; i < 1024u; i += kThreads) hist[i] = 0u;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n_total; i += kThreads) {
-          const uint32_t u = cbits[i] & 0x7FFFFu;
-          if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        const uint32_t b = nb - 1 - threadIdx.x;
-        const uint32_t cnt = threadIdx.x < nb ? hist[b] : 0u;
-        uint32_t tot;
-        const uint32_t before = block_exclusive_scan(cnt, scratch, tot);
-        if (threadIdx.x < nb && before < rem && rem <= before + cnt) {
-          s_digit = b;
-          s_rem = rem - before;
-        }
-        __syncthreads();
-        prefix |= s_digit << shift;
-        mask |= (nb - 1) << shift;
-        rem = s_rem;
-        __syncthreads();
-      }
-      thr = (cbits[0] & ~0x7FFFFu) | prefix;
-      need_eq = rem;
-      // above / equal counts of the listed entries of the chunks before this one
-      const uint32_t lim = coff[chunk];
-      uint32_t g = 0, q = 0;
-      for (uint32_t i = threadIdx.x; i < lim; i += kThreads) {
-        g += cbits[i] > thr;
-        q += cbits[i] == thr;
-      }
-      for (int c = threadIdx.x; c < chunk; c += kThreads) g += c_above[c];
-      prev_gt = block_sum(g, scratch);
-      prev_eq = block_sum(q, scratch);
-    } else {
-      uint32_t above;
-      thr = radix_over_row(h, rowbits, h.k_sel, hist, above);
-      need_eq = h.k_sel - above;
-      const int64_t lim = (int64_t)chunk * kChunk < h.rec_begin ? (int64_t)chunk * kChunk : h.rec_begin;
-      uint32_t g = 0, q = 0;
-      for (int64_t j = h.sink_end + threadIdx.x; j < lim; j += kThreads) {
-        const uint32_t u = rowbits[j];
-        g += u > thr;
-        q += u == thr;
-      }
-      prev_gt = block_sum(g, scratch);
-      prev_eq = block_sum(q, scratch);
-    }
-    eq_before = prev_eq;
-  }
-  // output offset of this chunk: mandatory keys, candidates above the
-  // threshold and the equal candidates taken, all in the chunks before it
-  uint32_t mand_before = 0;
-  for (int c = threadIdx.x; c < chunk; c += kThreads) mand_before += chunk_mandatory(h, c);
-  mand_before = block_sum(mand_before, scratch);
-  const uint32_t taken_before = need_eq < eq_before ? need_eq : eq_before;
-  const int64_t out_base = (int64_t)mand_before + prev_gt + taken_before;
-
-  uint32_t flags[4];  // 1: kept, 2: equal to the threshold (kept in index order)
-  uint32_t neq = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t j = j0 + e;
-    flags[e] = 0u;
+    flag[e] = 0u;
     if (j >= h.s) continue;
-    if (j < h.sink_end || j >= h.rec_begin) { flags[e] = 1u; continue; }
-    if (h.k_sel == 0) continue;
-    const uint32_t u = vbits[e];
-    if (u > thr) flags[e] = 1u;
-    else if (u == thr) { flags[e] = 2u; ++neq; }
+    if (h.keep_all || !is_candidate(h, j)) flag[e] = 1u;
+    else if (ranked) flag[e] = vb[e] > thr ? 1u : (vb[e] == thr ? 2u : 0u);
+    n_kept += flag[e] == 1u;
+    n_eq += flag[e] == 2u;
   }
-  uint32_t tot;
-  uint32_t eq_rank = eq_before + block_exclusive_scan(neq, scratch, tot);
-  uint32_t nkeep = 0;
+  // one scan of (kept << 16 | equal); both halves stay below 2^16
+  const uint32_t packed = (n_kept << 16) | n_eq;
+  const uint32_t incl = wave_inclusive_sum(packed);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - packed, total = 0;
+#pragma unroll
+  for (int w = 0; w < kCWaves; ++w) {
+    const uint32_t t = scratch[w];
+    before += w < wave ? t : 0u;
+    total += t;
+  }
+  uint32_t eq_seen = before & 0xFFFFu;
+  uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
+  const int64_t row0 = a.heads.offset[head];
+  int32_t* out = a.idx_out + row0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if (flags[e] == 2u) {
-      flags[e] = eq_rank < need_eq ? 1u : 0u;
-      ++eq_rank;
+    bool keep = flag[e] == 1u;
+    if (flag[e] == 2u) {
+      keep = eq_seen < quota;
+      ++eq_seen;
     }
-    nkeep += flags[e];
+    if (keep) {
+      const int64_t o = (int64_t)first + p;
+      const int32_t j = (int32_t)(j0 + e);
+      if (o < h.budget) {
+        out[o] = j;
+        if (GATHER) a.pos_out[row0 + o] = (int32_t)(a.pos_offset + j);
+      }
+      if (GATHER) kept_keys[p] = j;
+      ++p;
+    }
   }
-  const uint32_t pos0 = block_exclusive_scan(nkeep, scratch, tot);
-  int64_t o = out_base + pos0;
-  const int64_t limit = h.budget;  // never past this head's rows
+  if constexpr (GATHER) {
+    const uint32_t eq_all = total & 0xFFFFu;
+    int64_t n = (int64_t)(total >> 16) + (eq_all < quota ? eq_all : quota);
+    if (n > h.budget - (int64_t)first) n = h.budget - (int64_t)first;  // never past this head's rows
+    __syncthreads();
+    // a row is d/8 16-byte units of K then d/8 of V; consecutive threads take
+    // consecutive units, so each row is one contiguous read and write
+    const int cpr = a.d >> 3;
+    const int units = 2 * cpr;
+    const int rpp = kCompactThreads / units;  // rows per pass
+    const int u = threadIdx.x % units, r0 = threadIdx.x / units;
+    const bool is_k = u < cpr;
+    const int cu = is_k ? u : u - cpr;
+    const uint16_t* src = (is_k ? a.k + (int64_t)head * a.k_head : a.v + (int64_t)head * a.v_head) + cu * 8;
+    const int64_t tok = is_k ? a.k_tok : a.v_tok;
+    uint16_t* dst = (is_k ? a.k_out : a.v_out) + (row0 + first) * a.d + cu * 8;
+    const int nr = (int)n;
+    for (int r = r0; r < nr; r += kCopyUnroll * rpp) {
+      u32x4 buf[kCopyUnroll];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (flags[e]) {
-      if (o < limit) out[o] = (int32_t)(j0 + e);
-      ++o;
+      for (int i = 0; i < kCopyUnroll; ++i) {
+        const int rr = r + i * rpp;
+        const int key = kept_keys[rr < nr ? rr : r];
+        if (rr < nr) buf[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)key * tok);
+      }
+#pragma unroll
+      for (int i = 0; i < kCopyUnroll; ++i) {
+        const int rr = r + i * rpp;
+        if (rr < nr) *reinterpret_cast<u32x4*>(dst + (int64_t)rr * a.d) = buf[i];
+      }
     }
   }
 }
 
 }  // namespace
 
-size_t select_lds_bytes(int n_chunks) {
-  return (size_t)kCandCap * 4 + (size_t)(n_chunks + 1) * 4;
+size_t select_lds_bytes(int n_chunks, int n_subs) {
+  (void)n_chunks;
+  (void)n_subs;
+  return (size_t)kCandCap * 4;
 }
 
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
@@ -461,10 +592,12 @@ hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hi
   }
   e = hipLaunchKernel(reinterpret_cast<const void*>(&filter_kernel), chunks, dim3(kThreads), kargs, 0, st);
   if (e != hipSuccess) return e;
-  const size_t lds = select_lds_bytes(a.n_chunks);
-  e = ensure_lds(reinterpret_cast<const void*>(&select_kernel), lds);
+  const size_t lds = select_lds_bytes(a.n_chunks, a.n_subs);
+  const void* compact = a.k != nullptr ? reinterpret_cast<const void*>(&compact_kernel<true>)
+                                       : reinterpret_cast<const void*>(&compact_kernel<false>);
+  e = ensure_lds(compact, lds);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&select_kernel), chunks, dim3(kThreads), kargs, lds, st);
+  return hipLaunchKernel(compact, dim3((unsigned)(L.hkv * a.n_subs)), dim3(kCompactThreads), kargs, lds, st);
 }
 
 }  // namespace kvc
