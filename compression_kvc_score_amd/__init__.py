@@ -4,8 +4,9 @@ Python binding whose functions carry the C entry points' names."""
 from ._lib import (  # noqa: F401
     KVC_ERR_ALIGN, KVC_ERR_HIP, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE,
     KVC_MAX_KV_HEADS, KVC_MAX_POOL, KVC_MAX_ROWS, KVC_OK, LIB_PATH, KvcError, LayerDesc,
-    LayerOutputs, PreparedLayer, alloc_outputs, alloc_workspace, compress_layer, desc_for, kvc_budgets_inverse_stability,
-    kvc_compress_layer, kvc_gather_retained, kvc_retained_offsets, kvc_score_pass1,
+    LayerOutputs, PreparedLayer, PreparedSweep, SWEEP_STREAMS, alloc_outputs, alloc_sweep_workspace,
+    alloc_workspace, compress_layer, desc_for, kvc_budgets_inverse_stability,
+    kvc_compress_layer, kvc_compress_layers, kvc_gather_retained, kvc_retained_offsets, kvc_score_pass1,
     kvc_score_pass2, kvc_select_topk, kvc_strerror, kvc_version, kvc_workspace_size, lib,
     make_desc,
 )

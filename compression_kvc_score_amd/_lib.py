@@ -96,6 +96,7 @@ def _load():
         "kvc_select_topk": (ctypes.c_int, [D, P, P, P, P, SZ, P]),
         "kvc_gather_retained": (ctypes.c_int, [D, P, P, P, P, P, P, P, P]),
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -248,6 +249,43 @@ def kvc_compress_layer(desc, q_win, k, v, budgets, idx_out, k_out, v_out, pos_ou
                                 _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p.value
+    return arr
+
+
+def _sweep_args(desc, layers, budgets, outs, ws):
+    """Marshalled arguments of kvc_compress_layers (without the stream)."""
+    n = len(layers)
+    if len(outs) != n:
+        raise ValueError("one LayerOutputs per layer")
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int64))
+    if b.shape != (n, desc.hkv):
+        raise ValueError(f"budgets must have shape ({n}, {desc.hkv})")
+    if np.any(b < np.iinfo(np.int32).min) or np.any(b > np.iinfo(np.int32).max):
+        raise ValueError("budgets do not fit in int32")
+    b = np.ascontiguousarray(b.astype(np.int32))
+    cols = [_ptr_array([_bf16_ptr(l[j], name) for l in layers]) for j, name in enumerate(("q_win", "k", "v"))]
+    idx = _ptr_array([_dev_ptr(o.idx, "idx", 4) for o in outs])
+    kh = _ptr_array([_bf16_ptr(o.k_hat, "k_hat") for o in outs])
+    vh = _ptr_array([_bf16_ptr(o.v_hat, "v_hat") for o in outs])
+    pos = _ptr_array([_dev_ptr(o.pos, "pos", 4) for o in outs])
+    keep = (layers, outs, ws, b, cols, idx, kh, vh, pos)
+    args = (ctypes.byref(desc), n, cols[0], cols[1], cols[2], b.ctypes.data_as(ctypes.c_void_p),
+            idx, kh, vh, pos, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size())
+    return args, keep
+
+
+def kvc_compress_layers(desc, layers, budgets, outs, ws):
+    """layers: sequence of (q_win, k, v) tensors of one shape; budgets:
+    [n_layers][hkv]; outs: one LayerOutputs per layer; ws: sweep workspace
+    (alloc_sweep_workspace)."""
+    args, _keep = _sweep_args(desc, layers, budgets, outs, ws)
+    _check(_load().kvc_compress_layers(*args, _stream()))
+
+
 # ------------------------------------------------------------------ convenience
 
 @dataclass
@@ -265,6 +303,14 @@ class LayerOutputs:
 def alloc_workspace(desc: LayerDesc, device="cuda"):
     import torch
     return torch.empty(kvc_workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+SWEEP_STREAMS = 2  # layers in flight in kvc_compress_layers
+
+
+def alloc_sweep_workspace(desc: LayerDesc, device="cuda"):
+    import torch
+    return torch.empty(SWEEP_STREAMS * kvc_workspace_size(desc), dtype=torch.uint8, device=device)
 
 
 def alloc_outputs(desc: LayerDesc, budgets, device="cuda", with_intermediates=True) -> LayerOutputs:
@@ -333,3 +379,18 @@ class PreparedLayer:
 
     def kvc_compress_layer(self, stream=None):
         _check(self._L.kvc_compress_layer(*self._af, self._s(stream)))
+
+
+class PreparedSweep:
+    """Pre-marshalled kvc_compress_layers call over fixed buffers (the tensors
+    must stay alive while this object is used)."""
+
+    def __init__(self, desc, layers, budgets, outs, ws):
+        self._L = _load()
+        self.desc = desc
+        self.n_layers = len(layers)
+        self._args, self._keep = _sweep_args(desc, layers, budgets, outs, ws)
+
+    def kvc_compress_layers(self, stream=None):
+        st = ctypes.c_void_p(stream) if stream is not None else _stream()
+        _check(self._L.kvc_compress_layers(*self._args, st))

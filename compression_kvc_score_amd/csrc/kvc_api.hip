@@ -359,6 +359,59 @@ int run_gather(const Layer& L, const void* k, const void* v, const int32_t* idx,
   return KVC_OK;
 }
 
+// Pointers every whole-layer call needs.
+int check_layer_ptrs(const void* q_win, const void* k, const void* v, const int32_t* idx_out,
+                     const void* k_out, const void* v_out, const int32_t* pos_out) {
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(v, 16, "v"));
+  KVC_TRY(check_ptr(idx_out, 4, "idx_out"));
+  KVC_TRY(check_ptr(k_out, 16, "k_out"));
+  KVC_TRY(check_ptr(v_out, 16, "v_out"));
+  KVC_TRY(check_ptr(pos_out, 4, "pos_out"));
+  return KVC_OK;
+}
+
+// One validated layer onto one stream; m, z, scores NULL: in the workspace.
+int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* v, const HeadTable& ht,
+                  float* m_out, float* z_out, float* scores_out, int32_t* idx_out, void* k_out,
+                  void* v_out, int32_t* pos_out, void* ws, hipStream_t st) {
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
+  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
+  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
+  // pass 2 builds the selection histogram unless ranking uses pooled values
+  const bool hist_in_pass2 = L.pool == 1;
+  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
+  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
+  // the compaction of the selection copies the retained rows as it goes
+  return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out);
+}
+
+// The library's own streams for whole-layer sweeps, one set per device:
+// non-blocking (no implicit order with the null stream), default priority,
+// created on first use and kept until the process ends.
+constexpr int kSweepStreams = 2;
+int aux_stream(int j, hipStream_t& out) {
+  static std::mutex mu;
+  static hipStream_t streams[64][kSweepStreams - 1] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KVC_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev][j] == nullptr) {
+    e = hipStreamCreateWithFlags(&streams[dev][j], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      streams[dev][j] = nullptr;
+      return hip_fail(e, "hipStreamCreateWithFlags");
+    }
+  }
+  out = streams[dev][j];
+  return KVC_OK;
+}
+
 }  // namespace
 
 namespace kvc {
@@ -502,13 +555,7 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
                        size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
-  KVC_TRY(check_ptr(q_win, 16, "q_win"));
-  KVC_TRY(check_ptr(k, 16, "k"));
-  KVC_TRY(check_ptr(v, 16, "v"));
-  KVC_TRY(check_ptr(idx_out, 4, "idx_out"));
-  KVC_TRY(check_ptr(k_out, 16, "k_out"));
-  KVC_TRY(check_ptr(v_out, 16, "v_out"));
-  KVC_TRY(check_ptr(pos_out, 4, "pos_out"));
+  KVC_TRY(check_layer_ptrs(q_win, k, v, idx_out, k_out, v_out, pos_out));
   if (m_out) KVC_TRY(check_ptr(m_out, 4, "m_out"));
   if (z_out) KVC_TRY(check_ptr(z_out, 4, "z_out"));
   if (scores_out) KVC_TRY(check_ptr(scores_out, 4, "scores_out"));
@@ -516,20 +563,63 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
   KVC_TRY(head_table(L, budgets, ht));
   KVC_TRY(check_ws(L, ws, ws_bytes));
   KVC_TRY(check_lds(L));
+  return enqueue_layer(L, q_win, k, v, ht, m_out, z_out, scores_out, idx_out, k_out, v_out, pos_out, ws,
+                       static_cast<hipStream_t>(stream));
+}
 
-  const WsLayout lay = ws_layout(L);
-  char* wsb = static_cast<char*>(ws);
-  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
-  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  // pass 2 builds the selection histogram unless ranking uses pooled values
-  const bool hist_in_pass2 = L.pool == 1;
-  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
-  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
-  // the compaction of the selection copies the retained rows as it goes
-  KVC_TRY(run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out));
-  return KVC_OK;
+int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void* const* q_win,
+                        const void* const* k, const void* const* v, const int32_t* budgets,
+                        int32_t* const* idx_out, void* const* k_out, void* const* v_out,
+                        int32_t* const* pos_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  if (n_layers < 0) return fail(KVC_ERR_INVALID_ARG, "n_layers=%d < 0", n_layers);
+  if (n_layers == 0) return KVC_OK;
+  if (!q_win || !k || !v || !budgets || !idx_out || !k_out || !v_out || !pos_out)
+    return fail(KVC_ERR_INVALID_ARG, "a per-layer pointer array is NULL");
+  const size_t one = ws_layout(L).total;  // a multiple of 256
+  if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", kSweepStreams * one);
+  if (ws_bytes < kSweepStreams * one)
+    return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, kSweepStreams * one);
+  if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
+  std::vector<HeadTable> hts((size_t)n_layers);
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const int st = check_layer_ptrs(q_win[i], k[i], v[i], idx_out[i], k_out[i], v_out[i], pos_out[i]);
+    if (st != KVC_OK) return fail(st, "layer %d: %s", i, g_last_error.c_str());
+    const int bt = head_table(L, budgets + (size_t)i * L.hkv, hts[(size_t)i]);
+    if (bt != KVC_OK) return fail(bt, "layer %d: %s", i, g_last_error.c_str());
+  }
+  KVC_TRY(check_lds(L));
+  hipStream_t lanes[kSweepStreams];
+  lanes[0] = static_cast<hipStream_t>(stream);
+  for (int j = 1; j < kSweepStreams; ++j) KVC_TRY(aux_stream(j - 1, lanes[j]));
+  // fork: the other lanes start after the caller's earlier work
+  hipEvent_t ev;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  e = hipEventRecord(ev, lanes[0]);
+  for (int j = 1; j < kSweepStreams && e == hipSuccess; ++j) e = hipStreamWaitEvent(lanes[j], ev, 0);
+  hipEventDestroy(ev);
+  if (e != hipSuccess) return hip_fail(e, "sweep fork");
+  int status = KVC_OK;
+  for (int32_t i = 0; i < n_layers && status == KVC_OK; ++i) {
+    const int j = i % kSweepStreams;
+    status = enqueue_layer(L, q_win[i], k[i], v[i], hts[(size_t)i], nullptr, nullptr, nullptr, idx_out[i],
+                           k_out[i], v_out[i], pos_out[i], static_cast<char*>(ws) + j * one, lanes[j]);
+  }
+  // join: later work on the caller's stream waits for every lane (also after
+  // a failed launch, so that nothing of this call outlives the caller's order)
+  for (int j = 1; j < kSweepStreams; ++j) {
+    hipEvent_t jv;
+    e = hipEventCreateWithFlags(&jv, hipEventDisableTiming);
+    if (e == hipSuccess) {
+      e = hipEventRecord(jv, lanes[j]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(lanes[0], jv, 0);
+      hipEventDestroy(jv);
+    }
+    if (e != hipSuccess && status == KVC_OK) status = hip_fail(e, "sweep join");
+  }
+  return status;
 }
 
 }  // extern "C"

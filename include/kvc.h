@@ -199,16 +199,38 @@ int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v
                         kvc_stream_t stream);
 
 /*
- * The whole layer: pass 1, pass 2, (pool), select, gather, enqueued in that
- * order on one stream. m_out, z_out, scores_out and idx_out may be NULL (they
- * then live in the workspace); k_out, v_out and pos_out are required.
- * Results equal those of the four staged calls bit for bit.
+ * The whole layer: pass 1, pass 2, (pool), select and gather, enqueued in
+ * that order on one stream (the gather runs inside the selection's last
+ * kernel). m_out, z_out and scores_out may be NULL (they then live in the
+ * workspace); idx_out, k_out, v_out and pos_out are required. Results equal
+ * those of the four staged calls bit for bit.
  */
 int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void* k,
                        const void* v, const int32_t* budgets,
                        float* m_out, float* z_out, float* scores_out, int32_t* idx_out,
                        void* k_out, void* v_out, int32_t* pos_out,
                        void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * A layer-major sweep (TideKV, Fig. 2 caption: layers are compressed one
+ * after another at their layer boundaries): n_layers layers of the one shape
+ * `desc`, layer i compressed exactly as kvc_compress_layer would (same
+ * outputs, bit for bit, with m, z and scores kept in the workspace). Layers
+ * alternate between `stream` and a second stream that the library creates
+ * per device on first use (non-blocking, default priority, kept until the
+ * process ends), so that one layer's selection and gather overlap the next
+ * layer's scans. The call is ordered after earlier work on `stream`, and
+ * later work on `stream` is ordered after all of it.
+ * q_win, k, v, idx_out, k_out, v_out, pos_out: HOST arrays of n_layers device
+ * pointers, each as for kvc_compress_layer; budgets: HOST int32
+ * [n_layers][hkv]. ws: at least 2 * kvc_workspace_size(desc) bytes (one
+ * workspace per stream), 256-byte aligned. n_layers == 0 enqueues nothing.
+ */
+int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers,
+                        const void* const* q_win, const void* const* k, const void* const* v,
+                        const int32_t* budgets, int32_t* const* idx_out,
+                        void* const* k_out, void* const* v_out, int32_t* const* pos_out,
+                        void* ws, size_t ws_bytes, kvc_stream_t stream);
 
 #ifdef __cplusplus
 }

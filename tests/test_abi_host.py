@@ -152,6 +152,55 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert msg.startswith("KVC_ERR_WORKSPACE")
 
 
+def test_sweep_rejects_bad_arguments_before_launch():
+    """kvc_compress_layers checks every layer's pointers and budgets and the
+    doubled workspace before anything is enqueued (no GPU needed)."""
+    lib = kvc.lib()
+    d = base_desc()
+    dd = ctypes.byref(d)
+    ws_n = kvc.kvc_workspace_size(d)
+    n = 3
+
+    def arr(addrs):
+        a = (ctypes.c_void_p * len(addrs))()
+        for i, x in enumerate(addrs):
+            a[i] = x
+        return a
+
+    good = [0x10000 + 0x1000 * i for i in range(n)]
+    b = np.full((n, 8), 4096, dtype=np.int32)
+    bp = b.ctypes.data_as(ctypes.c_void_p)
+    cols = [arr(good) for _ in range(7)]
+    ws = _fake(0x100000)
+
+    def call(cols=cols, budgets=bp, ws=ws, ws_bytes=2 * ws_n, n_layers=n):
+        return lib.kvc_compress_layers(dd, n_layers, cols[0], cols[1], cols[2], budgets, cols[3],
+                                       cols[4], cols[5], cols[6], ws, ws_bytes, None)
+
+    assert call(n_layers=0) == kvc.KVC_OK  # nothing to do, nothing touched
+    assert call(n_layers=-1) == kvc.KVC_ERR_INVALID_ARG
+    assert call(ws_bytes=2 * ws_n - 1) == kvc.KVC_ERR_WORKSPACE
+    assert call(ws_bytes=ws_n) == kvc.KVC_ERR_WORKSPACE  # one workspace per stream
+    assert call(ws=_fake(0x100080)) == kvc.KVC_ERR_ALIGN
+    assert call(budgets=None) == kvc.KVC_ERR_INVALID_ARG
+    for j in range(7):
+        c = list(cols)
+        c[j] = None
+        assert call(cols=c) == kvc.KVC_ERR_INVALID_ARG
+        bad = list(good)
+        bad[2] = 0  # the last layer's pointer is NULL
+        c[j] = arr(bad)
+        assert call(cols=c) == kvc.KVC_ERR_INVALID_ARG
+        assert "layer 2" in lib.kvc_last_error().decode()
+    c = list(cols)
+    c[1] = arr([good[0], good[1] + 2, good[2]])  # k of layer 1 misaligned
+    assert call(cols=c) == kvc.KVC_ERR_ALIGN
+    b2 = b.copy()
+    b2[1, 3] = 10  # below the mandatory set
+    assert call(budgets=b2.ctypes.data_as(ctypes.c_void_p)) == kvc.KVC_ERR_INVALID_ARG
+    assert "layer 1" in lib.kvc_last_error().decode()
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_budgets_match_oracle(seed):
     rng = np.random.default_rng(seed)

@@ -298,6 +298,41 @@ def test_deterministic_repeat():
         np.testing.assert_array_equal(a1[key], a2[key], err_msg=key)
 
 
+@pytest.mark.parametrize("name,s,n_layers", [("llama8b_16k", 8192, 5), ("qwen14b_hetero_64k", 8192, 4)])
+def test_sweep_equals_layer_by_layer(name, s, n_layers):
+    """kvc_compress_layers over several layers (alternating between the
+    caller's stream and the library's second stream) writes what one
+    kvc_compress_layer call per layer writes, bit for bit, and later work on
+    the caller's stream sees all of it."""
+    cfg = get_config(name).with_(s=s)
+    xs = [layer_inputs(cfg, l) for l in range(n_layers)]
+    layers = [dev_inputs(x) for x in xs]
+    budgets = np.stack([budgets_for(cfg, x) for x in xs])
+    desc = desc_from(cfg, *layers[0])
+    say(f"sweep {name}: {n_layers} layers one by one")
+    want = [run_fused(desc, *layers[i], budgets[i], intermediates=False) for i in range(n_layers)]
+    outs = [kvc.alloc_outputs(desc, budgets[i], with_intermediates=False) for i in range(n_layers)]
+    for o in outs:  # stale contents must all be overwritten
+        o.idx.fill_(-7)
+        o.k_hat.view(torch.int16).fill_(-7)
+    ws = kvc.alloc_sweep_workspace(desc)
+    say(f"sweep {name}: one sweep call")
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws)
+    # ordered after the sweep on the caller's stream, no host synchronisation
+    copies = [(o.idx.clone(), o.k_hat.clone(), o.v_hat.clone(), o.pos.clone()) for o in outs]
+    torch.cuda.synchronize()
+    for i in range(n_layers):
+        np.testing.assert_array_equal(copies[i][0].cpu().numpy(), want[i]["idx"], err_msg=f"idx {i}")
+        np.testing.assert_array_equal(from_dev_bits(copies[i][1]), want[i]["k_hat"], err_msg=f"k_hat {i}")
+        np.testing.assert_array_equal(from_dev_bits(copies[i][2]), want[i]["v_hat"], err_msg=f"v_hat {i}")
+        np.testing.assert_array_equal(copies[i][3].cpu().numpy(), want[i]["pos"], err_msg=f"pos {i}")
+    # a second sweep into the same buffers gives the same bits again
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws)
+    torch.cuda.synchronize()
+    for i in range(n_layers):
+        np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"], err_msg=f"repeat idx {i}")
+
+
 def test_binding_errors_on_gpu():
     cfg = get_config("tiny")
     x = layer_inputs(cfg, 0)
