@@ -302,11 +302,13 @@ constexpr int kSpecEntries = kSpecRounds * kWave - kSlotHdr;
 // k-th best candidate, the number need_eq of candidates equal to T that are
 // kept, and, for the keys before sub-chunk `sub`, the candidates above T and
 // equal to T. One speculative read per slot brings its header and most of its
-// list. Returns false (nothing resolved) if a chunk's slot or the gathered
-// list overflowed.
+// list; once b* is known, on_bstar(b*) runs (before the radix rounds).
+// Returns false (nothing resolved) if a chunk's slot or the gathered list
+// overflowed.
+template <typename OnBstar>
 __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int head, int sub,
                                    const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
-                                   uint32_t& gt_before, uint32_t& eq_before) {
+                                   uint32_t& gt_before, uint32_t& eq_before, OnBstar on_bstar) {
   constexpr int NW = kCWaves;
   __shared__ uint32_t s_count, s_flag, s_bstar;
   const int nc = a.n_chunks;
@@ -372,6 +374,7 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
   }
   block_sum2<NW>(ab_all, ab_before, m.scratch);
   if (s_flag != 0u) return false;
+  on_bstar(s_bstar);
 
   // radix over pattern bits 18..9, then 8..0 (the listed patterns share the rest)
   const uint32_t n_total = s_count;
@@ -465,6 +468,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
   const bool ranked = !h.keep_all && h.k_sel > 0;
   uint32_t vb[4] = {0u, 0u, 0u, 0u};
   uint32_t thr = 0xFFFFFFFFu, quota = 0u, first;
+  uint32_t touched[4][4] = {};  // words of prefetched rows (consumed at the end)
   if (ranked) {
     const float* vals = a.vals + (int64_t)head * h.s;
 #pragma unroll
@@ -480,8 +484,39 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     m.hist2 = hist2;
     m.scratch = scratch;
     m.pick = pick;
+    // with the copy: once b* is known, touch the rows of the keys that are
+    // kept for sure (mandatory, or above b*) or may be (inside b*), so that
+    // they are in L2 when the copy runs after the resolve
+    auto prefetch = [&](uint32_t bstar) {
+      if constexpr (GATHER) {
+        // decide for all four keys first: a decision after a prefetch would
+        // wait for it
+        bool want[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t j = j0 + e;
+          want[e] = j < h.s && (!is_candidate(h, j) || bin_of(vb[e]) >= bstar);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (want[e]) {
+            // one word per 128-byte line; the words are only consumed at the
+            // end of the kernel, so nothing waits for them before then
+            const int64_t j = j0 + e;
+            const uint16_t* kr = a.k + j * a.k_tok + (int64_t)head * a.k_head;
+            const uint16_t* vr = a.v + j * a.v_tok + (int64_t)head * a.v_head;
+            touched[e][0] = *reinterpret_cast<const uint32_t*>(kr);
+            touched[e][1] = *reinterpret_cast<const uint32_t*>(vr);
+            if (a.d > 64) {
+              touched[e][2] = *reinterpret_cast<const uint32_t*>(kr + 64);
+              touched[e][3] = *reinterpret_cast<const uint32_t*>(vr + 64);
+            }
+          }
+        }
+      }
+    };
     uint32_t need_eq, gt_before, eq_before;
-    if (!resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before))
+    if (!resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch))
       resolve_from_row(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
     quota = need_eq > eq_before ? need_eq - eq_before : 0u;  // equal candidates this sub-chunk may take
     first = mandatory_in(h, 0, s0) + gt_before + (need_eq < eq_before ? need_eq : eq_before);
@@ -565,6 +600,10 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
         if (rr < nr) *reinterpret_cast<u32x4*>(dst + (int64_t)rr * a.d) = buf[i];
       }
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) asm volatile("" : : "v"(touched[e][q]));
   }
 }
 
