@@ -87,6 +87,26 @@ __device__ void block_sum2(uint32_t& x, uint32_t& y, uint32_t* scratch) {
   __syncthreads();
 }
 
+// Sums over a workgroup of NW wavefronts of N values per thread (every
+// thread gets all N). Uses `scratch` (N * NW entries) in LDS.
+template <int NW, int N>
+__device__ void block_sums(uint32_t (&x)[N], uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t inc = wave_inclusive_sum(x[i]);
+    if (lane == 63) scratch[i * NW + wave] = inc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i] = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x[i] += scratch[i * NW + w];
+  }
+  __syncthreads();
+}
+
 struct HeadGeom {
   int64_t s, sink_end, rec_begin;
   int64_t budget;
@@ -298,6 +318,116 @@ constexpr int kGroupChunks = 4;             // chunk slots a wavefront reads per
 constexpr int kSpecRounds = 4;              // 64-word reads per slot: header + 240 entries
 constexpr int kSpecEntries = kSpecRounds * kWave - kSlotHdr;
 
+enum ResolveOutcome { kResolved = 0, kNeedLists = 1, kNeedRow = 2 };
+
+// As resolve_from_lists, for heads of at most NG x 16 chunks whose lists all
+// fit in the first 256 words of their slots: the words stay in registers
+// (wavefront w holds chunks 16g + 4w + i, word 64r + lane) and the radix
+// histograms are built from them directly. Returns kNeedLists if a list is
+// longer (nothing done yet) and kNeedRow if a slot overflowed.
+template <int NG, typename OnBstar>
+__device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int head, int sub,
+                                    const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
+                                    uint32_t& gt_before, uint32_t& eq_before, OnBstar on_bstar) {
+  constexpr int NW = kCWaves;
+  constexpr int GC = NW * kGroupChunks;  // chunks per group
+  const int nc = a.n_chunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t* slots = a.slots + (int64_t)head * nc * kSlotStride;
+  uint32_t v[NG][kGroupChunks][kSpecRounds];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = g * GC + wave * kGroupChunks + i;
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r)
+        v[g][i][r] = c < nc ? slots[(int64_t)c * kSlotStride + r * kWave + lane] : 0u;
+    }
+  // headers (wavefront-uniform): listed entries per chunk; candidates above b*
+  // in all sub-chunks and in those before this one; long lists; b* (chunk 0)
+  uint32_t n[NG][kGroupChunks];
+  uint32_t sums[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = g * GC + wave * kGroupChunks + i;
+      n[g][i] = 0u;
+#pragma unroll
+      for (int q = 0; q < kSubsPerChunk; ++q) {
+        n[g][i] += (uint32_t)__builtin_amdgcn_readlane((int)v[g][i][0], q);
+        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)v[g][i][0], kSubsPerChunk + q);
+        sums[0] += ab;
+        sums[1] += c * kSubsPerChunk + q < sub ? ab : 0u;
+      }
+      if (n[g][i] > (uint32_t)kSpecEntries) sums[2] += n[g][i] > (uint32_t)kSlotCap ? 0x10000u : 1u;
+    }
+  if (wave == 0) sums[3] = (uint32_t)__builtin_amdgcn_readlane((int)v[0][0][0], 2 * kSubsPerChunk);
+  if (lane != 0) {  // wavefront-uniform: count once per wavefront
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sums[i] = 0u;
+  }
+  block_sums<NW, 4>(sums, m.scratch);
+  if (sums[2] >= 0x10000u) return kNeedRow;
+  if (sums[2] != 0u) return kNeedLists;
+  const uint32_t bstar = sums[3];
+  on_bstar(bstar);
+
+  // radix over pattern bits 18..9, then 8..0 (the listed patterns share the rest)
+  uint32_t rem = h.k_sel - sums[0];  // rank of the threshold inside the lists
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = r * kWave + lane - kSlotHdr;
+        if (e >= 0 && (uint32_t)e < n[g][i]) atomicAdd(&m.hist1[(v[g][i][r] >> 9) & 1023u], 1u);
+      }
+  __syncthreads();
+  if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
+  __syncthreads();
+  const uint32_t d1 = m.pick[0];
+  rem = m.pick[1];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = r * kWave + lane - kSlotHdr;
+        if (e >= 0 && (uint32_t)e < n[g][i] && ((v[g][i][r] >> 9) & 1023u) == d1)
+          atomicAdd(&m.hist2[v[g][i][r] & 511u], 1u);
+      }
+  __syncthreads();
+  if (threadIdx.x < kWave) pick_digit_wave<512>(m.hist2, rem, m.pick);
+  __syncthreads();
+  const uint32_t low = (d1 << 9) | m.pick[0];
+  need_eq = m.pick[1];
+  thr = (bstar << 19) | low;
+  // listed candidates of the sub-chunks before this one
+  uint32_t gq[2] = {0u, 0u};
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = r * kWave + lane - kSlotHdr;
+        const uint32_t x = v[g][i][r];
+        if (e >= 0 && (uint32_t)e < n[g][i] && (int)(x >> 19) < sub) {
+          gq[0] += (x & 0x7FFFFu) > low;
+          gq[1] += (x & 0x7FFFFu) == low;
+        }
+      }
+  block_sums<NW, 2>(gq, m.scratch);
+  gt_before = sums[1] + gq[0];
+  eq_before = gq[1];
+  return kResolved;
+}
+
 // Threshold of one head, resolved from the chunk lists: the pattern T of the
 // k-th best candidate, the number need_eq of candidates equal to T that are
 // kept, and, for the keys before sub-chunk `sub`, the candidates above T and
@@ -458,7 +588,7 @@ template <bool GATHER>
 __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ uint32_t hist1[1024], hist2[512];
-  __shared__ uint32_t scratch[2 * kCWaves], pick[2];
+  __shared__ uint32_t scratch[4 * kCWaves], pick[2];
   __shared__ int32_t kept_keys[GATHER ? kSub : 1];
   const int head = blockIdx.x / a.n_subs, sub = blockIdx.x % a.n_subs;
   const HeadGeom h = head_geom(a, head);
@@ -516,8 +646,16 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
       }
     };
     uint32_t need_eq, gt_before, eq_before;
-    if (!resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch))
-      resolve_from_row(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
+    constexpr int GC = kCWaves * kGroupChunks;
+    int outcome = kNeedLists;
+    if (a.n_chunks <= GC)
+      outcome = resolve_in_registers<1>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+    else if (a.n_chunks <= 2 * GC)
+      outcome = resolve_in_registers<2>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+    if (outcome == kNeedLists)
+      outcome = resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch) ? kResolved
+                                                                                                   : kNeedRow;
+    if (outcome == kNeedRow) resolve_from_row(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
     quota = need_eq > eq_before ? need_eq - eq_before : 0u;  // equal candidates this sub-chunk may take
     first = mandatory_in(h, 0, s0) + gt_before + (need_eq < eq_before ? need_eq : eq_before);
   } else {

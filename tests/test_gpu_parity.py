@@ -221,6 +221,41 @@ def test_select_heavy_ties_take_the_slow_path_exactly(case):
         np.testing.assert_array_equal(got[g], want, err_msg=f"head {g}")
 
 
+@pytest.mark.parametrize("case", ["long_list", "many_chunks", "two_groups"])
+def test_select_list_paths_are_exact(case):
+    """Each way the compaction resolves the threshold gives the oracle's
+    selection: lists held in registers (up to 32 chunks of 4096 keys), a list
+    longer than one read brings (gathered through LDS), and more chunks than
+    the registers hold."""
+    rng = np.random.default_rng({"long_list": 21, "many_chunks": 22, "two_groups": 23}[case])
+    hkv = 2
+    if case == "long_list":
+        s = 40000
+        vals = (rng.random((hkv, s)) * 0.5).astype(np.float32)
+        vals[:, 20000:20300] = 2.0 + rng.random((hkv, 300)).astype(np.float32)  # surely kept
+        # 600 distinct values in one histogram bin, all inside one 4096-key chunk
+        vals[:, 8200:8800] = (1.0 + np.arange(600) * 2.0 ** -16).astype(np.float32)
+        budgets = np.array([36 + 300 + 250, 36 + 300 + 599])
+    elif case == "many_chunks":
+        s = 4096 * 36 + 123
+        vals = rng.random((hkv, s)).astype(np.float32)
+        budgets = np.array([4096, 30001])
+    else:
+        s = 4096 * 30 + 77
+        vals = rng.random((hkv, s)).astype(np.float32) ** 3
+        budgets = np.array([4096, 777])
+    desc = kvc.make_desc(s, 8, 8, hkv, 64, 64, n_sink=4, n_recent=32, pool=1)
+    scores = torch.from_numpy(vals).cuda()
+    ws = kvc.alloc_workspace(desc)
+    off = kvc.kvc_retained_offsets(desc, budgets)
+    idx = torch.empty(int(off[-1]), dtype=torch.int32, device="cuda")
+    kvc.kvc_select_topk(desc, scores, budgets, idx, ws)
+    got = split_heads(idx.cpu().numpy(), off)
+    for g in range(hkv):
+        want = oracle.select_head(vals[g].astype(np.float64), int(budgets[g]), 4, 32)
+        np.testing.assert_array_equal(got[g], want, err_msg=f"head {g}")
+
+
 def test_gather_given_indices_strided_and_offset():
     rng = np.random.default_rng(4)
     s, hkv, d = 3000, 4, 128
