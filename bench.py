@@ -248,6 +248,24 @@ def main(argv=None):
     log(f"sweep of {K} layers (2 in flight): {sweep_wall * 1e3 / K:.4f} ms/layer wall, "
         f"{sweep_gpu_ms:.4f} ms/layer on GPU")
 
+    # ---- cold layers: before each layer a 512 MiB write evicts the memory-side
+    # cache (256 MB), then HIP events bracket one kvc_compress_layer call;
+    # median and p10 / p90 over the resident layers
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ev = []
+    for i in range(n_layers):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        prepared[i].kvc_compress_layer(sp)
+        e1.record(stream)
+        cold_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_us = np.array([a.elapsed_time(b) * 1e3 for a, b in cold_ev])
+    del flush
+    log(f"cold layers (cache flushed before each): median {np.median(cold_us):.1f} us, "
+        f"p10 {np.percentile(cold_us, 10):.1f}, p90 {np.percentile(cold_us, 90):.1f} over {n_layers}")
+
     # ---- per-stage breakdown: each staged entry point called K times back to
     # back over the same layers (same kernels and launch configuration as the
     # whole-layer call; every stage reads what the timed region wrote), HIP
@@ -306,6 +324,11 @@ def main(argv=None):
                              for n in ("pass1", "pass2")},
         "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
         "retained_arena_bytes": arena_bytes,
+        "cold_layer_us": {"median": round(float(np.median(cold_us)), 2),
+                          "p10": round(float(np.percentile(cold_us, 10)), 2),
+                          "p90": round(float(np.percentile(cold_us, 90)), 2), "layers": n_layers,
+                          "note": "512 MiB write before each layer evicts the memory-side cache; "
+                                  "HIP events around one kvc_compress_layer call"},
         "sweep": {
             "entry_point": "kvc_compress_layers", "layers_in_flight": kvc.SWEEP_STREAMS,
             "value": round(cfg.s * K / sweep_wall, 1), "unit": "tokens/s",
