@@ -27,6 +27,25 @@ observation-by-prefix tensor that the page's scan avoids:
   gather    K_hat = K[idx, g], V_hat = V[idx, g] bit for bit;
             pos = pos_offset + idx
 
+Score modes other than the softmax weights (HillInfer, Algorithmic
+Simplification: ranking needs only the order of the keys and the softmax is
+monotonic, so the raw inner product Q.K^T is used, without exponentiation or
+scaling; Streaming Execution and Asymmetric Precision: those inner products in
+INT8 for the ranking only, the streamed keys cast on the fly, the original
+rows retrieved afterwards):
+
+  logit     score[g,j] = sum over the visible rows (h, i) of group g of
+            <Q_win[i,h], K[j,g]>, with no scale; for one query row this is the
+            page's raw inner product. Summed over rows it is one dot product
+            of K[j,g] with the pooled query of the rows that see key j.
+  int8      the pooled query (summed exactly, rounded once to fp32) and each
+            key row quantised symmetrically per vector: s = max |x|,
+            x8 = round-half-even(x * fp32(127 / s)), all in fp32; the integer
+            dot product is exact and the score is
+            fp32(fp32(dot * fp32(s_q / 127)) * fp32(s_k / 127)).
+  overlap   the overlap coefficient |A & B| / min(|A|, |B|) of two retained
+            index sets (HeteroCache summary, Key Contributions item 1).
+
 Per-KV-head budgets for the heterogeneous workload follow the inverse
 stability weighting of the HeteroCache summary (Methodology, Phase 2):
 w_h = 1 / S_stable,h and K_h proportional to w_h, rounded to integers that sum
@@ -121,6 +140,89 @@ def scores(q: np.ndarray, k: np.ndarray, scale: float | None = None) -> np.ndarr
         a = e / e.sum(axis=2, keepdims=True)
         out[g] = a.sum(axis=(0, 1))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Raw inner-product ranking (HillInfer, Algorithmic Simplification) and its
+# INT8 form (HillInfer, Streaming Execution and Asymmetric Precision)
+# ---------------------------------------------------------------------------
+
+def logit_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Raw inner-product scores [Hkv, S] float64: for key j of KV head g, the
+    unscaled logits <Q_win[i,h], K[j,g]> summed over the rows (h in group g,
+    window query i) that see key j under the causal mask."""
+    w, hq, d = q.shape
+    s, hkv, _ = k.shape
+    out = np.empty((hkv, s))
+    for g in range(hkv):
+        lg = group_logits(q, k, g, 1.0)
+        lg[~np.isfinite(lg)] = 0.0        # masked (future) keys contribute nothing
+        out[g] = lg.sum(axis=(0, 1))
+    return out
+
+
+def first_visible_row(s: int, w: int) -> np.ndarray:
+    """For each key j, the first window row i that sees it: max(0, j - (S-W))."""
+    return np.maximum(np.arange(s) - (s - w), 0)
+
+
+def pooled_query(q_bits: np.ndarray, hkv: int, t: int) -> np.ndarray:
+    """fp32 [Hkv, D]: the sum of the bf16 window queries of each group over
+    rows i >= t, summed exactly (math.fsum) and rounded once to fp32."""
+    import math
+    q = bf16_to_f64(q_bits)
+    w, hq, d = q.shape
+    grp = hq // hkv
+    out = np.empty((hkv, d), dtype=np.float32)
+    for g in range(hkv):
+        blk = q[t:, g * grp:(g + 1) * grp, :].reshape(-1, d)
+        for c in range(d):
+            out[g, c] = np.float32(math.fsum(blk[:, c]))
+    return out
+
+
+def quantize_int8(x: np.ndarray):
+    """Symmetric per-vector INT8 codes of fp32 vectors along the last axis.
+
+    s = max |x|; each element becomes round-half-even(x * fp32(127 / s)),
+    computed in fp32 (the decision the kernel takes, in its precision); the
+    dequantisation step is fp32(s / 127). An all-zero vector gives zero codes
+    and a zero step. Returns (codes int32, step float32).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    s = np.max(np.abs(x), axis=-1).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = (np.float32(127.0) / safe).astype(np.float32)
+    codes = np.rint((x * r[..., None]).astype(np.float32)).astype(np.int32)
+    codes = np.where((s > 0)[..., None], codes, 0)
+    step = np.where(s > 0, (s / np.float32(127.0)).astype(np.float32), np.float32(0.0)).astype(np.float32)
+    return codes, step
+
+
+def logit_scores_int8(q_bits: np.ndarray, k_bits: np.ndarray) -> np.ndarray:
+    """INT8 raw inner-product scores [Hkv, S] float32: the pooled query of the
+    rows that see key j and the key row, each quantised by quantize_int8; the
+    score is fp32(fp32(dot * step_q) * step_k) with the exact integer dot."""
+    w, hq, d = q_bits.shape
+    s, hkv, _ = k_bits.shape
+    kf = bf16_to_f64(k_bits).astype(np.float32)        # exact: bf16 fits fp32
+    k8, ks = quantize_int8(kf)                          # [S, Hkv, D], [S, Hkv]
+    t_of = first_visible_row(s, w)
+    out = np.empty((hkv, s), dtype=np.float32)
+    for t in np.unique(t_of):
+        q8, qs = quantize_int8(pooled_query(q_bits, hkv, int(t)))   # [Hkv, D], [Hkv]
+        keys = np.nonzero(t_of == t)[0]
+        for g in range(hkv):
+            dot = k8[keys, g, :].astype(np.int64) @ q8[g].astype(np.int64)
+            out[g, keys] = ((dot.astype(np.float32) * qs[g]).astype(np.float32) * ks[keys, g]).astype(np.float32)
+    return out
+
+
+def overlap_coefficient(a, b) -> float:
+    """|A & B| / min(|A|, |B|) of two index sets; 1.0 when either is empty."""
+    a, b = np.unique(np.asarray(a)), np.unique(np.asarray(b))
+    n = min(a.size, b.size)
+    return 1.0 if n == 0 else np.intersect1d(a, b).size / n
 
 
 # ---------------------------------------------------------------------------
@@ -235,8 +337,8 @@ def inverse_stability_budgets(s_stable, total: int) -> np.ndarray:
 
 @dataclass
 class LayerResult:
-    m: np.ndarray          # [Hq, W]
-    z: np.ndarray          # [Hq, W]
+    m: np.ndarray          # [Hq, W] (None unless score_mode == "softmax")
+    z: np.ndarray          # [Hq, W] (None unless score_mode == "softmax")
     scores: np.ndarray     # [Hkv, S] (not pooled)
     idx: list              # per head, ascending int64
     k_hat: np.ndarray      # [sum K_h, D] uint16
@@ -245,11 +347,22 @@ class LayerResult:
 
 
 def compress_layer(q_bits, k_bits, v_bits, budgets, n_sink, n_recent,
-                   scale=None, pool=1, pos_offset=0) -> LayerResult:
+                   scale=None, pool=1, pos_offset=0, score_mode="softmax") -> LayerResult:
+    """One layer with scores of ``score_mode``: "softmax" (the default),
+    "logit" (raw inner products) or "int8" (their INT8 form)."""
     q = bf16_to_f64(q_bits)
     k = bf16_to_f64(k_bits)
-    m, z = normalizers(q, k, scale)
-    sc = scores(q, k, scale)
+    if score_mode == "softmax":
+        m, z = normalizers(q, k, scale)
+        sc = scores(q, k, scale)
+    elif score_mode == "logit":
+        m = z = None
+        sc = logit_scores(q, k)
+    elif score_mode == "int8":
+        m = z = None
+        sc = logit_scores_int8(q_bits, k_bits).astype(np.float64)
+    else:
+        raise ValueError(f"unknown score mode {score_mode!r}")
     sel_vals = maxpool(sc, pool) if pool > 1 else sc
     idx = select(sel_vals, budgets, n_sink, n_recent)
     k_hat, v_hat, pos = gather(k_bits, v_bits, idx, pos_offset)
