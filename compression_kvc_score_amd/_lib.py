@@ -26,6 +26,9 @@ KVC_ERR_HIP = -5
 KVC_MAX_KV_HEADS = 64
 KVC_MAX_ROWS = 256
 KVC_MAX_POOL = 31
+KVC_SCORE_SOFTMAX = 0
+KVC_SCORE_LOGIT = 1
+KVC_SCORE_LOGIT_INT8 = 2
 
 
 class KvcError(RuntimeError):
@@ -47,7 +50,7 @@ class LayerDesc(ctypes.Structure):
         ("n_sink", ctypes.c_int32),
         ("n_recent", ctypes.c_int32),
         ("pool", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("score_mode", ctypes.c_int32),
         ("pos_offset", ctypes.c_int64),
         ("q_tok_stride", ctypes.c_int64),
         ("q_head_stride", ctypes.c_int64),
@@ -59,9 +62,10 @@ class LayerDesc(ctypes.Structure):
 
 
 def make_desc(s, w, hq, hkv, d, block=256, scale=0.0, n_sink=0, n_recent=0, pool=1,
-              pos_offset=0, q_strides=(0, 0), k_strides=(0, 0), v_strides=(0, 0)) -> LayerDesc:
+              pos_offset=0, q_strides=(0, 0), k_strides=(0, 0), v_strides=(0, 0),
+              score_mode=0) -> LayerDesc:
     return LayerDesc(s=s, w=w, hq=hq, hkv=hkv, d=d, block=block, scale=scale, n_sink=n_sink,
-                     n_recent=n_recent, pool=pool, reserved0=0, pos_offset=pos_offset,
+                     n_recent=n_recent, pool=pool, score_mode=score_mode, pos_offset=pos_offset,
                      q_tok_stride=q_strides[0], q_head_stride=q_strides[1],
                      k_tok_stride=k_strides[0], k_head_stride=k_strides[1],
                      v_tok_stride=v_strides[0], v_head_stride=v_strides[1])
@@ -97,6 +101,7 @@ def _load():
         "kvc_gather_retained": (ctypes.c_int, [D, P, P, P, P, P, P, P, P]),
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "kvc_overlap_coefficient": (ctypes.c_int, [D, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -156,7 +161,7 @@ def _host_i32(arr, n, name):
 
 
 def desc_for(q_win, k, v=None, *, block=256, scale=0.0, n_sink=0, n_recent=0, pool=1,
-             pos_offset=0) -> LayerDesc:
+             pos_offset=0, score_mode=0) -> LayerDesc:
     """Descriptor for tensors Q_win [W, hq, D] and K (V) [S, hkv, D] with their
     strides (the head dimension must be contiguous)."""
     w, hq, d = q_win.shape
@@ -165,7 +170,7 @@ def desc_for(q_win, k, v=None, *, block=256, scale=0.0, n_sink=0, n_recent=0, po
         raise ValueError("Q_win and K head dimensions differ")
     vs = (v.stride(0), v.stride(1)) if v is not None else (0, 0)
     return make_desc(s, w, hq, hkv, d, block=block, scale=scale, n_sink=n_sink,
-                     n_recent=n_recent, pool=pool, pos_offset=pos_offset,
+                     n_recent=n_recent, pool=pool, pos_offset=pos_offset, score_mode=score_mode,
                      q_strides=(q_win.stride(0), q_win.stride(1)),
                      k_strides=(k.stride(0), k.stride(1)), v_strides=vs)
 
@@ -247,6 +252,14 @@ def kvc_compress_layer(desc, q_win, k, v, budgets, idx_out, k_out, v_out, pos_ou
                                 _dev_ptr(idx_out, "idx_out", 4), _bf16_ptr(k_out, "k_out"),
                                 _bf16_ptr(v_out, "v_out"), _dev_ptr(pos_out, "pos_out", 4),
                                 _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+
+
+def kvc_overlap_coefficient(desc, idx_a, idx_b, budgets, out):
+    """Per-KV-head overlap coefficient of two packed retained index sets."""
+    L = _load()
+    b = _host_i32(budgets, desc.hkv, "budgets")
+    _check(L.kvc_overlap_coefficient(ctypes.byref(desc), _dev_ptr(idx_a, "idx_a", 4), _dev_ptr(idx_b, "idx_b", 4),
+                                     b.ctypes.data_as(ctypes.c_void_p), _dev_ptr(out, "out", 4), _stream()))
 
 
 def _ptr_array(ptrs):

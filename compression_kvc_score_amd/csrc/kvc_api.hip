@@ -93,6 +93,10 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   if (d->n_sink < 0 || d->n_recent < 0) return fail(KVC_ERR_INVALID_ARG, "n_sink/n_recent must be >= 0");
   if (d->pool < 1 || d->pool % 2 == 0) return fail(KVC_ERR_INVALID_ARG, "pool=%d must be odd and >= 1", d->pool);
   if (d->pool > KVC_MAX_POOL) return fail(KVC_ERR_UNSUPPORTED, "pool=%d > %d", d->pool, KVC_MAX_POOL);
+  if (d->score_mode < KVC_SCORE_SOFTMAX || d->score_mode > KVC_SCORE_LOGIT_INT8)
+    return fail(KVC_ERR_INVALID_ARG, "score_mode=%d is not a kvc_score_mode", d->score_mode);
+  if (d->score_mode != KVC_SCORE_SOFTMAX && d->s > kMaxPrompt / 2)
+    return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^22 with signed (raw inner-product) scores", (long long)d->s);
   if (d->pos_offset < 0 || d->pos_offset + d->s > kInt32Max)
     return fail(KVC_ERR_INVALID_ARG, "pos_offset=%lld: positions must fit in int32", (long long)d->pos_offset);
 
@@ -117,6 +121,7 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   L.n_recent = d->n_recent;
   L.pool = d->pool;
   L.pos_offset = d->pos_offset;
+  L.score_mode = d->score_mode;
   L.q_tok = d->q_tok_stride ? d->q_tok_stride : (int64_t)d->hq * d->d;
   L.q_head = d->q_head_stride ? d->q_head_stride : d->d;
   L.k_tok = d->k_tok_stride ? d->k_tok_stride : (int64_t)d->hkv * d->d;
@@ -317,6 +322,7 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
   a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
   a.slots = reinterpret_cast<uint32_t*>(wsb + lay.slots);
   a.heads = ht;
+  a.signed_keys = L.score_mode != KVC_SCORE_SOFTMAX;
   if (k != nullptr) {
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -332,6 +338,33 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
   }
   const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
+  return KVC_OK;
+}
+
+// Raw inner-product scores (the non-softmax score modes) into `scores`; with
+// hist (cleared beforehand) also the selection histogram.
+int run_logit(const Layer& L, const void* q, const void* k, float* scores, uint32_t* hist, hipStream_t st) {
+  LogitArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.q_tok = L.q_tok;
+  a.q_head = L.q_head;
+  a.k_tok = L.k_tok;
+  a.k_head = L.k_head;
+  a.s = (int)L.s;
+  a.w = L.w;
+  a.g = L.g;
+  a.hkv = L.hkv;
+  const int64_t prefix = L.s - L.w + 1;  // keys seen by every window row
+  a.n_split = (int)std::max<int64_t>(1, std::min<int64_t>(stream_wg_target() / L.hkv, (prefix + 255) / 256));
+  a.keys_per_wg = (int)((prefix + a.n_split - 1) / a.n_split);
+  a.scores = scores;
+  a.hist = hist;
+  const int64_t sink_end = std::min<int64_t>(L.n_sink, L.s);
+  a.sink_end = (int)sink_end;
+  a.rec_begin = (int)std::max<int64_t>(L.s - L.n_recent, sink_end);
+  const hipError_t e = launch_logit_scan(L, a, L.score_mode == KVC_SCORE_LOGIT_INT8, st);
+  if (e != hipSuccess) return hip_fail(e, "raw inner-product scan launch");
   return KVC_OK;
 }
 
@@ -381,8 +414,20 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
   float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
   float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
   float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
-  // pass 2 builds the selection histogram unless ranking uses pooled values
+  // the last scan builds the selection histogram unless ranking uses pooled values
   const bool hist_in_pass2 = L.pool == 1;
+  if (L.score_mode != KVC_SCORE_SOFTMAX) {
+    uint32_t* hist = nullptr;
+    if (hist_in_pass2) {
+      SelectArgs sa{};
+      sa.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+      const hipError_t e = launch_hist_clear(L, sa, st);
+      if (e != hipSuccess) return hip_fail(e, "histogram clear launch");
+      hist = sa.hist;
+    }
+    KVC_TRY(run_logit(L, q_win, k, sc, hist, st));
+    return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out);
+  }
   KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
   KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
   // the compaction of the selection copies the retained rows as it goes
@@ -503,6 +548,8 @@ int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k
   KVC_TRY(check_ptr(m_out, 4, "m_out"));
   KVC_TRY(check_ptr(z_out, 4, "z_out"));
   KVC_TRY(check_ws(L, ws, ws_bytes));
+  if (L.score_mode != KVC_SCORE_SOFTMAX)
+    return fail(KVC_ERR_UNSUPPORTED, "score_mode=%d has no softmax normalisers (pass 1)", L.score_mode);
   KVC_TRY(check_lds(L));
   return run_pass1(L, q_win, k, m_out, z_out, ws, false, static_cast<hipStream_t>(stream));
 }
@@ -513,9 +560,11 @@ int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k
   KVC_TRY(normalize(desc, L));
   KVC_TRY(check_ptr(q_win, 16, "q_win"));
   KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(scores, 4, "scores"));
+  if (L.score_mode != KVC_SCORE_SOFTMAX)
+    return run_logit(L, q_win, k, scores, nullptr, static_cast<hipStream_t>(stream));
   KVC_TRY(check_ptr(m, 4, "m"));
   KVC_TRY(check_ptr(z, 4, "z"));
-  KVC_TRY(check_ptr(scores, 4, "scores"));
   KVC_TRY(check_lds(L));
   return run_pass2(L, q_win, k, m, z, scores, nullptr, static_cast<hipStream_t>(stream));
 }
@@ -565,6 +614,25 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
   KVC_TRY(check_lds(L));
   return enqueue_layer(L, q_win, k, v, ht, m_out, z_out, scores_out, idx_out, k_out, v_out, pos_out, ws,
                        static_cast<hipStream_t>(stream));
+}
+
+int kvc_overlap_coefficient(const kvc_layer_desc* desc, const int32_t* idx_a, const int32_t* idx_b,
+                            const int32_t* budgets, float* out, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(idx_a, 4, "idx_a"));
+  KVC_TRY(check_ptr(idx_b, 4, "idx_b"));
+  KVC_TRY(check_ptr(out, 4, "out"));
+  HeadTable ht;
+  KVC_TRY(head_table(L, budgets, ht));
+  OverlapArgs a{};
+  a.idx_a = idx_a;
+  a.idx_b = idx_b;
+  a.out = out;
+  a.heads = ht;
+  const hipError_t e = launch_overlap(a, L.hkv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "overlap launch");
+  return KVC_OK;
 }
 
 int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void* const* q_win,

@@ -39,6 +39,7 @@ struct Layer {
   int blocks_per_wg;  // consecutive key blocks (stages) scanned by one workgroup
   int n_split;        // workgroups per KV head (per head group when streaming)
   int stream_hg;      // 0: per-head scans; 1 or 2: streaming scans with this many heads per workgroup
+  int score_mode;     // KVC_SCORE_*
 };
 
 // Arguments of the two scans and the split combine (passed by value).
@@ -61,6 +62,19 @@ struct ScoreArgs {
   int sink_end, rec_begin;  // candidate keys [sink_end, rec_begin) for the histogram
 };
 
+// Arguments of the raw inner-product scan (score modes other than softmax).
+struct LogitArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_tok, q_head, k_tok, k_head;
+  int s, w, g, hkv;
+  int n_split;      // prefix-key workgroups per KV head (plus one for the window keys)
+  int keys_per_wg;  // prefix keys per workgroup
+  float* scores;    // [hkv][s]
+  uint32_t* hist;   // [hkv][kHistBins] signed-key bins (null: skip)
+  int sink_end, rec_begin;
+};
+
 struct HeadTable {
   int32_t budget[KVC_MAX_KV_HEADS];
   int64_t offset[KVC_MAX_KV_HEADS + 1];  // packed row offsets of the retained outputs
@@ -81,6 +95,7 @@ struct SelectArgs {
                          // above the threshold bin b* of each sub-chunk, b*, and the list of
                          // those inside b* (sub-chunk << 19 | low 19 pattern bits, key order)
   HeadTable heads;
+  bool signed_keys;      // scores may be negative (raw inner-product modes)
   // retained rows copied by the compaction (k == nullptr: indices only)
   const uint16_t* k;
   const uint16_t* v;
@@ -118,8 +133,21 @@ hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
 // otherwise pass 2 has built it. a.k != nullptr: the compaction also copies
 // the retained K/V rows and positions.
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st);
+// Clear the selection histograms (before a scan that fills them).
+hipError_t launch_hist_clear(const Layer& L, const SelectArgs& a, hipStream_t st);
 size_t select_lds_bytes(int n_chunks, int n_subs);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+struct OverlapArgs {
+  const int32_t* idx_a;
+  const int32_t* idx_b;
+  float* out;
+  HeadTable heads;
+};
+hipError_t launch_overlap(const OverlapArgs& a, int hkv, hipStream_t st);
+
+// Raw inner-product scores (int8: their INT8 form) of all keys; with a.hist
+// also the signed-key histogram of the candidates (cleared beforehand).
+hipError_t launch_logit_scan(const Layer& L, const LogitArgs& a, bool int8, hipStream_t st);
 
 // Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;
 // larger blocks give each wavefront block / 256 tiles per block.

@@ -1,0 +1,50 @@
+// Overlap coefficient of two retained index sets (HeteroCache summary, Key
+// Contributions item 1): per KV head, |A & B| / min(|A|, |B|). Both sets of a
+// head are ascending and of the same size; each thread looks its entries of
+// A up in B by binary search, and one workgroup per head sums the hits.
+
+#include "kvc_internal.h"
+#include "wave_ops.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kOThreads = 256;
+
+__global__ void __launch_bounds__(kOThreads) overlap_kernel(OverlapArgs a) {
+  __shared__ uint32_t part[kOThreads / kWave];
+  const int head = blockIdx.x;
+  const int64_t o = a.heads.offset[head];
+  const int64_t n = a.heads.offset[head + 1] - o;
+  const int32_t* A = a.idx_a + o;
+  const int32_t* B = a.idx_b + o;
+  uint32_t hits = 0;
+  for (int64_t i = threadIdx.x; i < n; i += kOThreads) {
+    const int32_t x = A[i];
+    int64_t lo = 0, hi = n;  // first position with B[pos] >= x
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (B[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    hits += lo < n && B[lo] == x;
+  }
+  const uint32_t tot = wave_total(wave_inclusive_sum(hits));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = tot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kOThreads / kWave; ++w) t += part[w];
+    a.out[head] = n > 0 ? __fdiv_rn((float)t, (float)n) : 1.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_overlap(const OverlapArgs& a, int hkv, hipStream_t st) {
+  OverlapArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&overlap_kernel), dim3((unsigned)hkv), dim3(kOThreads), kargs,
+                         0, st);
+}
+
+}  // namespace kvc

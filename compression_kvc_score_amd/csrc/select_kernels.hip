@@ -44,7 +44,29 @@ constexpr int kCopyUnroll = 8;                    // rows in flight per thread i
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t bin_of(uint32_t bits) { return (bits >> 19) & (kHistBins - 1); }
+// Ranking keys: uint32 patterns ordered like the values. Softmax scores are
+// >= +0, so their IEEE-754 patterns already are; signed scores (the raw
+// inner-product modes) map negatives to their complement and set the sign
+// bit of the others (-0 is taken as +0). The histogram bin is the 12 bits
+// above the LOW pattern bits that the radix rounds resolve (10 bits, then
+// LOW - 10); listed candidates keep a sub-chunk tag in the bits above LOW.
+template <bool SIGNED>
+struct KeyFmt {
+  static constexpr int LOW = SIGNED ? 20 : 19;
+  static constexpr uint32_t LOW_MASK = (1u << LOW) - 1u;
+  static constexpr int R2 = LOW - 10;
+  static constexpr uint32_t R2_BINS = 1u << R2;
+  __device__ static __forceinline__ uint32_t key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if constexpr (SIGNED) {
+      if (u == 0x80000000u) u = 0u;
+      return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    } else {
+      return u;
+    }
+  }
+  __device__ static __forceinline__ uint32_t bin(uint32_t key) { return (key >> LOW) & (kHistBins - 1); }
+};
 
 // Exclusive prefix sum over a workgroup of NW wavefronts, one value per
 // thread; also returns the total. Uses `scratch` (NW entries) in LDS.
@@ -190,7 +212,9 @@ __global__ void __launch_bounds__(256) init_kernel(SelectArgs a, int hkv) {
 // hist: per-chunk LDS histogram of candidate ranking values, merged into the
 // head's global histogram; writes pooled values when pooling.
 // ---------------------------------------------------------------------------
+template <bool SIGNED>
 __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
+  using KF = KeyFmt<SIGNED>;
   __shared__ uint32_t lh[kHistBins];
   const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
   const HeadGeom h = head_geom(a, head);
@@ -206,7 +230,7 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
     if (j >= h.s) break;
     const float v = a.pool_radius > 0 ? rank_value(row, h.s, j, a.pool_radius) : row[j];
     if (prow) prow[j] = v;
-    if (is_candidate(h, j)) atomicAdd(&lh[bin_of(__float_as_uint(v))], 1u);
+    if (is_candidate(h, j)) atomicAdd(&lh[KF::bin(KF::key(v))], 1u);
   }
   __syncthreads();
   uint32_t* gh = a.hist + (int64_t)head * kHistBins;
@@ -219,7 +243,9 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(SelectArgs a) {
 // it, and list, in key order, the patterns of those inside b* (in the chunk's
 // own slot: no atomics).
 // ---------------------------------------------------------------------------
+template <bool SIGNED>
 __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
+  using KF = KeyFmt<SIGNED>;
   __shared__ uint32_t scratch[kWaves];
   __shared__ uint32_t w_in[kWaves], w_above[kWaves];
   __shared__ uint32_t s_b, s_hit;
@@ -235,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t j = j0 + e;
-    bits[e] = (j < h.s && is_candidate(h, j)) ? __float_as_uint(vals[j]) : 0u;
+    bits[e] = (j < h.s && is_candidate(h, j)) ? KF::key(vals[j]) : 0u;
   }
   // b*: the bin holding the k-th best candidate (thread t owns bins
   // 4095-4t .. 4092-4t, descending)
@@ -265,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
     const int64_t j = j0 + e;
     in[e] = false;
     if (j < h.s && is_candidate(h, j)) {
-      const uint32_t b = bin_of(bits[e]);
+      const uint32_t b = KF::bin(bits[e]);
       above += b > bstar;
       in[e] = b == bstar;
       nin += in[e];
@@ -280,14 +306,14 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   uint32_t pos = inc_in - nin;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) pos += w < wave ? w_in[w] : 0u;
-  // listed entries carry their sub-chunk: the patterns inside b* share bits
-  // 31..19, so the low 19 bits identify them
+  // listed entries carry their sub-chunk: the keys inside b* share the bits
+  // above LOW, so the low LOW bits identify them
   uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotStride;
-  const uint32_t tag = (uint32_t)(chunk * kSubsPerChunk + (int)threadIdx.x / (kSub / 4)) << 19;
+  const uint32_t tag = (uint32_t)(chunk * kSubsPerChunk + (int)threadIdx.x / (kSub / 4)) << KF::LOW;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (in[e]) {
-      if (pos < (uint32_t)kSlotCap) slot[kSlotHdr + pos] = tag | (bits[e] & 0x7FFFFu);
+      if (pos < (uint32_t)kSlotCap) slot[kSlotHdr + pos] = tag | (bits[e] & KF::LOW_MASK);
       ++pos;
     }
   }
@@ -325,10 +351,11 @@ enum ResolveOutcome { kResolved = 0, kNeedLists = 1, kNeedRow = 2 };
 // (wavefront w holds chunks 16g + 4w + i, word 64r + lane) and the radix
 // histograms are built from them directly. Returns kNeedLists if a list is
 // longer (nothing done yet) and kNeedRow if a slot overflowed.
-template <int NG, typename OnBstar>
+template <bool SIGNED, int NG, typename OnBstar>
 __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int head, int sub,
                                     const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
                                     uint32_t& gt_before, uint32_t& eq_before, OnBstar on_bstar) {
+  using KF = KeyFmt<SIGNED>;
   constexpr int NW = kCWaves;
   constexpr int GC = NW * kGroupChunks;  // chunks per group
   const int nc = a.n_chunks;
@@ -375,7 +402,8 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
   const uint32_t bstar = sums[3];
   on_bstar(bstar);
 
-  // radix over pattern bits 18..9, then 8..0 (the listed patterns share the rest)
+  // radix over the LOW key bits: the top 10, then the other R2 (the listed
+  // keys share the bits above LOW)
   uint32_t rem = h.k_sel - sums[0];  // rank of the threshold inside the lists
 #pragma unroll
   for (int g = 0; g < NG; ++g)
@@ -384,7 +412,7 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
 #pragma unroll
       for (int r = 0; r < kSpecRounds; ++r) {
         const int e = r * kWave + lane - kSlotHdr;
-        if (e >= 0 && (uint32_t)e < n[g][i]) atomicAdd(&m.hist1[(v[g][i][r] >> 9) & 1023u], 1u);
+        if (e >= 0 && (uint32_t)e < n[g][i]) atomicAdd(&m.hist1[(v[g][i][r] >> KF::R2) & 1023u], 1u);
       }
   __syncthreads();
   if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
@@ -398,15 +426,15 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
 #pragma unroll
       for (int r = 0; r < kSpecRounds; ++r) {
         const int e = r * kWave + lane - kSlotHdr;
-        if (e >= 0 && (uint32_t)e < n[g][i] && ((v[g][i][r] >> 9) & 1023u) == d1)
-          atomicAdd(&m.hist2[v[g][i][r] & 511u], 1u);
+        if (e >= 0 && (uint32_t)e < n[g][i] && ((v[g][i][r] >> KF::R2) & 1023u) == d1)
+          atomicAdd(&m.hist2[v[g][i][r] & (KF::R2_BINS - 1u)], 1u);
       }
   __syncthreads();
-  if (threadIdx.x < kWave) pick_digit_wave<512>(m.hist2, rem, m.pick);
+  if (threadIdx.x < kWave) pick_digit_wave<KF::R2_BINS>(m.hist2, rem, m.pick);
   __syncthreads();
-  const uint32_t low = (d1 << 9) | m.pick[0];
+  const uint32_t low = (d1 << KF::R2) | m.pick[0];
   need_eq = m.pick[1];
-  thr = (bstar << 19) | low;
+  thr = (bstar << KF::LOW) | low;
   // listed candidates of the sub-chunks before this one
   uint32_t gq[2] = {0u, 0u};
 #pragma unroll
@@ -417,9 +445,9 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
       for (int r = 0; r < kSpecRounds; ++r) {
         const int e = r * kWave + lane - kSlotHdr;
         const uint32_t x = v[g][i][r];
-        if (e >= 0 && (uint32_t)e < n[g][i] && (int)(x >> 19) < sub) {
-          gq[0] += (x & 0x7FFFFu) > low;
-          gq[1] += (x & 0x7FFFFu) == low;
+        if (e >= 0 && (uint32_t)e < n[g][i] && (int)(x >> KF::LOW) < sub) {
+          gq[0] += (x & KF::LOW_MASK) > low;
+          gq[1] += (x & KF::LOW_MASK) == low;
         }
       }
   block_sums<NW, 2>(gq, m.scratch);
@@ -435,10 +463,11 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
 // list; once b* is known, on_bstar(b*) runs (before the radix rounds).
 // Returns false (nothing resolved) if a chunk's slot or the gathered list
 // overflowed.
-template <typename OnBstar>
+template <bool SIGNED, typename OnBstar>
 __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int head, int sub,
                                    const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
                                    uint32_t& gt_before, uint32_t& eq_before, OnBstar on_bstar) {
+  using KF = KeyFmt<SIGNED>;
   constexpr int NW = kCWaves;
   __shared__ uint32_t s_count, s_flag, s_bstar;
   const int nc = a.n_chunks;
@@ -510,7 +539,7 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
   const uint32_t n_total = s_count;
   uint32_t rem = h.k_sel - ab_all;  // rank of the threshold inside the list
   for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads)
-    atomicAdd(&m.hist1[(m.cbits[i] >> 9) & 1023u], 1u);
+    atomicAdd(&m.hist1[(m.cbits[i] >> KF::R2) & 1023u], 1u);
   __syncthreads();
   if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
   __syncthreads();
@@ -518,21 +547,21 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
   rem = m.pick[1];
   for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads) {
     const uint32_t e = m.cbits[i];
-    if (((e >> 9) & 1023u) == d1) atomicAdd(&m.hist2[e & 511u], 1u);
+    if (((e >> KF::R2) & 1023u) == d1) atomicAdd(&m.hist2[e & (KF::R2_BINS - 1u)], 1u);
   }
   __syncthreads();
-  if (threadIdx.x < kWave) pick_digit_wave<512>(m.hist2, rem, m.pick);
+  if (threadIdx.x < kWave) pick_digit_wave<KF::R2_BINS>(m.hist2, rem, m.pick);
   __syncthreads();
-  const uint32_t low = (d1 << 9) | m.pick[0];
+  const uint32_t low = (d1 << KF::R2) | m.pick[0];
   need_eq = m.pick[1];
-  thr = (s_bstar << 19) | low;
+  thr = (s_bstar << KF::LOW) | low;
   // listed candidates of the sub-chunks before this one
   uint32_t g = 0, q = 0;
   for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads) {
     const uint32_t e = m.cbits[i];
-    if ((int)(e >> 19) < sub) {
-      g += (e & 0x7FFFFu) > low;
-      q += (e & 0x7FFFFu) == low;
+    if ((int)(e >> KF::LOW) < sub) {
+      g += (e & KF::LOW_MASK) > low;
+      q += (e & KF::LOW_MASK) == low;
     }
   }
   block_sum2<NW>(g, q, m.scratch);
@@ -543,17 +572,19 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
 
 // Slow path: the same quantities by radix passes over the head's whole
 // score row (8 bits per round from the top).
+template <bool SIGNED>
 __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int head, int sub,
                                  const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
                                  uint32_t& gt_before, uint32_t& eq_before) {
+  using KF = KeyFmt<SIGNED>;
   constexpr int NT = kCompactThreads, NW = kCWaves;
-  const uint32_t* bits = reinterpret_cast<const uint32_t*>(a.vals + (int64_t)head * h.s);
+  const float* row = a.vals + (int64_t)head * h.s;
   uint32_t prefix = 0u, mask = 0u, rem = h.k_sel;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += NT) m.hist1[i] = 0u;
     __syncthreads();
     for (int64_t j = h.sink_end + threadIdx.x; j < h.rec_begin; j += NT) {
-      const uint32_t u = bits[j];
+      const uint32_t u = KF::key(row[j]);
       if ((u & mask) == prefix) atomicAdd(&m.hist1[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -570,7 +601,7 @@ __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int hea
   const int64_t lim = s0 < h.rec_begin ? s0 : h.rec_begin;
   uint32_t g = 0, q = 0;
   for (int64_t j = h.sink_end + threadIdx.x; j < lim; j += NT) {
-    const uint32_t u = bits[j];
+    const uint32_t u = KF::key(row[j]);
     g += u > thr;
     q += u == thr;
   }
@@ -584,10 +615,11 @@ __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int hea
 // indices (and positions) in ascending order from the sub-chunk's first
 // output row; with GATHER also copy their K and V rows.
 // ---------------------------------------------------------------------------
-template <bool GATHER>
+template <bool GATHER, bool SIGNED>
 __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) {
+  using KF = KeyFmt<SIGNED>;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ uint32_t hist1[1024], hist2[512];
+  __shared__ uint32_t hist1[1024], hist2[1024];
   __shared__ uint32_t scratch[4 * kCWaves], pick[2];
   __shared__ int32_t kept_keys[GATHER ? kSub : 1];
   const int head = blockIdx.x / a.n_subs, sub = blockIdx.x % a.n_subs;
@@ -604,10 +636,10 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t j = j0 + e;
-      if (j < h.s && is_candidate(h, j)) vb[e] = __float_as_uint(vals[j]);
+      if (j < h.s && is_candidate(h, j)) vb[e] = KF::key(vals[j]);
     }
     for (int i = threadIdx.x; i < 1024; i += kCompactThreads) hist1[i] = 0u;
-    for (int i = threadIdx.x; i < 512; i += kCompactThreads) hist2[i] = 0u;
+    for (int i = threadIdx.x; i < 1024; i += kCompactThreads) hist2[i] = 0u;
     ResolveLds m;
     m.cbits = reinterpret_cast<uint32_t*>(smem);
     m.hist1 = hist1;
@@ -625,7 +657,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t j = j0 + e;
-          want[e] = j < h.s && (!is_candidate(h, j) || bin_of(vb[e]) >= bstar);
+          want[e] = j < h.s && (!is_candidate(h, j) || KF::bin(vb[e]) >= bstar);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -649,13 +681,14 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     constexpr int GC = kCWaves * kGroupChunks;
     int outcome = kNeedLists;
     if (a.n_chunks <= GC)
-      outcome = resolve_in_registers<1>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+      outcome = resolve_in_registers<SIGNED, 1>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
     else if (a.n_chunks <= 2 * GC)
-      outcome = resolve_in_registers<2>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+      outcome = resolve_in_registers<SIGNED, 2>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
     if (outcome == kNeedLists)
-      outcome = resolve_from_lists(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch) ? kResolved
-                                                                                                   : kNeedRow;
-    if (outcome == kNeedRow) resolve_from_row(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
+      outcome = resolve_from_lists<SIGNED>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch)
+                    ? kResolved
+                    : kNeedRow;
+    if (outcome == kNeedRow) resolve_from_row<SIGNED>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before);
     quota = need_eq > eq_before ? need_eq - eq_before : 0u;  // equal candidates this sub-chunk may take
     first = mandatory_in(h, 0, s0) + gt_before + (need_eq < eq_before ? need_eq : eq_before);
   } else {
@@ -753,7 +786,8 @@ size_t select_lds_bytes(int n_chunks, int n_subs) {
   return (size_t)kCandCap * 4;
 }
 
-hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
+template <bool SIGNED>
+hipError_t launch_select_keys(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
   SelectArgs args = a;
   void* kargs[] = {&args};
   const dim3 chunks((unsigned)(L.hkv * a.n_chunks));
@@ -764,17 +798,29 @@ hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hi
     e = hipLaunchKernel(reinterpret_cast<const void*>(&init_kernel),
                         dim3((unsigned)((L.hkv * kHistBins + 255) / 256)), dim3(256), iargs, 0, st);
     if (e != hipSuccess) return e;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&hist_kernel), chunks, dim3(kThreads), kargs, 0, st);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&hist_kernel<SIGNED>), chunks, dim3(kThreads), kargs, 0, st);
     if (e != hipSuccess) return e;
   }
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&filter_kernel), chunks, dim3(kThreads), kargs, 0, st);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&filter_kernel<SIGNED>), chunks, dim3(kThreads), kargs, 0, st);
   if (e != hipSuccess) return e;
   const size_t lds = select_lds_bytes(a.n_chunks, a.n_subs);
-  const void* compact = a.k != nullptr ? reinterpret_cast<const void*>(&compact_kernel<true>)
-                                       : reinterpret_cast<const void*>(&compact_kernel<false>);
+  const void* compact = a.k != nullptr ? reinterpret_cast<const void*>(&compact_kernel<true, SIGNED>)
+                                       : reinterpret_cast<const void*>(&compact_kernel<false, SIGNED>);
   e = ensure_lds(compact, lds);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(compact, dim3((unsigned)(L.hkv * a.n_subs)), dim3(kCompactThreads), kargs, lds, st);
+}
+
+hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {
+  return a.signed_keys ? launch_select_keys<true>(L, a, need_hist, st) : launch_select_keys<false>(L, a, need_hist, st);
+}
+
+hipError_t launch_hist_clear(const Layer& L, const SelectArgs& a, hipStream_t st) {
+  SelectArgs args = a;
+  int hkv = L.hkv;
+  void* iargs[] = {&args, &hkv};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&init_kernel),
+                         dim3((unsigned)((L.hkv * kHistBins + 255) / 256)), dim3(256), iargs, 0, st);
 }
 
 }  // namespace kvc

@@ -69,12 +69,29 @@ typedef enum kvc_status {
   KVC_ERR_HIP = -5           /* the HIP runtime reported an error (message in kvc_last_error) */
 } kvc_status;
 
+/* How keys are scored (kvc_layer_desc.score_mode). */
+typedef enum kvc_score_mode {
+  /* softmax weights exp(l - m) / Z summed over the window rows (TideKV,
+     Fig. 3 caption): two K passes, pass 1 for the normalisers */
+  KVC_SCORE_SOFTMAX = 0,
+  /* raw inner products <q, k> summed over the rows that see the key, no
+     scale, no softmax (HillInfer, Algorithmic Simplification): one K pass;
+     scores may be negative */
+  KVC_SCORE_LOGIT = 1,
+  /* as KVC_SCORE_LOGIT with the pooled query and every key row quantised to
+     symmetric per-vector INT8 on the fly and an exact integer dot product
+     (HillInfer, Streaming Execution and Asymmetric Precision); the gather
+     still copies the original bf16 rows */
+  KVC_SCORE_LOGIT_INT8 = 2
+} kvc_score_mode;
+
 /* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
 typedef void* kvc_stream_t;
 
 /*
  * Shape and options of one layer's compression.
  *  s            prompt length = number of keys scored, 1 <= s <= 2^23
+ *               (2^22 in the raw inner-product score modes)
  *  w            observation window: the last w prompt queries, 1 <= w <= s
  *  hq, hkv      query and KV heads, hq % hkv == 0, 1 <= hkv <= KVC_MAX_KV_HEADS,
  *               (hq / hkv) * w <= KVC_MAX_ROWS
@@ -88,6 +105,15 @@ typedef void* kvc_stream_t;
  *               <= KVC_MAX_POOL; the window is truncated at both ends
  *  pos_offset   added to retained key indices to form positions;
  *               0 <= pos_offset and pos_offset + s <= 2^31 - 1
+ *  score_mode   a kvc_score_mode; 0 (the default layout of this field) is
+ *               the softmax score. In the raw inner-product modes
+ *               kvc_score_pass1 is not available (no normalisers exist),
+ *               kvc_score_pass2 writes those scores (m and z are ignored and
+ *               may be NULL), kvc_select_topk ranks signed scores, and the
+ *               whole-layer calls leave m_out and z_out unwritten. For
+ *               KVC_SCORE_LOGIT_INT8 the pooled query is the exact sum of the
+ *               bf16 window queries rounded once to fp32 (exact when their
+ *               magnitudes span less than 2^45). `scale` is not used.
  *  *_tok_stride, *_head_stride
  *               element strides between tokens and between heads of Q_win, K
  *               and V; 0 selects the default dense layout; non-zero strides
@@ -104,7 +130,7 @@ typedef struct kvc_layer_desc {
   int32_t n_sink;
   int32_t n_recent;
   int32_t pool;
-  int32_t reserved0;
+  int32_t score_mode;
   int64_t pos_offset;
   int64_t q_tok_stride, q_head_stride;
   int64_t k_tok_stride, k_head_stride;
@@ -210,6 +236,18 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
                        float* m_out, float* z_out, float* scores_out, int32_t* idx_out,
                        void* k_out, void* v_out, int32_t* pos_out,
                        void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * Overlap coefficient between two retained index sets of one layer shape
+ * (HeteroCache summary, Key Contributions item 1, the measure of how much
+ * two heads' or two scorers' retained keys agree): per KV head g,
+ * out[g] = |A_g & B_g| / min(|A_g|, |B_g|), and 1 when the head retains no
+ * key. idx_a, idx_b: device int32 packed as kvc_select_topk writes them for
+ * the same HOST budgets [hkv] (so |A_g| = |B_g|), each head's indices
+ * ascending. out: device fp32 [hkv]. Needs no workspace.
+ */
+int kvc_overlap_coefficient(const kvc_layer_desc* desc, const int32_t* idx_a, const int32_t* idx_b,
+                            const int32_t* budgets, float* out, kvc_stream_t stream);
 
 /*
  * A layer-major sweep (TideKV, Fig. 2 caption: layers are compressed one

@@ -218,3 +218,34 @@ def test_budgets_ties_and_errors():
         kvc.kvc_budgets_inverse_stability([0.5, 0.0], 10)
     with pytest.raises(kvc.KvcError):
         kvc.kvc_budgets_inverse_stability([0.5, float("inf")], 10)
+
+
+def test_score_mode_arguments_are_checked_before_launch():
+    lib = kvc.lib()
+    P = _fake(0x10000)
+    b = np.full(8, 4096, dtype=np.int32)
+    bp = b.ctypes.data_as(ctypes.c_void_p)
+    d = base_desc(score_mode=3)
+    assert lib.kvc_score_pass2(ctypes.byref(d), P, P, P, P, P, None) == kvc.KVC_ERR_INVALID_ARG
+    assert "score_mode" in lib.kvc_last_error().decode()
+    d = base_desc(score_mode=-1)
+    assert kvc.lib().kvc_workspace_size(ctypes.byref(d)) == 0
+    big = base_desc(s=(1 << 22) + 1, score_mode=kvc.KVC_SCORE_LOGIT)
+    assert lib.kvc_score_pass2(ctypes.byref(big), P, P, None, None, P, None) == kvc.KVC_ERR_UNSUPPORTED
+    ok_big = base_desc(s=(1 << 22) + 1)  # the softmax mode allows up to 2^23
+    assert kvc.kvc_workspace_size(ok_big) > 0
+    for mode in (kvc.KVC_SCORE_LOGIT, kvc.KVC_SCORE_LOGIT_INT8):
+        d = base_desc(score_mode=mode)
+        ws_n = kvc.kvc_workspace_size(d)
+        # pass 1 has nothing to compute without softmax normalisers
+        assert lib.kvc_score_pass1(ctypes.byref(d), P, P, P, P, P, ws_n, None) == kvc.KVC_ERR_UNSUPPORTED
+        # pass 2 still checks its pointers (m and z are not needed)
+        assert lib.kvc_score_pass2(ctypes.byref(d), P, P, None, None, None, None) == kvc.KVC_ERR_INVALID_ARG
+        assert lib.kvc_score_pass2(ctypes.byref(d), _fake(0x10008), P, None, None, P, None) == kvc.KVC_ERR_ALIGN
+    d = base_desc()
+    dd = ctypes.byref(d)
+    assert lib.kvc_overlap_coefficient(dd, None, P, bp, P, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_overlap_coefficient(dd, P, _fake(0x10002), bp, P, None) == kvc.KVC_ERR_ALIGN
+    assert lib.kvc_overlap_coefficient(dd, P, P, None, P, None) == kvc.KVC_ERR_INVALID_ARG
+    bad = np.full(8, 10, dtype=np.int32)
+    assert lib.kvc_overlap_coefficient(dd, P, P, bad.ctypes.data_as(ctypes.c_void_p), P, None) == kvc.KVC_ERR_INVALID_ARG
