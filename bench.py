@@ -286,6 +286,46 @@ def main(argv=None):
     log("staged breakdown (back-to-back batches): " + ", ".join(f"{n} {stage_ms[n] * 1e3:.1f} us" for n in stage_names)
         + f" (sum {staged_ms * 1e3:.1f} us)")
 
+    # ---- the raw inner-product score modes on the same layers: the warm
+    # whole-layer loop, their one-pass scan (K back-to-back kvc_score_pass2
+    # calls) against the HBM peak, and how much their retained sets overlap
+    # the softmax ones (per-head overlap coefficient, layer 0)
+    mode_detail = {}
+    for mode_name, mode in (("logit", kvc.KVC_SCORE_LOGIT), ("int8", kvc.KVC_SCORE_LOGIT_INT8)):
+        mdesc = kvc.desc_for(q0, k0, v0, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                             pool=cfg.pool, score_mode=mode)
+        mprep = [kvc.PreparedLayer(mdesc, q, k, v, budgets, kvc.alloc_outputs(mdesc, budgets, dev), ws)
+                 for (q, k, v, budgets) in layers]
+        for i in range(args.warmup):
+            mprep[i % n_layers].kvc_compress_layer(sp)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            mprep[i % n_layers].kvc_compress_layer(sp)
+        torch.cuda.synchronize()
+        mwall = time.perf_counter() - t0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            mprep[i % n_layers].kvc_score_pass2(sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        scan_ms = e0.elapsed_time(e1) / K
+        scan_bytes = cfg.s * cfg.hkv * cfg.d * 2 + cfg.w * cfg.hq * cfg.d * 2 + cfg.hkv * cfg.s * 4
+        res = torch.empty(cfg.hkv, dtype=torch.float32, device=dev)
+        kvc.kvc_overlap_coefficient(desc, prepared[0]._keep[3].idx, mprep[0]._keep[3].idx, layers[0][3], res)
+        torch.cuda.synchronize()
+        mode_detail[mode_name] = {
+            "ms_per_step": round(mwall * 1e3 / K, 5), "value": round(cfg.s * K / mwall, 1),
+            "scan_us": round(scan_ms * 1e3, 2),
+            "scan_hbm_frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "overlap_with_softmax_mean": round(float(res.mean().item()), 4),
+        }
+        log(f"score mode {mode_name}: {mwall * 1e3 / K:.4f} ms/layer; scan {scan_ms * 1e3:.1f} us "
+            f"({mode_detail[mode_name]['scan_hbm_frac'] * 100:.1f}% of HBM peak); retained-set overlap with "
+            f"softmax {mode_detail[mode_name]['overlap_with_softmax_mean']:.3f}")
+        del mprep
+
     ms_per_step = wall * 1e3 / K
     value = cfg.s * K / wall
 
@@ -329,6 +369,7 @@ def main(argv=None):
                           "p90": round(float(np.percentile(cold_us, 90)), 2), "layers": n_layers,
                           "note": "512 MiB write before each layer evicts the memory-side cache; "
                                   "HIP events around one kvc_compress_layer call"},
+        "score_modes": mode_detail,
         "sweep": {
             "entry_point": "kvc_compress_layers", "layers_in_flight": kvc.SWEEP_STREAMS,
             "value": round(cfg.s * K / sweep_wall, 1), "unit": "tokens/s",

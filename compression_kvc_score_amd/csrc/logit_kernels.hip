@@ -20,8 +20,8 @@
 //    fixed order. INT8 rows are quantised by the same lanes (the row maximum
 //    by DPP, the codes by round-half-even of x * 127/max) and multiplied with
 //    dot4 instructions, exactly.
-//  - one extra workgroup per KV head scores the window keys j > S-W, one lane
-//    group per key, each summing its own suffix of window rows.
+//  - one more workgroup per window key j = S-W+t (t >= 1) forms the pooled
+//    query of rows t .. W-1 the same way and scores that key.
 //
 // With a histogram buffer the scan also counts the candidates' ranking keys
 // per head (signed-key bins of the selection).
@@ -91,16 +91,23 @@ __device__ __forceinline__ float group_max_all(float x) {
 
 // Symmetric INT8 codes of this lane's 8 values given the vector's max |x|
 // (the rule of the oracle: round-half-even of x * fp32(127 / max)), packed
-// four to a word.
+// four to a word. Adding 1.5 * 2^23 to the separately rounded product (the
+// compiler would otherwise fuse the two into one rounding) leaves
+// exactly that rounded integer in the low mantissa bits (|x * r| <= 127), so
+// its low byte is the two's-complement code; an all-zero vector (r = 0) gives
+// zero codes.
 __device__ __forceinline__ void quantize8(const float (&x)[8], float amax, int (&packed)[2]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   const float r = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint32_t p = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = amax > 0.f ? (int)__builtin_rintf(__fmul_rn(x[4 * h + i], r)) : 0;
-      p |= ((uint32_t)c & 0xFFu) << (8 * i);
+      float prod = x[4 * h + i] * r;
+      asm volatile("" : "+v"(prod));  // keep the product's own rounding: no fused multiply-add
+      const uint32_t c = __float_as_uint(prod + kMagic) & 0xFFu;
+      p |= c << (8 * i);
     }
     packed[h] = (int)p;
   }
@@ -150,10 +157,13 @@ __global__ void __launch_bounds__(kLThreads) logit_scan_kernel(LogitArgs a) {
   __shared__ float s_amax;
   __shared__ uint32_t lh[HIST ? kHistBins : 1];
   const int grp = threadIdx.x / LPR, l = threadIdx.x % LPR;
-  const bool window_wg = (int)blockIdx.x >= a.hkv * a.n_split;
-  const int head = window_wg ? (int)blockIdx.x - a.hkv * a.n_split : (int)blockIdx.x / a.n_split;
-  const int split = window_wg ? 0 : (int)blockIdx.x % a.n_split;
   const int s = a.s, w = a.w, G = a.g;
+  const int nmain = a.hkv * a.n_split;
+  const bool window_wg = (int)blockIdx.x >= nmain;
+  // main: (head, split), rows from 0; window: (head, t), rows from t
+  const int head = window_wg ? ((int)blockIdx.x - nmain) / (w - 1) : (int)blockIdx.x / a.n_split;
+  const int split = window_wg ? 0 : (int)blockIdx.x % a.n_split;
+  const int t_first = window_wg ? 1 + ((int)blockIdx.x - nmain) % (w - 1) : 0;
   const int first_win = s - w + 1;  // keys from here on are seen by fewer than all rows
   float* out = a.scores + (int64_t)head * s;
   const uint16_t* kh = a.k + (int64_t)head * a.k_head + 8 * l;
@@ -162,102 +172,89 @@ __global__ void __launch_bounds__(kLThreads) logit_scan_kernel(LogitArgs a) {
     for (int i = threadIdx.x; i < kHistBins; i += kLThreads) lh[i] = 0u;
   }
 
+  // ---- pooled query of rows t_first .. W-1: lane group grp sums flattened
+  // rows r = t_first*G + grp, + GROUPS, ... (row r = window query r / G of
+  // head head*G + r % G), exactly in fp64
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = t_first * G + grp; r < w * G; r += GROUPS) {
+    const uint4 v = *reinterpret_cast<const uint4*>(a.q + (int64_t)(r / G) * a.q_tok +
+                                                    (int64_t)(head * G + r % G) * a.q_head + 8 * l);
+    float x[8];
+    unpack8(v, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[grp][8 * l + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double t = 0.0;
+    for (int g2 = 0; g2 < GROUPS; ++g2) t += part[g2][threadIdx.x];
+    qbar[threadIdx.x] = (float)t;
+  }
+  __syncthreads();
+  float qf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qf[i] = qbar[8 * l + i];
+  int q8[2] = {0, 0};
+  float step_q = 0.f;
+  if constexpr (I8) {
+    if (threadIdx.x < kWave) {
+      float m = 0.f;
+      for (int i = threadIdx.x; i < D; i += kWave) m = fmaxf(m, fabsf(qbar[i]));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (threadIdx.x == 0) s_amax = m;
+    }
+    __syncthreads();
+    quantize8(qf, s_amax, q8);
+    step_q = step_of(s_amax);
+  }
+
   if (!window_wg) {
-    // ---- prefix keys [kb, ke): one pooled query of all W*G rows
+    // ---- prefix keys [kb, ke), all seen by every window row
     const int kb = split * a.keys_per_wg;
     const int ke = min(kb + a.keys_per_wg, first_win);
-    // pooled query: lane group grp sums rows r = grp, grp + GROUPS, ... (row
-    // r = window query r / G of head head*G + r % G), exactly in fp64
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int r = grp; r < w * G; r += GROUPS) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.q + (int64_t)(r / G) * a.q_tok +
-                                                      (int64_t)(head * G + r % G) * a.q_head + 8 * l);
-      float x[8];
-      unpack8(v, x);
+    // two register buffers of U rows per lane group: the next rows load while
+    // the current ones are scored; loads are clamped into the range (never
+    // conditional), so the compiler can count the ones in flight
+    constexpr int STEP = GROUPS * U;
+    uint4 ka[U], kb2[U];
+    auto load = [&](uint4 (&buf)[U], int base) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part[grp][8 * l + i] = acc[i];
-    __syncthreads();
-    if (threadIdx.x < D) {
-      double t = 0.0;
-      for (int g2 = 0; g2 < GROUPS; ++g2) t += part[g2][threadIdx.x];
-      qbar[threadIdx.x] = (float)t;
-    }
-    __syncthreads();
-    float qf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qf[i] = qbar[8 * l + i];
-    int q8[2] = {0, 0};
-    float step_q = 0.f;
-    if constexpr (I8) {
-      if (threadIdx.x < kWave) {
-        float m = 0.f;
-        for (int i = threadIdx.x; i < D; i += kWave) m = fmaxf(m, fabsf(qbar[i]));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (threadIdx.x == 0) s_amax = m;
+      for (int u = 0; u < U; ++u) {
+        const int key = min(base + u * GROUPS + grp, ke - 1);
+        buf[u] = *reinterpret_cast<const uint4*>(kh + (int64_t)key * a.k_tok);
       }
-      __syncthreads();
-      quantize8(qf, s_amax, q8);
-      step_q = step_of(s_amax);
-    }
-
-    for (int base = kb; base < ke; base += GROUPS * U) {
-      uint4 kr[U];
+    };
+    auto score = [&](const uint4 (&buf)[U], int base) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int key = base + u * GROUPS + grp;
-        kr[u] = key < ke ? *reinterpret_cast<const uint4*>(kh + (int64_t)key * a.k_tok) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int key = base + u * GROUPS + grp;
-        const float sc = row_score<LPR, I8>(kr[u], qf, q8, step_q);
+        const float sc = row_score<LPR, I8>(buf[u], qf, q8, step_q);
         if (l == LPR - 1 && key < ke) {
           out[key] = sc;
           if (HIST && key >= a.sink_end && key < a.rec_begin) atomicAdd(&lh[signed_bin(sc)], 1u);
         }
       }
-    }
-  } else {
-    // ---- window keys j = S-W+t, t = 1 .. W-1: lane group per key, each with
-    // its own pooled query of rows t .. W-1
-    for (int t0 = 1; t0 < w; t0 += GROUPS) {
-      const int t = t0 + grp;
-      if (t < w) {
-        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int i = t; i < w; ++i)
-          for (int hh = 0; hh < G; ++hh) {
-            const uint4 v = *reinterpret_cast<const uint4*>(a.q + (int64_t)i * a.q_tok +
-                                                            (int64_t)(head * G + hh) * a.q_head + 8 * l);
-            float x[8];
-            unpack8(v, x);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] += (double)x[c];
-          }
-        float qf[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qf[c] = (float)acc[c];
-        int q8[2] = {0, 0};
-        float step_q = 0.f;
-        if constexpr (I8) {
-          float am = 0.f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(qf[c]));
-          am = group_max_all<LPR>(am);
-          quantize8(qf, am, q8);
-          step_q = step_of(am);
-        }
-        const int key = s - w + t;
-        const uint4 kraw = *reinterpret_cast<const uint4*>(kh + (int64_t)key * a.k_tok);
-        const float sc = row_score<LPR, I8>(kraw, qf, q8, step_q);
-        if (l == LPR - 1) {
-          out[key] = sc;
-          if (HIST && key >= a.sink_end && key < a.rec_begin) atomicAdd(&lh[signed_bin(sc)], 1u);
-        }
+    };
+    if (kb < ke) load(ka, kb);
+    for (int base = kb; base < ke; base += 2 * STEP) {
+      if (base + STEP < ke) load(kb2, base + STEP);
+      score(ka, base);
+      if (base + STEP < ke) {
+        if (base + 2 * STEP < ke) load(ka, base + 2 * STEP);
+        score(kb2, base + STEP);
       }
+    }
+  } else if (grp == 0) {
+    // ---- the window key j = S-W+t_first, seen by rows t_first .. W-1
+    const int key = s - w + t_first;
+    const uint4 kraw = *reinterpret_cast<const uint4*>(kh + (int64_t)key * a.k_tok);
+    const float sc = row_score<LPR, I8>(kraw, qf, q8, step_q);
+    if (l == LPR - 1) {
+      out[key] = sc;
+      if (HIST && key >= a.sink_end && key < a.rec_begin) atomicAdd(&lh[signed_bin(sc)], 1u);
     }
   }
 
@@ -283,7 +280,7 @@ hipError_t launch_logit_scan(const Layer& L, const LogitArgs& a, bool int8, hipS
   const bool hist = a.hist != nullptr;
   const void* fn = L.d == 128 ? (int8 ? logit_fn<128, true>(hist) : logit_fn<128, false>(hist))
                               : (int8 ? logit_fn<64, true>(hist) : logit_fn<64, false>(hist));
-  const dim3 grid((unsigned)(L.hkv * (a.n_split + 1)));  // + one window workgroup per head
+  const dim3 grid((unsigned)(L.hkv * (a.n_split + L.w - 1)));  // + one workgroup per window key
   return hipLaunchKernel(fn, grid, dim3(kLThreads), kargs, 0, st);
 }
 
