@@ -1,7 +1,8 @@
 // Overlap coefficient of two retained index sets (HeteroCache summary, Key
 // Contributions item 1): per KV head, |A & B| / min(|A|, |B|). Both sets of a
-// head are ascending and of the same size; each thread looks its entries of
-// A up in B by binary search, and one workgroup per head sums the hits.
+// head are ascending and of the same size. One workgroup per head copies B
+// into LDS (when it fits) and each thread looks its entries of A up in it by
+// binary search; the hits are summed over the workgroup.
 
 #include "kvc_internal.h"
 #include "wave_ops.h"
@@ -10,14 +11,21 @@ namespace kvc {
 namespace {
 
 constexpr int kOThreads = 256;
+constexpr int kOCap = 15360;  // entries of B held in LDS (60 KiB)
 
 __global__ void __launch_bounds__(kOThreads) overlap_kernel(OverlapArgs a) {
   __shared__ uint32_t part[kOThreads / kWave];
+  __shared__ int32_t lb[kOCap];
   const int head = blockIdx.x;
   const int64_t o = a.heads.offset[head];
   const int64_t n = a.heads.offset[head + 1] - o;
   const int32_t* A = a.idx_a + o;
   const int32_t* B = a.idx_b + o;
+  if (n <= kOCap) {
+    for (int64_t i = threadIdx.x; i < n; i += kOThreads) lb[i] = B[i];
+    __syncthreads();
+    B = lb;
+  }
   uint32_t hits = 0;
   for (int64_t i = threadIdx.x; i < n; i += kOThreads) {
     const int32_t x = A[i];

@@ -235,3 +235,29 @@ def test_sweep_in_a_raw_inner_product_mode_equals_layer_by_layer():
     for i in range(3):
         np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"])
         np.testing.assert_array_equal(from_dev_bits(outs[i].k_hat), want[i]["k_hat"])
+
+
+def test_overlap_coefficient_synthetic_sets_both_paths():
+    """Given ascending index sets (sizes below and above what the kernel keeps
+    in LDS, and an empty head): the GPU's overlap equals the oracle's."""
+    rng = np.random.default_rng(41)
+    s, hkv = 30000, 5
+    budgets = np.array([100, 15360, 15361, 20000, 0])
+    desc = kvc.make_desc(s, 8, hkv, hkv, 64, 64, n_sink=0, n_recent=0)
+    off = kvc.kvc_retained_offsets(desc, budgets)
+    a_sets, b_sets = [], []
+    for g in range(hkv):
+        n = int(off[g + 1] - off[g])
+        a = np.sort(rng.choice(s, size=n, replace=False))
+        keep = rng.random(n) < rng.random()
+        b = np.sort(np.concatenate([a[keep], rng.choice(np.setdiff1d(np.arange(s), a), size=n - keep.sum(),
+                                                          replace=False)]))
+        a_sets.append(a)
+        b_sets.append(b)
+    ia = torch.from_numpy(np.concatenate(a_sets).astype(np.int32)).cuda()
+    ib = torch.from_numpy(np.concatenate(b_sets).astype(np.int32)).cuda()
+    res = torch.empty(hkv, dtype=torch.float32, device="cuda")
+    kvc.kvc_overlap_coefficient(desc, ia, ib, budgets, res)
+    torch.cuda.synchronize()
+    want = np.array([oracle.overlap_coefficient(a_sets[g], b_sets[g]) for g in range(hkv)], dtype=np.float32)
+    np.testing.assert_array_equal(res.cpu().numpy(), want)
