@@ -46,6 +46,14 @@ rows retrieved afterwards):
   overlap   the overlap coefficient |A & B| / min(|A|, |B|) of two retained
             index sets (HeteroCache summary, Key Contributions item 1).
 
+Immediate eviction, the schedule TideKV's layer-end eviction is compared
+with (TideKV, Fig. 1 caption, schedule (c): chunked prefill that evicts after
+every chunk; Table 8: Block-SnapKV): the prompt's keys arrive in chunks of C,
+and after chunk b the same scorer and selection run over the keys retained so
+far plus chunk b, with chunk b's last W queries as the window and one budget
+for every head. Keys keep their prompt positions; the mandatory sink and
+recent keys are the first n_sink and last n_recent of the accumulated keys.
+
 Per-KV-head budgets for the heterogeneous workload follow the inverse
 stability weighting of the HeteroCache summary (Methodology, Phase 2):
 w_h = 1 / S_stable,h and K_h proportional to w_h, rounded to integers that sum
@@ -367,3 +375,49 @@ def compress_layer(q_bits, k_bits, v_bits, budgets, n_sink, n_recent,
     idx = select(sel_vals, budgets, n_sink, n_recent)
     k_hat, v_hat, pos = gather(k_bits, v_bits, idx, pos_offset)
     return LayerResult(m=m, z=z, scores=sc, idx=idx, k_hat=k_hat, v_hat=v_hat, pos=pos)
+
+
+# ---------------------------------------------------------------------------
+# Immediate (chunk-boundary) eviction (TideKV, Fig. 1 caption, schedule (c);
+# Table 8, Block-SnapKV)
+# ---------------------------------------------------------------------------
+
+def chunk_bounds(s: int, chunk: int) -> list[tuple[int, int]]:
+    """Token ranges [c0, c1) of the chunks of an s-token prompt."""
+    return [(c0, min(c0 + chunk, s)) for c0 in range(0, s, chunk)]
+
+
+def compress_chunked(q_windows, k_bits, v_bits, chunk: int, budget: int, n_sink: int,
+                     n_recent: int, scale=None, pool=1, pos_offset=0, score_mode="softmax"):
+    """Final retained set of immediate eviction: per KV head, ascending prompt
+    indices, K_hat / V_hat rows (bf16 bits) and positions, as compress_layer's
+    LayerResult (m, z and scores of the last chunk boundary).
+
+    q_windows: bf16 bits [n_chunks, W, Hq, D], window b being the queries at
+    the last W positions of chunk b. At each boundary the accumulated keys of
+    a head are its retained keys (ascending positions) followed by the
+    chunk's keys, so the window's causal mask by index is the mask by
+    position -- which needs every chunk, the last included, to hold at least
+    W tokens (otherwise a window row would precede retained keys).
+    """
+    s, hkv, d = k_bits.shape
+    w = q_windows.shape[1]
+    bounds = chunk_bounds(s, chunk)
+    if len(q_windows) != len(bounds) or any(c1 - c0 < w for c0, c1 in bounds):
+        raise ValueError("one window per chunk, and every chunk at least W tokens long")
+    kept = [np.zeros(0, dtype=np.int64) for _ in range(hkv)]   # prompt indices per head
+    res = None
+    for b, (c0, c1) in enumerate(bounds):
+        new = np.arange(c0, c1)
+        acc = [np.concatenate([kept[g], new]) for g in range(hkv)]
+        n_acc = acc[0].size
+        k_acc = np.stack([k_bits[acc[g], g, :] for g in range(hkv)], axis=1)   # [S_acc, Hkv, D]
+        v_acc = np.stack([v_bits[acc[g], g, :] for g in range(hkv)], axis=1)
+        res = compress_layer(q_windows[b], k_acc, v_acc, [budget] * hkv, n_sink, n_recent,
+                             scale=scale, pool=pool, score_mode=score_mode)
+        kept = [acc[g][res.idx[g]] for g in range(hkv)]
+        assert all(x.size == min(budget, n_acc) for x in kept)
+    k_hat = np.concatenate([k_bits[kept[g], g, :] for g in range(hkv)], axis=0)
+    v_hat = np.concatenate([v_bits[kept[g], g, :] for g in range(hkv)], axis=0)
+    pos = np.concatenate([pos_offset + kept[g] for g in range(hkv)]).astype(np.int64)
+    return LayerResult(m=res.m, z=res.z, scores=res.scores, idx=kept, k_hat=k_hat, v_hat=v_hat, pos=pos)
