@@ -10,8 +10,19 @@
 namespace kvc {
 namespace {
 
-constexpr int kOThreads = 256;
+constexpr int kOThreads = 1024;
 constexpr int kOCap = 15360;  // entries of B held in LDS (60 KiB)
+
+// Position of the first entry >= x among B[0, n) (ascending).
+template <typename P>
+__device__ __forceinline__ int64_t lower_bound(P B, int64_t n, int32_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (B[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
 
 __global__ void __launch_bounds__(kOThreads) overlap_kernel(OverlapArgs a) {
   __shared__ uint32_t part[kOThreads / kWave];
@@ -21,20 +32,21 @@ __global__ void __launch_bounds__(kOThreads) overlap_kernel(OverlapArgs a) {
   const int64_t n = a.heads.offset[head + 1] - o;
   const int32_t* A = a.idx_a + o;
   const int32_t* B = a.idx_b + o;
-  if (n <= kOCap) {
+  const bool in_lds = n <= kOCap;
+  if (in_lds) {
     for (int64_t i = threadIdx.x; i < n; i += kOThreads) lb[i] = B[i];
     __syncthreads();
-    B = lb;
   }
   uint32_t hits = 0;
   for (int64_t i = threadIdx.x; i < n; i += kOThreads) {
     const int32_t x = A[i];
-    int64_t lo = 0, hi = n;  // first position with B[pos] >= x
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (B[mid] < x) lo = mid + 1; else hi = mid;
+    if (in_lds) {
+      const int64_t p = lower_bound(lb, n, x);
+      hits += p < n && lb[p] == x;
+    } else {
+      const int64_t p = lower_bound(B, n, x);
+      hits += p < n && B[p] == x;
     }
-    hits += lo < n && B[lo] == x;
   }
   const uint32_t tot = wave_total(wave_inclusive_sum(hits));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = tot;
