@@ -122,6 +122,78 @@ def copy_probe():
     return 0
 
 
+def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
+    """Time one layer's immediate eviction (kvc_compress_chunked: every chunk
+    boundary of the prompt) and the layer-end compressor (kvc_compress_layer)
+    on the same tensors and budget; HIP events around `reps` back-to-back
+    calls of each. Also the per-head overlap of the two retained sets."""
+    from synth import chunk_windows, get_config, layer_inputs
+    cfg = get_config(name)
+    x = layer_inputs(cfg, 0)
+    qw = chunk_windows(cfg, cfg.chunk, 0, q_last=x.q)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, qwd = dev_bf16(x.q), dev_bf16(x.k), dev_bf16(x.v), dev_bf16(qw)
+    del x
+    desc = kvc.desc_for(q, k, v, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool)
+    rows = min(cfg.budget, cfg.s)
+    k_out = torch.empty((cfg.hkv, rows, cfg.d), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty_like(k_out)
+    pos = torch.empty((cfg.hkv, rows), dtype=torch.int32, device=dev)
+    ws = torch.empty(kvc.kvc_chunked_workspace_size(desc, cfg.chunk, cfg.budget), dtype=torch.uint8, device=dev)
+    imm = kvc.PreparedChunked(desc, cfg.chunk, qwd, k, v, cfg.budget, k_out, v_out, pos, ws)
+    budgets = np.full(cfg.hkv, cfg.budget, dtype=np.int32)
+    lws = kvc.alloc_workspace(desc, dev)
+    lout = kvc.alloc_outputs(desc, budgets, dev, with_intermediates=False)
+    delayed = kvc.PreparedLayer(desc, q, k, v, budgets, lout, lws)
+
+    def timed(call):
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps, (time.perf_counter() - t0) * 1e6 / reps
+
+    imm_us, imm_wall = timed(lambda: imm.kvc_compress_chunked(sp))
+    del_us, _ = timed(lambda: delayed.kvc_compress_layer(sp))
+    ov = torch.empty(cfg.hkv, dtype=torch.float32, device=dev)
+    kvc.kvc_overlap_coefficient(desc, pos.view(-1), lout.idx, budgets, ov)
+    torch.cuda.synchronize()
+    n_chunks = (cfg.s + cfg.chunk - 1) // cfg.chunk
+    # algorithmic bytes of all boundaries: the chunk appended (K, V read and
+    # written), the accumulated K read by both scans, the scores written and
+    # read once, and the retained K, V rows read and written by the gather
+    row = cfg.hkv * cfg.d * 2
+    alg, kept = 0, 0
+    for b in range(n_chunks):
+        c = min(cfg.chunk, cfg.s - b * cfg.chunk)
+        s_acc = kept + c
+        alg += 4 * c * row
+        if s_acc > cfg.budget or b == n_chunks - 1:
+            r = min(cfg.budget, s_acc)
+            alg += 2 * s_acc * row + 2 * cfg.hkv * s_acc * 4 + 4 * r * row
+        kept = min(s_acc, cfg.budget)
+    out = {"s": cfg.s, "chunk": cfg.chunk, "budget_per_head": cfg.budget, "boundaries": n_chunks,
+           "immediate_us_per_layer": round(imm_us, 2), "immediate_wall_us_per_layer": round(imm_wall, 2),
+           "us_per_boundary": round(imm_us / n_chunks, 2), "layer_end_us_per_layer": round(del_us, 2),
+           "immediate_over_layer_end": round(imm_us / del_us, 3),
+           "retained_overlap_mean": round(float(ov.mean().item()), 4),
+           "alg_bytes_per_layer": alg, "hbm_frac": round(alg / (imm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "entry_points": ["kvc_compress_chunked", "kvc_compress_layer"]}
+    log(f"immediate eviction {name}: {imm_us:.1f} us/layer over {n_chunks} boundaries "
+        f"({imm_us / n_chunks:.2f} us each; wall {imm_wall:.1f} us) vs layer-end {del_us:.1f} us "
+        f"({imm_us / del_us:.2f}x); retained-set overlap {out['retained_overlap_mean']:.3f}")
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +399,13 @@ def main(argv=None):
             f"softmax {mode_detail[mode_name]['overlap_with_softmax_mean']:.3f}")
         del mprep
 
+    # ---- immediate (chunk-boundary) eviction, the schedule layer-end eviction
+    # is compared with: the Table-8 setting (16K prompt, 512-token chunks,
+    # 1024 keys per head) and the 64K layer with 2048-token chunks and 4096
+    # keys, each against the one-shot layer-end compressor on the same tensors
+    imm_detail = {name: immediate_eviction(kvc, torch, dev, name, max(4, K // 4), sp, stream)
+                  for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
+
     ms_per_step = wall * 1e3 / K
     value = cfg.s * K / wall
 
@@ -371,6 +450,7 @@ def main(argv=None):
                           "note": "a 512 MiB read before each layer evicts the memory-side cache; "
                                   "HIP events around one kvc_compress_layer call"},
         "score_modes": mode_detail,
+        "immediate_eviction": imm_detail,
         "sweep": {
             "entry_point": "kvc_compress_layers", "layers_in_flight": kvc.SWEEP_STREAMS,
             "value": round(cfg.s * K / sweep_wall, 1), "unit": "tokens/s",

@@ -9,5 +9,6 @@ from ._lib import (  # noqa: F401
     alloc_workspace, compress_layer, desc_for, kvc_budgets_inverse_stability,
     kvc_compress_layer, kvc_compress_layers, kvc_gather_retained, kvc_retained_offsets, kvc_score_pass1,
     kvc_score_pass2, kvc_select_topk, kvc_strerror, kvc_version, kvc_workspace_size, lib,
-    make_desc,
+    make_desc, kvc_chunk_workspace_size, kvc_evict_chunk, kvc_chunked_workspace_size, kvc_compress_chunked,
+    alloc_arena, PreparedChunked,
 )

@@ -102,6 +102,10 @@ def _load():
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kvc_overlap_coefficient": (ctypes.c_int, [D, P, P, P, P, P]),
+        "kvc_chunk_workspace_size": (SZ, [D, I64]),
+        "kvc_evict_chunk": (ctypes.c_int, [D, P, P, P, I32, I64, I64, P, P, P, P, P, P, P, SZ, P]),
+        "kvc_chunked_workspace_size": (SZ, [D, I64, I32]),
+        "kvc_compress_chunked": (ctypes.c_int, [D, I64, P, P, P, I32, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -297,6 +301,68 @@ def kvc_compress_layers(desc, layers, budgets, outs, ws):
     (alloc_sweep_workspace)."""
     args, _keep = _sweep_args(desc, layers, budgets, outs, ws)
     _check(_load().kvc_compress_layers(*args, _stream()))
+
+
+# ------------------------------------------------------------------ immediate eviction
+
+def kvc_chunk_workspace_size(desc: LayerDesc, cap: int) -> int:
+    n = _load().kvc_chunk_workspace_size(ctypes.byref(desc), int(cap))
+    if n == 0:
+        _check(KVC_ERR_INVALID_ARG)
+    return n
+
+
+def kvc_evict_chunk(desc, q_win, k_chunk, v_chunk, budget, n_kept, cap, cur, nxt, ws):
+    """One chunk boundary. cur, nxt: (k, v, pos) arenas of `cap` rows per
+    head (nxt and ws may be None when the boundary only appends)."""
+    L = _load()
+    nk, nv, npos = nxt if nxt is not None else (None, None, None)
+    _check(L.kvc_evict_chunk(ctypes.byref(desc), _bf16_ptr(q_win, "q_win"), _bf16_ptr(k_chunk, "k_chunk"),
+                             _bf16_ptr(v_chunk, "v_chunk"), int(budget), int(n_kept), int(cap),
+                             _bf16_ptr(cur[0], "k_cur"), _bf16_ptr(cur[1], "v_cur"), _dev_ptr(cur[2], "pos_cur", 4),
+                             _bf16_ptr(nk, "k_next"), _bf16_ptr(nv, "v_next"), _dev_ptr(npos, "pos_next", 4),
+                             _dev_ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+
+
+def kvc_chunked_workspace_size(desc: LayerDesc, chunk: int, budget: int) -> int:
+    n = _load().kvc_chunked_workspace_size(ctypes.byref(desc), int(chunk), int(budget))
+    if n == 0:
+        _check(KVC_ERR_INVALID_ARG)
+    return n
+
+
+def kvc_compress_chunked(desc, chunk, q_windows, k, v, budget, k_out, v_out, pos_out, ws):
+    """Immediate eviction over a resident prompt; q_windows [n_chunks * w, hq, D]."""
+    L = _load()
+    _check(L.kvc_compress_chunked(ctypes.byref(desc), int(chunk), _bf16_ptr(q_windows, "q_windows"),
+                                  _bf16_ptr(k, "k"), _bf16_ptr(v, "v"), int(budget), _bf16_ptr(k_out, "k_out"),
+                                  _bf16_ptr(v_out, "v_out"), _dev_ptr(pos_out, "pos_out", 4),
+                                  _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+
+
+def alloc_arena(hkv: int, cap: int, d: int, device="cuda"):
+    """(K, V, positions) of an arena: bf16 [hkv, cap, d] twice, int32 [hkv, cap]."""
+    import torch
+    return (torch.empty((hkv, cap, d), dtype=torch.bfloat16, device=device),
+            torch.empty((hkv, cap, d), dtype=torch.bfloat16, device=device),
+            torch.empty((hkv, cap), dtype=torch.int32, device=device))
+
+
+class PreparedChunked:
+    """Pre-marshalled kvc_compress_chunked call over fixed buffers (the
+    tensors must stay alive while this object is used)."""
+
+    def __init__(self, desc, chunk, q_windows, k, v, budget, k_out, v_out, pos_out, ws):
+        self._L = _load()
+        self.desc = desc
+        self._keep = (q_windows, k, v, k_out, v_out, pos_out, ws)
+        self._args = (ctypes.byref(desc), int(chunk), _bf16_ptr(q_windows, "q_windows"), _bf16_ptr(k, "k"),
+                      _bf16_ptr(v, "v"), int(budget), _bf16_ptr(k_out, "k_out"), _bf16_ptr(v_out, "v_out"),
+                      _dev_ptr(pos_out, "pos_out", 4), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size())
+
+    def kvc_compress_chunked(self, stream=None):
+        st = ctypes.c_void_p(stream) if stream is not None else _stream()
+        _check(self._L.kvc_compress_chunked(*self._args, st))
 
 
 # ------------------------------------------------------------------ convenience

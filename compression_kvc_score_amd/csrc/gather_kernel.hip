@@ -26,7 +26,36 @@ __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
   if (c == 0) a.pos_out[row] = (int32_t)(a.pos_offset + j);
 }
 
+// Immediate eviction appends each prompt chunk behind the keys a head has
+// retained so far (TideKV, Fig. 1 caption, schedule (c)); the arena is
+// head-major, so one thread moves one 16-byte chunk of a K row and of the V
+// row, reading the token-major chunk and writing the arena tail coalesced.
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+  const int cpr = a.d / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.n * a.hkv * cpr) return;
+  const int c = (int)(t % cpr);
+  const int64_t r = t / cpr;
+  const int g = (int)(r / a.n);
+  const int64_t tok = r % a.n;
+  const int64_t dst = ((int64_t)g * a.cap + a.row0 + tok) * a.d + c * 8;
+  const uint4 kv = *reinterpret_cast<const uint4*>(a.k + tok * a.k_tok + (int64_t)g * a.k_head + c * 8);
+  const uint4 vv = *reinterpret_cast<const uint4*>(a.v + tok * a.v_tok + (int64_t)g * a.v_head + c * 8);
+  *reinterpret_cast<uint4*>(a.k_arena + dst) = kv;
+  *reinterpret_cast<uint4*>(a.v_arena + dst) = vv;
+  if (c == 0) a.pos_arena[(int64_t)g * a.cap + a.row0 + tok] = (int32_t)(a.pos0 + tok);
+}
+
 }  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  if (a.n == 0) return hipSuccess;
+  AppendArgs args = a;
+  void* kargs[] = {&args};
+  const int64_t threads = a.n * a.hkv * (a.d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&append_kernel), grid, dim3(256), kargs, 0, st);
+}
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
   if (a.total_rows == 0) return hipSuccess;

@@ -305,7 +305,7 @@ int run_pass2(const Layer& L, const void* q, const void* k, const float* m, cons
 int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
                void* ws, bool need_hist, hipStream_t st, const void* k = nullptr,
                const void* v = nullptr, void* k_out = nullptr, void* v_out = nullptr,
-               int32_t* pos_out = nullptr) {
+               int32_t* pos_out = nullptr, const int32_t* pos_in = nullptr, int64_t pos_in_head = 0) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   SelectArgs a{};
@@ -334,6 +334,8 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
     a.v_out = static_cast<uint16_t*>(v_out);
     a.pos_out = pos_out;
     a.pos_offset = L.pos_offset;
+    a.pos_in = pos_in;
+    a.pos_in_head = pos_in_head;
     a.d = L.d;
   }
   const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
@@ -406,9 +408,12 @@ int check_layer_ptrs(const void* q_win, const void* k, const void* v, const int3
 }
 
 // One validated layer onto one stream; m, z, scores NULL: in the workspace.
+// pos_in non-null: retained positions are looked up there (per head, stride
+// pos_in_head) instead of pos_offset + index.
 int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* v, const HeadTable& ht,
                   float* m_out, float* z_out, float* scores_out, int32_t* idx_out, void* k_out,
-                  void* v_out, int32_t* pos_out, void* ws, hipStream_t st) {
+                  void* v_out, int32_t* pos_out, void* ws, hipStream_t st,
+                  const int32_t* pos_in = nullptr, int64_t pos_in_head = 0) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
@@ -426,12 +431,105 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
       hist = sa.hist;
     }
     KVC_TRY(run_logit(L, q_win, k, sc, hist, st));
-    return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out);
+    return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
+                      pos_in_head);
   }
   KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
   KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
   // the compaction of the selection copies the retained rows as it goes
-  return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out);
+  return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
+                    pos_in_head);
+}
+
+// ---- immediate (chunk-boundary) eviction (TideKV, Fig. 1 caption, schedule
+// (c); Table 8, Block-SnapKV). A boundary's accumulated keys -- the retained
+// ones, then the new chunk -- live in a head-major arena of `cap` rows per
+// head (K, V bf16 [hkv][cap][D], positions int32 [hkv][cap]), so the scans
+// and the selection see one ordinary layer of n_kept + c keys.
+
+struct Arena {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t* pos;
+};
+
+// The accumulated keys of a boundary as a layer: the chunk's shape and
+// options, s_acc keys read from an arena of `cap` rows per head.
+int arena_layer(const kvc_layer_desc* chunk, int64_t s_acc, int64_t cap, Layer& La) {
+  kvc_layer_desc a = *chunk;
+  a.s = s_acc;
+  a.pos_offset = 0;
+  a.k_tok_stride = a.v_tok_stride = chunk->d;
+  a.k_head_stride = a.v_head_stride = cap * chunk->d;
+  return normalize(&a, La);
+}
+
+// One budget for every head; head g's retained rows start at g * row_stride.
+HeadTable arena_table(const Layer& La, int32_t budget, int64_t row_stride) {
+  HeadTable t;
+  std::memset(&t, 0, sizeof t);
+  for (int g = 0; g < La.hkv; ++g) {
+    t.budget[g] = budget;
+    t.offset[g] = (int64_t)g * row_stride;
+  }
+  t.offset[La.hkv] = (int64_t)(La.hkv - 1) * row_stride + std::min<int64_t>(budget, La.s);
+  return t;
+}
+
+// Workspace of one boundary: the layer's, then its retained indices [hkv][cap].
+size_t boundary_ws_bytes(const Layer& La, int64_t cap) {
+  return ws_layout(La).total + align_up((size_t)La.hkv * cap * 4, 256);
+}
+
+int check_boundary(const Layer& La, int32_t budget, int64_t cap) {
+  if (budget < La.s && budget < mandatory_count(La.s, La.n_sink, La.n_recent))
+    return fail(KVC_ERR_INVALID_ARG, "budget=%d below the %lld mandatory keys of %lld accumulated keys", budget,
+                (long long)mandatory_count(La.s, La.n_sink, La.n_recent), (long long)La.s);
+  if (cap < La.s) return fail(KVC_ERR_INVALID_ARG, "arena of %lld rows cannot hold %lld keys", (long long)cap, (long long)La.s);
+  return KVC_OK;
+}
+
+// Append the chunk to `cur` at row n_kept; with `compress`, score and select
+// the n_kept + c accumulated keys and write the retained rows (positions
+// carried from `cur`) to `out`, head g at row g * out_stride.
+int enqueue_boundary(const Layer& Lc, const kvc_layer_desc* chunk_desc, const void* q_win, const void* k_chunk,
+                     const void* v_chunk, int32_t budget, int64_t n_kept, int64_t cap, const Arena& cur,
+                     bool compress, const Arena& out, int64_t out_stride, void* ws, hipStream_t st) {
+  AppendArgs ap{};
+  ap.k = static_cast<const uint16_t*>(k_chunk);
+  ap.v = static_cast<const uint16_t*>(v_chunk);
+  ap.k_tok = Lc.k_tok;
+  ap.k_head = Lc.k_head;
+  ap.v_tok = Lc.v_tok;
+  ap.v_head = Lc.v_head;
+  ap.k_arena = cur.k;
+  ap.v_arena = cur.v;
+  ap.pos_arena = cur.pos;
+  ap.cap = cap;
+  ap.row0 = n_kept;
+  ap.n = Lc.s;
+  ap.pos0 = Lc.pos_offset;
+  ap.hkv = Lc.hkv;
+  ap.d = Lc.d;
+  const hipError_t e = launch_append(ap, st);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (!compress) return KVC_OK;
+  Layer La;
+  KVC_TRY(arena_layer(chunk_desc, n_kept + Lc.s, cap, La));
+  const HeadTable ht = arena_table(La, budget, out_stride);
+  int32_t* idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(La).total);
+  return enqueue_layer(La, q_win, cur.k, cur.v, ht, nullptr, nullptr, nullptr, idx, out.k, out.v, out.pos, ws, st,
+                       cur.pos, cap);
+}
+
+int check_arena(const Arena& a, const char* which) {
+  char name[32];
+  std::snprintf(name, sizeof name, "k_%s", which);
+  KVC_TRY(check_ptr(a.k, 16, name));
+  std::snprintf(name, sizeof name, "v_%s", which);
+  KVC_TRY(check_ptr(a.v, 16, name));
+  std::snprintf(name, sizeof name, "pos_%s", which);
+  return check_ptr(a.pos, 4, name);
 }
 
 // The library's own streams for whole-layer sweeps, one set per device:
@@ -688,6 +786,162 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
     if (e != hipSuccess && status == KVC_OK) status = hip_fail(e, "sweep join");
   }
   return status;
+}
+
+size_t kvc_chunk_workspace_size(const kvc_layer_desc* desc, int64_t cap) {
+  Layer Lc, La;
+  if (normalize(desc, Lc) != KVC_OK || cap < desc->s || cap > kMaxPrompt) return 0;
+  if (arena_layer(desc, cap, cap, La) != KVC_OK) return 0;
+  return boundary_ws_bytes(La, cap);
+}
+
+int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k_chunk, const void* v_chunk,
+                    int32_t budget, int64_t n_kept, int64_t cap, void* k_cur, void* v_cur, int32_t* pos_cur,
+                    void* k_next, void* v_next, int32_t* pos_next, void* ws, size_t ws_bytes,
+                    kvc_stream_t stream) {
+  Layer Lc;
+  KVC_TRY(normalize(desc, Lc));
+  if (budget < 0) return fail(KVC_ERR_INVALID_ARG, "budget=%d < 0", budget);
+  if (n_kept < 0) return fail(KVC_ERR_INVALID_ARG, "n_kept=%lld < 0", (long long)n_kept);
+  if (cap < n_kept + Lc.s || cap > kMaxPrompt)
+    return fail(KVC_ERR_INVALID_ARG, "cap=%lld outside [n_kept + s, 2^23]", (long long)cap);
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k_chunk, 16, "k_chunk"));
+  KVC_TRY(check_ptr(v_chunk, 16, "v_chunk"));
+  const Arena cur{static_cast<uint16_t*>(k_cur), static_cast<uint16_t*>(v_cur), pos_cur};
+  KVC_TRY(check_arena(cur, "cur"));
+  const bool compress = n_kept + Lc.s > budget;
+  const Arena next{static_cast<uint16_t*>(k_next), static_cast<uint16_t*>(v_next), pos_next};
+  if (compress) {
+    Layer La;
+    KVC_TRY(arena_layer(desc, n_kept + Lc.s, cap, La));
+    KVC_TRY(check_boundary(La, budget, cap));
+    KVC_TRY(check_arena(next, "next"));
+    if (next.k == cur.k || next.v == cur.v || next.pos == cur.pos)
+      return fail(KVC_ERR_INVALID_ARG, "the next arena must not be the current one");
+    const size_t need = boundary_ws_bytes(La, cap);
+    if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (ws_bytes < need) return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
+    KVC_TRY(check_lds(La));
+  }
+  return enqueue_boundary(Lc, desc, q_win, k_chunk, v_chunk, budget, n_kept, cap, cur, compress, next, cap, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// Sizes of the whole-prompt immediate-eviction driver.
+struct ChunkedPlan {
+  int64_t n_chunks, cap, rows;
+  size_t arena_k, arena_pos, arena, total;
+};
+
+int chunked_plan(const kvc_layer_desc* desc, int64_t chunk, int32_t budget, ChunkedPlan& p) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  if (chunk < L.w) return fail(KVC_ERR_INVALID_ARG, "chunk=%lld shorter than the window w=%d", (long long)chunk, L.w);
+  if (budget < 0) return fail(KVC_ERR_INVALID_ARG, "budget=%d < 0", budget);
+  p.n_chunks = (L.s + chunk - 1) / chunk;
+  const int64_t last = L.s - (p.n_chunks - 1) * chunk;
+  if (last < L.w)
+    return fail(KVC_ERR_INVALID_ARG, "last chunk of %lld tokens shorter than the window w=%d", (long long)last, L.w);
+  p.cap = std::min<int64_t>((int64_t)budget + chunk, L.s);
+  p.rows = std::min<int64_t>(budget, L.s);
+  p.arena_k = align_up((size_t)L.hkv * p.cap * L.d * 2, 256);
+  p.arena_pos = align_up((size_t)L.hkv * p.cap * 4, 256);
+  p.arena = 2 * p.arena_k + p.arena_pos;
+  Layer La;
+  KVC_TRY(arena_layer(desc, p.cap, p.cap, La));
+  p.total = 2 * p.arena + boundary_ws_bytes(La, p.cap);
+  return KVC_OK;
+}
+
+}  // namespace
+
+size_t kvc_chunked_workspace_size(const kvc_layer_desc* desc, int64_t chunk, int32_t budget) {
+  ChunkedPlan p;
+  if (chunked_plan(desc, chunk, budget, p) != KVC_OK) return 0;
+  return p.total;
+}
+
+int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* q_windows, const void* k,
+                         const void* v, int32_t budget, void* k_out, void* v_out, int32_t* pos_out, void* ws,
+                         size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  ChunkedPlan p;
+  KVC_TRY(chunked_plan(desc, chunk, budget, p));
+  KVC_TRY(check_ptr(q_windows, 16, "q_windows"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  KVC_TRY(check_ptr(v, 16, "v"));
+  KVC_TRY(check_ptr(k_out, 16, "k_out"));
+  KVC_TRY(check_ptr(v_out, 16, "v_out"));
+  KVC_TRY(check_ptr(pos_out, 4, "pos_out"));
+  if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.total);
+  if (ws_bytes < p.total) return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, p.total);
+  if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
+
+  // one chunk descriptor per boundary, all validated before the first launch
+  std::vector<kvc_layer_desc> cds((size_t)p.n_chunks);
+  std::vector<Layer> lcs((size_t)p.n_chunks);
+  std::vector<char> squeeze((size_t)p.n_chunks);
+  std::vector<Layer> las;
+  int64_t n_kept = 0;
+  for (int64_t b = 0; b < p.n_chunks; ++b) {
+    const int64_t c0 = b * chunk, c = std::min(chunk, L.s - c0);
+    kvc_layer_desc& cd = cds[(size_t)b];
+    cd = *desc;
+    cd.s = c;
+    cd.pos_offset = desc->pos_offset + c0;
+    cd.q_tok_stride = L.q_tok;
+    cd.q_head_stride = L.q_head;
+    cd.k_tok_stride = L.k_tok;
+    cd.k_head_stride = L.k_head;
+    cd.v_tok_stride = L.v_tok;
+    cd.v_head_stride = L.v_head;
+    KVC_TRY(normalize(&cd, lcs[(size_t)b]));
+    const int64_t s_acc = n_kept + c;
+    const bool last = b + 1 == p.n_chunks;
+    squeeze[(size_t)b] = last || s_acc > budget;
+    if (squeeze[(size_t)b]) {
+      Layer La;
+      KVC_TRY(arena_layer(&cd, s_acc, p.cap, La));
+      const int st = check_boundary(La, budget, p.cap);
+      if (st != KVC_OK) return fail(st, "chunk %lld: %s", (long long)b, g_last_error.c_str());
+      las.push_back(La);
+    }
+    n_kept = std::min<int64_t>(s_acc, budget);
+  }
+  for (const Layer& La : las) KVC_TRY(check_lds(La));
+
+  char* wsb = static_cast<char*>(ws);
+  Arena arenas[2];
+  for (int i = 0; i < 2; ++i) {
+    char* base = wsb + i * p.arena;
+    arenas[i] = Arena{reinterpret_cast<uint16_t*>(base), reinterpret_cast<uint16_t*>(base + p.arena_k),
+                      reinterpret_cast<int32_t*>(base + 2 * p.arena_k)};
+  }
+  void* bws = wsb + 2 * p.arena;
+  const Arena final_out{static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), pos_out};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* qb = static_cast<const char*>(q_windows);
+  const char* kb = static_cast<const char*>(k);
+  const char* vb = static_cast<const char*>(v);
+  int cur = 0;
+  n_kept = 0;
+  for (int64_t b = 0; b < p.n_chunks; ++b) {
+    const Layer& Lc = lcs[(size_t)b];
+    const int64_t c0 = b * chunk;
+    const bool last = b + 1 == p.n_chunks;
+    const Arena& out = last ? final_out : arenas[1 - cur];
+    KVC_TRY(enqueue_boundary(Lc, &cds[(size_t)b], qb + (size_t)(b * L.w * L.q_tok) * 2, kb + (size_t)(c0 * L.k_tok) * 2,
+                             vb + (size_t)(c0 * L.v_tok) * 2, budget, n_kept, p.cap, arenas[cur], squeeze[(size_t)b],
+                             out, last ? p.rows : p.cap, bws, st));
+    if (squeeze[(size_t)b] && !last) cur = 1 - cur;
+    n_kept = std::min<int64_t>(n_kept + Lc.s, budget);
+  }
+  return KVC_OK;
 }
 
 }  // extern "C"

@@ -96,6 +96,8 @@ struct SelectArgs {
                          // those inside b* (sub-chunk << 19 | low 19 pattern bits, key order)
   HeadTable heads;
   bool signed_keys;      // scores may be negative (raw inner-product modes)
+  int replicas;          // compaction workgroups per sub-chunk (set by the launcher): each
+                         // resolves the sub-chunk and copies its share of the kept rows
   // retained rows copied by the compaction (k == nullptr: indices only)
   const uint16_t* k;
   const uint16_t* v;
@@ -104,6 +106,8 @@ struct SelectArgs {
   uint16_t* v_out;
   int32_t* pos_out;
   int64_t pos_offset;
+  const int32_t* pos_in;  // non-null: position of key j of head g is pos_in[g * pos_in_head + j]
+  int64_t pos_in_head;
   int d;
 };
 
@@ -137,6 +141,21 @@ hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hi
 hipError_t launch_hist_clear(const Layer& L, const SelectArgs& a, hipStream_t st);
 size_t select_lds_bytes(int n_chunks, int n_subs);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
+// Append of a prompt chunk to a head-major arena (immediate eviction): chunk
+// token t of head g goes to arena row g * cap + row0 + t, with position pos0 + t.
+struct AppendArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_tok, k_head, v_tok, v_head;
+  uint16_t* k_arena;
+  uint16_t* v_arena;
+  int32_t* pos_arena;
+  int64_t cap, row0, n;  // arena rows per head, first row written, chunk tokens
+  int64_t pos0;
+  int hkv, d;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 struct OverlapArgs {
   const int32_t* idx_a;
   const int32_t* idx_b;

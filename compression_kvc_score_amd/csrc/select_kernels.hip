@@ -40,6 +40,8 @@ constexpr int kWaves = kThreads / kWave;          // 16
 constexpr int kChunk = kSelectChunk;              // 4096 keys per filter workgroup, 4 per thread
 constexpr int kWavesPerSub = kWaves / kSubsPerChunk;
 constexpr int kCWaves = kCompactThreads / kWave;  // 4 per compaction workgroup
+constexpr int kMaxReplicas = 16;                  // compaction workgroups per sub-chunk, at most
+constexpr int kCompactTarget = 512;               // compaction workgroups aimed for with the row copy
 constexpr int kCopyUnroll = 8;                    // rows in flight per thread in the row copy
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -622,7 +624,10 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
   __shared__ uint32_t hist1[1024], hist2[1024];
   __shared__ uint32_t scratch[4 * kCWaves], pick[2];
   __shared__ int32_t kept_keys[GATHER ? kSub : 1];
-  const int head = blockIdx.x / a.n_subs, sub = blockIdx.x % a.n_subs;
+  // replicas of a sub-chunk resolve it alike; replica 0 writes the indices
+  // and each copies every replicas-th group of kept rows
+  const int rep = blockIdx.x % a.replicas, blk = blockIdx.x / a.replicas;
+  const int head = blk / a.n_subs, sub = blk % a.n_subs;
   const HeadGeom h = head_geom(a, head);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t s0 = (int64_t)sub * kSub;
@@ -651,6 +656,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     // they are in L2 when the copy runs after the resolve
     auto prefetch = [&](uint32_t bstar) {
       if constexpr (GATHER) {
+        if (a.replicas > 1) return;  // the copy is spread thin enough
         // decide for all four keys first: a decision after a prefetch would
         // wait for it
         bool want[4];
@@ -732,9 +738,10 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     if (keep) {
       const int64_t o = (int64_t)first + p;
       const int32_t j = (int32_t)(j0 + e);
-      if (o < h.budget) {
+      if (o < h.budget && rep == 0) {
         out[o] = j;
-        if (GATHER) a.pos_out[row0 + o] = (int32_t)(a.pos_offset + j);
+        if (GATHER)
+          a.pos_out[row0 + o] = a.pos_in ? a.pos_in[head * a.pos_in_head + j] : (int32_t)(a.pos_offset + j);
       }
       if (GATHER) kept_keys[p] = j;
       ++p;
@@ -757,7 +764,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     const int64_t tok = is_k ? a.k_tok : a.v_tok;
     uint16_t* dst = (is_k ? a.k_out : a.v_out) + (row0 + first) * a.d + cu * 8;
     const int nr = (int)n;
-    for (int r = r0; r < nr; r += kCopyUnroll * rpp) {
+    for (int r = r0 + rep * kCopyUnroll * rpp; r < nr; r += kCopyUnroll * rpp * a.replicas) {
       u32x4 buf[kCopyUnroll];
 #pragma unroll
       for (int i = 0; i < kCopyUnroll; ++i) {
@@ -803,12 +810,16 @@ hipError_t launch_select_keys(const Layer& L, const SelectArgs& a, bool need_his
   }
   e = hipLaunchKernel(reinterpret_cast<const void*>(&filter_kernel<SIGNED>), chunks, dim3(kThreads), kargs, 0, st);
   if (e != hipSuccess) return e;
+  // short rows (few sub-chunks) spread their row copy over more workgroups
+  const int subs = L.hkv * a.n_subs;
+  const int want = kCompactTarget / subs;
+  args.replicas = a.k == nullptr || want < 1 ? 1 : (want > kMaxReplicas ? kMaxReplicas : want);
   const size_t lds = select_lds_bytes(a.n_chunks, a.n_subs);
   const void* compact = a.k != nullptr ? reinterpret_cast<const void*>(&compact_kernel<true, SIGNED>)
                                        : reinterpret_cast<const void*>(&compact_kernel<false, SIGNED>);
   e = ensure_lds(compact, lds);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(compact, dim3((unsigned)(L.hkv * a.n_subs)), dim3(kCompactThreads), kargs, lds, st);
+  return hipLaunchKernel(compact, dim3((unsigned)(subs * args.replicas)), dim3(kCompactThreads), kargs, lds, st);
 }
 
 hipError_t launch_select(const Layer& L, const SelectArgs& a, bool need_hist, hipStream_t st) {

@@ -270,6 +270,77 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers,
                         void* const* k_out, void* const* v_out, int32_t* const* pos_out,
                         void* ws, size_t ws_bytes, kvc_stream_t stream);
 
+/*
+ * Immediate (chunk-boundary) eviction, the schedule that TideKV's layer-end
+ * eviction is compared with (TideKV, Fig. 1 caption, schedule (c): chunked
+ * prefill that evicts after every chunk; Table 8: Block-SnapKV): after each
+ * prompt chunk, the same scorer and selection run over the keys a KV head has
+ * retained so far followed by the chunk's keys, with the chunk's last w
+ * queries as the observation window and one budget for every head. The
+ * mandatory keys are the first n_sink and the last n_recent of those
+ * accumulated keys; retained keys keep their absolute positions.
+ *
+ * An arena holds one boundary's accumulated keys, head-major: K and V bf16
+ * [hkv][cap][D] (dense), positions int32 [hkv][cap]; rows [0, n) of every head
+ * are in use, in ascending position order.
+ */
+
+/*
+ * Workspace bytes kvc_evict_chunk needs for chunk descriptor `desc` and
+ * arenas of `cap` rows per head (enough for every n_kept with
+ * n_kept + desc->s <= cap). Pure host function; 0 if the arguments are
+ * invalid (cap < desc->s or cap > 2^23).
+ */
+size_t kvc_chunk_workspace_size(const kvc_layer_desc* desc, int64_t cap);
+
+/*
+ * One chunk boundary. desc describes the chunk: s = its c tokens (w <= c),
+ * the window, heads, options, pos_offset = absolute position of its first
+ * token, and the strides of q_win ([w][hq][D], the chunk's last w queries)
+ * and of k_chunk, v_chunk ([c][hkv][D]).
+ *  - The chunk is appended to the current arena (k_cur, v_cur, pos_cur) at
+ *    rows [n_kept, n_kept + c) of every head, with positions
+ *    pos_offset + t; cap >= n_kept + c.
+ *  - If n_kept + c <= budget nothing else happens: the current arena now
+ *    holds n_kept + c rows, and k_next, v_next, pos_next and ws are not used
+ *    (they may be NULL).
+ *  - Otherwise the n_kept + c accumulated keys are scored and selected as
+ *    kvc_compress_layer does for a layer of that many keys, and the `budget`
+ *    retained rows of every head (ascending positions, carried from pos_cur)
+ *    are written to rows [0, budget) of the next arena, which has the same
+ *    cap and must not overlap the current one. budget must cover the
+ *    mandatory keys of the accumulated ones. ws: at least
+ *    kvc_chunk_workspace_size(desc, cap) bytes, 256-byte aligned.
+ * budget >= 0; every pointer is device memory of the current device.
+ */
+int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k_chunk, const void* v_chunk,
+                    int32_t budget, int64_t n_kept, int64_t cap, void* k_cur, void* v_cur, int32_t* pos_cur,
+                    void* k_next, void* v_next, int32_t* pos_next, void* ws, size_t ws_bytes,
+                    kvc_stream_t stream);
+
+/* Workspace bytes of kvc_compress_chunked (two arenas of
+ * min(budget + chunk, s) rows per head and one boundary's workspace); 0 if
+ * the arguments are invalid. Pure host function. */
+size_t kvc_chunked_workspace_size(const kvc_layer_desc* desc, int64_t chunk, int32_t budget);
+
+/*
+ * Immediate eviction over a whole resident prompt: desc describes the prompt
+ * (s tokens, K and V [s][hkv][D] strided as for kvc_compress_layer,
+ * pos_offset = position of token 0); the chunks are [b * chunk,
+ * min((b + 1) * chunk, s)), each -- the last included -- at least w tokens.
+ * q_windows: the n_chunks windows stacked along the token axis, window b
+ * (the last w queries of chunk b) at token rows [b * w, (b + 1) * w) with the
+ * q strides of desc. Each boundary runs as kvc_evict_chunk; the last one
+ * always selects (keeping everything when budget covers the prompt) and
+ * writes the final retained set: k_out, v_out bf16 [hkv][rows][D] and
+ * pos_out int32 [hkv][rows], rows = min(budget, s), head-major, ascending
+ * positions. ws: kvc_chunked_workspace_size(desc, chunk, budget) bytes,
+ * 256-byte aligned.
+ */
+int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* q_windows, const void* k,
+                         const void* v, int32_t budget, void* k_out, void* v_out, int32_t* pos_out, void* ws,
+                         size_t ws_bytes, kvc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ from .gen import (
     layer_seed,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
+    chunk_windows,
 )
 
 __all__ = [
@@ -23,4 +24,5 @@ __all__ = [
     "layer_seed",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "chunk_windows",
 ]

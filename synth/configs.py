@@ -29,6 +29,7 @@ class LayerConfig:
     hetero: bool = False    # per-head budgets from inverse stability
     total_budget: int = 0   # sum of per-head budgets when hetero
     seed_base: int = 0
+    chunk: int = 0          # prefill chunk of immediate (chunk-boundary) eviction (0: none)
 
     @property
     def group(self) -> int:
@@ -76,6 +77,19 @@ CONFIGS: dict[str, LayerConfig] = {
         block=256, budget=4096, n_sink=4, n_recent=32,
         n_heavy=_heavy(0.01, 65536), sink_scale=4.0, layers=48, hetero=True,
         total_budget=8 * 4096, seed_base=20261700),
+    # Immediate eviction after every 512-token chunk of a 16K prompt with a
+    # 1024-key budget (the Block-SnapKV setting of TideKV Table 8); same
+    # tensors as llama8b_16k.
+    "llama8b_16k_imm": LayerConfig(
+        name="llama8b_16k_imm", hq=32, hkv=8, d=128, s=16384, w=32, block=256,
+        budget=1024, n_sink=4, n_recent=32, n_heavy=_heavy(0.01, 16384),
+        sink_scale=4.0, layers=1, seed_base=20261400, chunk=512),
+    # The 64K layer evicted after every 2048-token chunk with the 4096-key
+    # budget (TideKV Table 2's chunk and budget); same tensors as llama8b_64k.
+    "llama8b_64k_imm": LayerConfig(
+        name="llama8b_64k_imm", hq=32, hkv=8, d=128, s=65536, w=32, block=256,
+        budget=4096, n_sink=4, n_recent=32, n_heavy=_heavy(0.01, 65536),
+        sink_scale=4.0, layers=1, seed_base=20261500, chunk=2048),
 }
 
 

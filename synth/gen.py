@@ -14,7 +14,11 @@ Recipe (one layer of one workload):
   * the first ``n_sink`` keys of every head are multiplied by ``sink_scale``
     (a power of two, so the bf16 product is exact);
   * for the heterogeneous-budget workload, per-KV-head stabilities are drawn
-    from U(0.2, 0.9) (float64).
+    from U(0.2, 0.9) (float64);
+  * for chunked prefill with immediate eviction, chunk b's window (the queries
+    at its last w positions) is drawn like Q from child b of the seed
+    sequence [layer seed, 1]; the last chunk's window is the layer's Q itself,
+    the queries at the prompt's last w positions.
 """
 from __future__ import annotations
 
@@ -121,3 +125,16 @@ def layer_inputs(cfg: LayerConfig, layer: int = 0, threads: int | None = None) -
         s_stable = rng_s.uniform(0.2, 0.9, size=hkv)
 
     return LayerInputs(cfg=cfg, layer=layer, q=q, k=k, v=v, heavy_pos=heavy, s_stable=s_stable)
+
+
+def chunk_windows(cfg: LayerConfig, chunk: int, layer: int = 0, q_last: np.ndarray | None = None) -> np.ndarray:
+    """Window queries of every chunk, stacked [n_chunks * w, hq, d] (uint16):
+    rows [b * w, (b + 1) * w) are chunk b's window. q_last: the layer's Q
+    (drawn here when not given)."""
+    n_chunks = (cfg.s + chunk - 1) // chunk
+    if q_last is None:
+        q_last = layer_inputs(cfg.with_(s=max(cfg.w, 1), n_heavy=0), layer).q
+    kids = np.random.SeedSequence([layer_seed(cfg, layer), 1]).spawn(max(n_chunks - 1, 0))
+    parts = [_normal_bf16(kids[b], (cfg.w, cfg.hq, cfg.d)) for b in range(n_chunks - 1)]
+    parts.append(np.ascontiguousarray(q_last, dtype=np.uint16))
+    return np.concatenate(parts, axis=0)

@@ -249,3 +249,76 @@ def test_score_mode_arguments_are_checked_before_launch():
     assert lib.kvc_overlap_coefficient(dd, P, P, None, P, None) == kvc.KVC_ERR_INVALID_ARG
     bad = np.full(8, 10, dtype=np.int32)
     assert lib.kvc_overlap_coefficient(dd, P, P, bad.ctypes.data_as(ctypes.c_void_p), P, None) == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_chunk_workspace_sizes():
+    d = base_desc(s=512)
+    n1 = kvc.kvc_chunk_workspace_size(d, 1536)
+    n2 = kvc.kvc_chunk_workspace_size(d, 4096)
+    assert 0 < n1 < n2 and n1 % 256 == 0
+    lib = kvc.lib()
+    assert lib.kvc_chunk_workspace_size(ctypes.byref(d), 511) == 0        # cap below the chunk
+    assert lib.kvc_chunk_workspace_size(ctypes.byref(d), (1 << 23) + 1) == 0
+    p = base_desc(s=16384)
+    n = kvc.kvc_chunked_workspace_size(p, 512, 1024)
+    arena = 8 * 1536 * (2 * 128 * 2 + 4)
+    assert n >= 2 * arena + kvc.kvc_chunk_workspace_size(base_desc(s=512), 1536)
+    assert lib.kvc_chunked_workspace_size(ctypes.byref(p), 16, 1024) == 0     # chunk < w
+    assert lib.kvc_chunked_workspace_size(ctypes.byref(base_desc(s=16384 + 8)), 512, 1024) == 0  # last chunk < w
+    assert lib.kvc_chunked_workspace_size(ctypes.byref(p), 512, -1) == 0
+
+
+def test_chunk_eviction_rejects_bad_arguments_before_launch():
+    """Both immediate-eviction entry points validate everything, the next
+    arena and the workspace included, before the first launch."""
+    lib = kvc.lib()
+    d = base_desc(s=512)
+    dd = ctypes.byref(d)
+    cap = 1536
+    ws_n = kvc.kvc_chunk_workspace_size(d, cap)
+    good = [_fake(0x10000 + 0x1000 * i) for i in range(9)]
+
+    def call(q=good[0], kc=good[1], vc=good[2], budget=1024, n_kept=1024, cap=cap, cur=good[3:6], nxt=good[6:9],
+             ws=_fake(0x100000), ws_bytes=ws_n):
+        return lib.kvc_evict_chunk(dd, q, kc, vc, budget, n_kept, cap, *cur, *nxt, ws, ws_bytes, None)
+
+    assert call(budget=-1) == kvc.KVC_ERR_INVALID_ARG
+    assert call(n_kept=-1) == kvc.KVC_ERR_INVALID_ARG
+    assert call(cap=1535) == kvc.KVC_ERR_INVALID_ARG
+    for kw in ("q", "kc", "vc"):
+        assert call(**{kw: None}) == kvc.KVC_ERR_INVALID_ARG
+    assert call(kc=_fake(0x10008)) == kvc.KVC_ERR_ALIGN
+    for j in range(3):
+        c = list(good[3:6])
+        c[j] = None
+        assert call(cur=c) == kvc.KVC_ERR_INVALID_ARG
+        n = list(good[6:9])
+        n[j] = None
+        assert call(nxt=n) == kvc.KVC_ERR_INVALID_ARG      # eviction needs the next arena
+    assert call(nxt=good[3:6]) == kvc.KVC_ERR_INVALID_ARG  # next == current
+    assert call(ws=None) == kvc.KVC_ERR_WORKSPACE
+    assert call(ws_bytes=ws_n // 2) == kvc.KVC_ERR_WORKSPACE
+    assert call(ws=_fake(0x100080)) == kvc.KVC_ERR_ALIGN
+    assert call(budget=20) == kvc.KVC_ERR_INVALID_ARG      # below the 36 mandatory keys
+    assert "mandatory" in lib.kvc_last_error().decode()
+
+    p = base_desc(s=16384)
+    pp = ctypes.byref(p)
+    n = kvc.kvc_chunked_workspace_size(p, 512, 1024)
+    outs = good[3:6]
+
+    def run(chunk=512, q=good[0], k=good[1], v=good[2], budget=1024, outs=outs, ws=_fake(0x100000), ws_bytes=n):
+        return lib.kvc_compress_chunked(pp, chunk, q, k, v, budget, *outs, ws, ws_bytes, None)
+
+    assert run(chunk=16) == kvc.KVC_ERR_INVALID_ARG        # chunk shorter than w
+    assert run(chunk=16384 - 8) == kvc.KVC_ERR_INVALID_ARG  # last chunk of 8 < w
+    assert run(ws_bytes=n - 1) == kvc.KVC_ERR_WORKSPACE
+    assert run(ws=_fake(0x100040)) == kvc.KVC_ERR_ALIGN
+    for j in range(3):
+        o = list(outs)
+        o[j] = None
+        assert run(outs=o) == kvc.KVC_ERR_INVALID_ARG
+    assert run(q=None) == kvc.KVC_ERR_INVALID_ARG
+    m = kvc.kvc_chunked_workspace_size(p, 512, 30)
+    assert run(budget=30, ws_bytes=m) == kvc.KVC_ERR_INVALID_ARG   # the first evicting boundary fails
+    assert "chunk 0" in lib.kvc_last_error().decode()

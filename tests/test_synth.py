@@ -58,3 +58,17 @@ def test_hetero_stabilities():
     x = layer_inputs(cfg, 5)
     assert x.s_stable.shape == (8,)
     assert np.all((x.s_stable >= 0.2) & (x.s_stable < 0.9))
+
+
+def test_chunk_windows_end_with_the_layer_window():
+    from synth import chunk_windows
+    cfg = get_config("tiny")
+    x = layer_inputs(cfg, 0)
+    a = chunk_windows(cfg, 200, 0)
+    b = chunk_windows(cfg, 200, 0, q_last=x.q)
+    n = (cfg.s + 199) // 200
+    assert a.shape == (n * cfg.w, cfg.hq, cfg.d) and a.dtype == np.uint16
+    np.testing.assert_array_equal(a, b)                  # deterministic, and Q is the layer's
+    np.testing.assert_array_equal(a[-cfg.w:], x.q)
+    assert not np.array_equal(a[:cfg.w], a[cfg.w:2 * cfg.w])
+    assert not np.array_equal(a[:cfg.w], chunk_windows(cfg, 200, 1)[:cfg.w])
