@@ -61,6 +61,18 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
+class PrefillDesc(ctypes.Structure):
+    """kvc_prefill_desc: one layer's attention shape and rotary base."""
+    _fields_ = [
+        ("s", ctypes.c_int64),
+        ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("scale", ctypes.c_float),
+    ]
+
+
 def make_desc(s, w, hq, hkv, d, block=256, scale=0.0, n_sink=0, n_recent=0, pool=1,
               pos_offset=0, q_strides=(0, 0), k_strides=(0, 0), v_strides=(0, 0),
               score_mode=0) -> LayerDesc:
@@ -88,6 +100,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(LayerDesc)
+    PD = ctypes.POINTER(PrefillDesc)
     sig = {
         "kvc_version": (ctypes.c_int, []),
         "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -106,6 +119,10 @@ def _load():
         "kvc_evict_chunk": (ctypes.c_int, [D, P, P, P, I32, I64, I64, P, P, P, P, P, P, P, SZ, P]),
         "kvc_chunked_workspace_size": (SZ, [D, I64, I32]),
         "kvc_compress_chunked": (ctypes.c_int, [D, I64, P, P, P, I32, P, P, P, P, SZ, P]),
+        "kvc_rmsnorm": (ctypes.c_int, [P, P, P, I64, I32, ctypes.c_float, P]),
+        "kvc_rope_append": (ctypes.c_int, [PD, P, I64, I64, P, P, P, P]),
+        "kvc_chunk_attention": (ctypes.c_int, [PD, P, P, P, I64, I64, P, P]),
+        "kvc_swiglu": (ctypes.c_int, [P, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -363,6 +380,34 @@ class PreparedChunked:
     def kvc_compress_chunked(self, stream=None):
         st = ctypes.c_void_p(stream) if stream is not None else _stream()
         _check(self._L.kvc_compress_chunked(*self._args, st))
+
+
+# ------------------------------------------------------------------ prefill layer pieces
+
+def kvc_rmsnorm(x, w, y, eps=1e-5):
+    """x, y [rows, dim] bf16 (y may be x); w [dim]."""
+    rows, dim = x.shape
+    _check(_load().kvc_rmsnorm(_bf16_ptr(x, "x"), _bf16_ptr(w, "w"), _bf16_ptr(y, "y"), rows, dim, eps, _stream()))
+
+
+def kvc_rope_append(pdesc, qkv, c0, q_out, k_cache, v_cache):
+    """qkv [n, (hq + 2 hkv) d]; q_out [n, hq, d]; caches [s, hkv, d]."""
+    _check(_load().kvc_rope_append(ctypes.byref(pdesc), _bf16_ptr(qkv, "qkv"), int(c0), qkv.shape[0],
+                                   _bf16_ptr(q_out, "q_out"), _bf16_ptr(k_cache, "k_cache"),
+                                   _bf16_ptr(v_cache, "v_cache"), _stream()))
+
+
+def kvc_chunk_attention(pdesc, q, k_cache, v_cache, c0, o_out):
+    """q, o_out [n, hq, d] at positions c0 + t; caches [s, hkv, d]."""
+    _check(_load().kvc_chunk_attention(ctypes.byref(pdesc), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                       _bf16_ptr(v_cache, "v_cache"), int(c0), q.shape[0],
+                                       _bf16_ptr(o_out, "o_out"), _stream()))
+
+
+def kvc_swiglu(gu, a):
+    """gu [rows, 2 ffn] -> a [rows, ffn]."""
+    rows, two_f = gu.shape
+    _check(_load().kvc_swiglu(_bf16_ptr(gu, "gu"), _bf16_ptr(a, "a"), rows, two_f // 2, _stream()))
 
 
 # ------------------------------------------------------------------ convenience

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "kvc_internal.h"
+#include "prefill_internal.h"
 
 using namespace kvc;
 
@@ -558,6 +559,8 @@ int aux_stream(int j, hipStream_t& out) {
 }  // namespace
 
 namespace kvc {
+
+int record_error(int status, const char* msg) { return fail(status, "%s", msg); }
 
 hipError_t ensure_lds(const void* fn, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;

@@ -3,6 +3,7 @@ declared symbol, descriptors and budgets are validated before any launch,
 the workspace bound, and the heterogeneous-budget host function against the
 oracle."""
 import ctypes
+import glob
 import os
 import re
 
@@ -14,20 +15,24 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvc.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = kvc.lib()
-    names = declared_functions()
-    assert len(names) >= 10
-    for n in names:
-        assert hasattr(lib, n), f"{n} declared in kvc.h but not exported"
+    assert len(HEADERS) >= 2
+    for header in HEADERS:
+        names = declared_functions(header)
+        assert len(names) >= 4
+        for n in names:
+            assert hasattr(lib, n), f"{n} declared in {os.path.basename(header)} but not exported"
+    assert len(declared_functions()) >= 10
     assert kvc.kvc_version() == 1
 
 
@@ -322,3 +327,41 @@ def test_chunk_eviction_rejects_bad_arguments_before_launch():
     m = kvc.kvc_chunked_workspace_size(p, 512, 30)
     assert run(budget=30, ws_bytes=m) == kvc.KVC_ERR_INVALID_ARG   # the first evicting boundary fails
     assert "chunk 0" in lib.kvc_last_error().decode()
+
+
+def test_prefill_pieces_reject_bad_arguments_before_launch():
+    lib = kvc.lib()
+    good = [_fake(0x10000 + 0x1000 * i) for i in range(6)]
+    pd = kvc.PrefillDesc(s=4096, hq=32, hkv=8, d=128, rope_base=500000.0, scale=0.0)
+    def P(d):
+        return None if d is None else ctypes.byref(d)
+
+    def rope(desc=pd, c0=0, n=16, ptrs=good[:4]):
+        return lib.kvc_rope_append(P(desc), ptrs[0], c0, n, ptrs[1], ptrs[2], ptrs[3], None)
+
+    def attn(desc=pd, c0=0, n=16, ptrs=good[:4]):
+        return lib.kvc_chunk_attention(P(desc), ptrs[0], ptrs[1], ptrs[2], c0, n, ptrs[3], None)
+
+    for call in (rope, attn):
+        assert call(c0=4090, n=16) == kvc.KVC_ERR_INVALID_ARG     # past the cache
+        assert call(c0=-1) == kvc.KVC_ERR_INVALID_ARG
+        for j in range(4):
+            p = list(good[:4])
+            p[j] = None
+            assert call(ptrs=p) == kvc.KVC_ERR_INVALID_ARG
+            p[j] = _fake(0x10008)
+            assert call(ptrs=p) == kvc.KVC_ERR_ALIGN
+        for kw, val, st in [("hq", 30, kvc.KVC_ERR_INVALID_ARG), ("hq", 48, kvc.KVC_ERR_UNSUPPORTED),
+                            ("d", 96, kvc.KVC_ERR_UNSUPPORTED), ("rope_base", 0.0, kvc.KVC_ERR_INVALID_ARG),
+                            ("s", 0, kvc.KVC_ERR_INVALID_ARG), ("scale", float("inf"), kvc.KVC_ERR_INVALID_ARG)]:
+            bad = kvc.PrefillDesc(s=pd.s, hq=pd.hq, hkv=pd.hkv, d=pd.d, rope_base=pd.rope_base, scale=pd.scale)
+            setattr(bad, kw, val)
+            assert call(desc=bad) == st, (kw, val)
+        assert call(desc=None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_rmsnorm(good[0], good[1], good[2], 4, 100, 1e-5, None) == kvc.KVC_ERR_INVALID_ARG  # dim % 8
+    assert lib.kvc_rmsnorm(good[0], good[1], good[2], -1, 128, 1e-5, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_rmsnorm(good[0], None, good[2], 4, 128, 1e-5, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_rmsnorm(good[0], good[1], good[2], 4, 128, -1.0, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_swiglu(good[0], good[1], 4, 100, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_swiglu(good[0], _fake(0x10004), 4, 128, None) == kvc.KVC_ERR_ALIGN
+    assert "16-byte" in lib.kvc_last_error().decode()
