@@ -13,6 +13,9 @@ from .gen import (
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     chunk_windows,
+    SynthLayerWeights,
+    model_weights,
+    prompt_hidden,
 )
 
 __all__ = [
@@ -25,4 +28,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "chunk_windows",
+    "SynthLayerWeights",
+    "model_weights",
+    "prompt_hidden",
 ]

@@ -138,3 +138,41 @@ def chunk_windows(cfg: LayerConfig, chunk: int, layer: int = 0, q_last: np.ndarr
     parts = [_normal_bf16(kids[b], (cfg.w, cfg.hq, cfg.d)) for b in range(n_chunks - 1)]
     parts.append(np.ascontiguousarray(q_last, dtype=np.uint16))
     return np.concatenate(parts, axis=0)
+
+
+@dataclass
+class SynthLayerWeights:
+    """bf16 bit patterns of one decoder layer (layouts: w_qkv [(hq + 2 hkv) d,
+    hidden], w_o [hidden, hq d], w_gu [2 ffn, hidden], w_down [hidden, ffn],
+    norm weights [hidden])."""
+    w_attn: np.ndarray
+    w_qkv: np.ndarray
+    w_o: np.ndarray
+    w_mlp: np.ndarray
+    w_gu: np.ndarray
+    w_down: np.ndarray
+
+
+def model_weights(hidden: int, hq: int, hkv: int, d: int, ffn: int, layers: int, seed: int):
+    """Random decoder weights: projections N(0, 1/fan_in), norm weights
+    1 + N(0, 0.01), each drawn as float32 and rounded to bf16; layer l's six
+    tensors come from children of the seed sequence [seed, 2, l]."""
+    out = []
+    for l in range(layers):
+        kids = np.random.SeedSequence([seed, 2, l]).spawn(6)
+
+        def draw(k, shape, scale, shift=0.0):
+            rng = np.random.Generator(np.random.PCG64(kids[k]))
+            return f32_to_bf16_bits((rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+                                     + np.float32(shift)).astype(np.float32))
+
+        out.append(SynthLayerWeights(
+            w_attn=draw(0, (hidden,), 0.1, 1.0), w_qkv=draw(1, ((hq + 2 * hkv) * d, hidden), hidden ** -0.5),
+            w_o=draw(2, (hidden, hq * d), (hq * d) ** -0.5), w_mlp=draw(3, (hidden,), 0.1, 1.0),
+            w_gu=draw(4, (2 * ffn, hidden), hidden ** -0.5), w_down=draw(5, (hidden, ffn), ffn ** -0.5)))
+    return out
+
+
+def prompt_hidden(s: int, hidden: int, seed: int) -> np.ndarray:
+    """Synthetic prompt hidden states [s, hidden]: N(0, 1) rounded to bf16."""
+    return _normal_bf16(np.random.SeedSequence([seed, 3]), (s, hidden))
