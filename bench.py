@@ -194,6 +194,56 @@ def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
     return out
 
 
+def layer_major_prefill(kvc, torch, dev, s=65536, chunk=2048, w=32, budget=4096):
+    """The compressor inside the schedule it serves: a random-weight
+    Llama-3.1-8B-shaped stack (32 layers) prefilled layer-major in chunks with
+    layer-end eviction, against the same prefill without compression and
+    against keeping every layer's full K/V until the end (then compressing).
+    One warm and one timed run of each; HIP events around the timed run."""
+    from compression_kvc_score_amd import prefill as pf
+    cfg = pf.ModelConfig()
+    model = pf.SyntheticModel(cfg, device=dev, seed=1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    x0 = torch.randn((s, cfg.hidden), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    budgets = [budget] * cfg.hkv
+    out = {"s": s, "chunk": chunk, "w": w, "budget_per_head": budget, "layers": cfg.layers,
+           "model": "Llama-3.1-8B geometry, random bf16 weights", "weights_bytes": model.nbytes()}
+    for name, kw in [("layer_major_evict", dict(overlap=True)),
+                     ("layer_major_no_compression", dict(compress=False)),
+                     ("full_kv_then_compress", dict(keep_full_kv=True))]:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        drv = pf.LayerMajorPrefill(model, s, chunk, w, budgets, 4, 32, device=dev, **kw)
+        x = x0.clone()
+        drv.run(x)
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        drv.run(x)
+        e1.record()
+        torch.cuda.synchronize()
+        rep = drv.acct.report()
+        out[name] = {"ttft_ms": round(e0.elapsed_time(e1), 2),
+                     "layer_ms": round(float(np.mean([a.elapsed_time(b) for a, b, _ in drv.layer_events])), 3),
+                     "allocator_peak_bytes": int(rep["allocator_peak_bytes"]),
+                     "resident_at_peak": {k: int(v) for k, v in rep["peak_parts"].items() if k != "weights"}}
+        log(f"layer-major prefill {name}: {out[name]['ttft_ms']:.1f} ms for {cfg.layers} layers of {s} tokens "
+            f"({out[name]['layer_ms']:.2f} ms per layer); allocator peak beyond the weights and prompt "
+            f"{rep['allocator_peak_bytes'] / 2**30:.3f} GiB")
+        if name == "layer_major_evict":
+            out["final_cache_bytes"] = int(drv.cache.k.numel() * 2 + drv.cache.v.numel() * 2)
+        del drv, x
+    ev, base = out["layer_major_evict"]["ttft_ms"], out["layer_major_no_compression"]["ttft_ms"]
+    out["compression_overhead_frac"] = round((ev - base) / base, 5)
+    out["transient_reduction_frac"] = round(
+        1 - out["layer_major_evict"]["allocator_peak_bytes"] / out["full_kv_then_compress"]["allocator_peak_bytes"], 4)
+    del model, x0
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +253,8 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=0, help="distinct resident layers (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle baseline sample length in seconds (0: skip)")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="skip the layer-major prefill run (random-weight model around the compressor)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (to calibrate HBM byte counters)")
     args = ap.parse_args(argv)
@@ -405,6 +457,7 @@ def main(argv=None):
     # keys, each against the one-shot layer-end compressor on the same tensors
     imm_detail = {name: immediate_eviction(kvc, torch, dev, name, max(4, K // 4), sp, stream)
                   for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
+    prefill_detail = layer_major_prefill(kvc, torch, dev, s=cfg.s) if args.prefill else None
 
     ms_per_step = wall * 1e3 / K
     value = cfg.s * K / wall
@@ -451,6 +504,7 @@ def main(argv=None):
                                   "HIP events around one kvc_compress_layer call"},
         "score_modes": mode_detail,
         "immediate_eviction": imm_detail,
+        "layer_major_prefill": prefill_detail,
         "sweep": {
             "entry_point": "kvc_compress_layers", "layers_in_flight": kvc.SWEEP_STREAMS,
             "value": round(cfg.s * K / sweep_wall, 1), "unit": "tokens/s",

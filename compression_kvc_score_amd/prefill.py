@@ -30,7 +30,7 @@ whole prompt is done, then all layers are compressed.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -139,13 +139,6 @@ class RetainedCacheManager:
         return nbytes(self.k, self.v, self.pos)
 
 
-@dataclass
-class PrefillTimes:
-    total_ms: float = 0.0
-    layer_ms: list = field(default_factory=list)
-    commit_ms: list = field(default_factory=list)
-
-
 class LayerMajorPrefill:
     """Layer-major chunked prefill with layer-end eviction (see the module
     docstring). ``run(x)`` takes the prompt's hidden states [S, hidden] bf16
@@ -153,14 +146,14 @@ class LayerMajorPrefill:
 
     def __init__(self, model: SyntheticModel, s: int, chunk: int, w: int, budgets, n_sink: int, n_recent: int,
                  block: int = 256, overlap: bool = True, keep_full_kv: bool = False, device="cuda",
-                 accountant: MemoryAccountant | None = None):
+                 accountant: MemoryAccountant | None = None, compress: bool = True):
         import torch
         c = model.cfg
         if chunk < 1 or w < 1 or w > s:
             raise ValueError("need chunk >= 1 and 1 <= w <= s")
         self.model, self.cfg, self.s, self.chunk, self.w = model, c, s, chunk, w
         self.n_sink, self.n_recent, self.block = n_sink, n_recent, block
-        self.overlap, self.keep_full_kv = overlap, keep_full_kv
+        self.overlap, self.keep_full_kv, self.compress = overlap, keep_full_kv, compress
         self.acct = accountant or MemoryAccountant()
         self.acct.hold("weights", model.nbytes())
         self.pdesc = L.PrefillDesc(s=s, hq=c.hq, hkv=c.hkv, d=c.d, rope_base=c.rope_base, scale=0.0)
@@ -236,7 +229,7 @@ class LayerMajorPrefill:
             self._chunk(self.model.layers[l], x[c0:c1], c0, k, v, q_win)
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(main)
-        if self.keep_full_kv:
+        if self.keep_full_kv or not self.compress:
             return e0, e1, None
         ws = self.ws[i % len(self.ws)]
         if self.commit_stream is not None:
@@ -258,10 +251,11 @@ class LayerMajorPrefill:
         import torch
         main = torch.cuda.current_stream()
         self.acct.hold("bridge", nbytes(x))
+        self.kv_free = [None] * len(self.kv)
         self.layer_events = []
         for l in range(self.cfg.layers):
             self.layer_events.append(self.run_layer(l, x))
-        if self.keep_full_kv:
+        if self.keep_full_kv and self.compress:
             # post-prefill compression of every layer (Fig. 1 (b) then compression)
             for l in range(self.cfg.layers):
                 k, v = self.kv[l]
@@ -270,4 +264,5 @@ class LayerMajorPrefill:
             for ev in self.kv_free:
                 if ev is not None:
                     main.wait_event(ev)
+        self.acct.release("bridge")
         return self.cache
