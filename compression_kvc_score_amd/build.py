@@ -34,6 +34,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions. The chunk attention keeps its output accumulators in
+# ordinary VGPRs (the MFMA's VGPR form): with accumulation registers the
+# compiler copies them to VGPRs and back around the softmax rescale.
+EXTRA_FLAGS = {
+    "prefill_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = shutil.which("hipcc") or os.path.join(rocm, "bin", "hipcc")
@@ -54,7 +62,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in line)

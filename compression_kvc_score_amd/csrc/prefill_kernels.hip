@@ -154,9 +154,14 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluArgs a) {
 // online softmax in base 2, and accumulates O^T = V^T . P^T: the B operand is
 // P straight from the registers (k-slot j of lane half `half` in k-slice s is
 // the key 16s + 8(j/4) + 4 half + j%4 held in register 8s + j), the A operand
-// reads V from LDS in that same key order. Tiles are double-buffered through
-// registers and LDS; the causal mask is applied on tiles that reach past the
-// workgroup's first query. Workgroups with the most keys start first.
+// reads V^T from LDS in that same key order: V is staged transposed
+// ([d][key], rows padded to 36 keys), so each lane's eight keys are two
+// 8-byte reads. Tiles are double-buffered through registers and LDS; the
+// causal mask is applied on tiles that reach past the workgroup's first
+// query. The running max is only raised when a tile's max exceeds it by more
+// than 8 in base-2 units (weights up to 2^8 stay exact in fp32 and bf16), so
+// most tiles skip rescaling the output accumulators; lanes that do not raise
+// it scale by exactly 1. Workgroups with the most keys start first.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -168,10 +173,11 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int NST = D / 16;       // MFMA k-steps over D
   constexpr int DT = D / 32;        // 32-row tiles of O^T
   constexpr int PITCH = D + 8;      // +16 B per row: row-strided b128 reads stay conflict free
+  constexpr int VP = 36;            // keys per row of V^T (18 dwords: 16 rows of 8-byte reads hit 32 banks)
   constexpr int NT = 64 * G;
   constexpr int PER = (32 * CH + NT - 1) / NT;  // staged chunks per thread per matrix
   __shared__ __align__(16) uint16_t ks[2][32 * PITCH];
-  __shared__ __align__(16) uint16_t vs[2][32 * PITCH];
+  __shared__ __align__(16) uint16_t vt[2][D * VP];
 
   const int g = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;
@@ -193,46 +199,54 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
     for (int st = 0; st < NST; ++st) qf[st] = *reinterpret_cast<const bf16x8_t*>(qrow + 8 * st);
   }
 
-  uint4 kreg[PER], vreg[PER];
+  // two register sets: tile kt + 2 loads while tile kt is computed, so a
+  // load has two tiles of work to land before its store to LDS
+  // (passed by value: an array behind a reference would be moved to LDS)
+  struct TileRegs {
+    uint4 k[PER], v[PER];
+  };
   auto load_tile = [&](int kt) {
+    TileRegs r;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = threadIdx.x + j * NT;
       if (u < 32 * CH) {
-        int64_t key = (int64_t)kt * 32 + u / CH;
+        // 16 keys per wavefront, each key row read in runs of 64 bytes
+        int64_t key = (int64_t)kt * 32 + u % 16 + 16 * (u / (16 * CH));
         key = key < kmax ? key : kmax;
-        const int64_t off = key * tok + (int64_t)g * D + (u % CH) * 8;
-        kreg[j] = *reinterpret_cast<const uint4*>(a.k + off);
-        vreg[j] = *reinterpret_cast<const uint4*>(a.v + off);
+        const int64_t off = key * tok + (int64_t)g * D + ((u / 16) % CH) * 8;
+        r.k[j] = *reinterpret_cast<const uint4*>(a.k + off);
+        r.v[j] = *reinterpret_cast<const uint4*>(a.v + off);
       }
     }
+    return r;
   };
-  auto store_tile = [&](int b) {
+  auto store_tile = [&](int b, TileRegs r) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = threadIdx.x + j * NT;
       if (u < 32 * CH) {
-        const int o = (u / CH) * PITCH + (u % CH) * 8;
-        *reinterpret_cast<uint4*>(&ks[b][o]) = kreg[j];
-        *reinterpret_cast<uint4*>(&vs[b][o]) = vreg[j];
+        const int key = u % 16 + 16 * (u / (16 * CH)), c = (u / 16) % CH;
+        *reinterpret_cast<uint4*>(&ks[b][key * PITCH + c * 8]) = r.k[j];
+        const uint32_t w[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
+        uint16_t* col = &vt[b][(c * 8) * VP + key];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          col[(2 * i) * VP] = (uint16_t)(w[i] & 0xFFFFu);
+          col[(2 * i + 1) * VP] = (uint16_t)(w[i] >> 16);
+        }
       }
     }
   };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
 
   float m = -INFINITY, l = 0.f;
+  const float thr = 8.0f / a.c;  // lag of the running max allowed, in raw dot units
   f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto compute = [&](int kt) {
     const int b = kt & 1;
-    const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);
-
     f32x16_t s = {};
     const uint16_t* kr = &ks[b][l32 * PITCH + half * (D / 2)];
 #pragma unroll
@@ -249,10 +263,18 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
     float tmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);  // finite: key 0 is seen by every query
-    const float corr = __builtin_amdgcn_exp2f((m - mn) * a.c);
-    const float mc = mn * a.c;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // finite: key 0 is seen by every query
+    const bool up = tmax > m + thr;            // always on the first tile (m = -inf)
+    if (__ballot(up) != 0) {
+      const float corr = up ? __builtin_amdgcn_exp2f((m - tmax) * a.c) : 1.0f;
+      m = up ? tmax : m;
+      l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+    }
+    const float mc = m * a.c;
     float psum = 0.f;
     float p[16];
 #pragma unroll
@@ -260,12 +282,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
       p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mc));
       psum += p[r];
     }
-    l = fmaf(l, corr, psum);
-    m = mn;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
+    l += psum;
 
 #pragma unroll
     for (int ks_ = 0; ks_ < 2; ++ks_) {
@@ -274,17 +291,30 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
       for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * ks_ + j];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        bf16x8_t va;
-        const uint16_t* vcol = &vs[b][dt * 32 + l32];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = 16 * ks_ + 8 * (j >> 2) + 4 * half + (j & 3);
-          va[j] = __builtin_bit_cast(__bf16, vcol[key * PITCH]);
-        }
+        const uint16_t* vrow = &vt[b][(dt * 32 + l32) * VP + 16 * ks_ + 4 * half];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);      // keys 16s + 4 half + 0..3
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);  // keys 16s + 8 + 4 half + 0..3
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[dt] = mfma32(va, pb, o[dt]);
       }
     }
-    if (more) store_tile(b ^ 1);
+  };
+
+  // tile kt + 1 is in one register set, the other is free for tile kt + 2;
+  // tiles past the end load clamped rows and are never read
+  TileRegs rA = load_tile(0);
+  TileRegs rB = load_tile(1);
+  store_tile(0, rA);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    rA = load_tile(kt + 2);
+    compute(kt);
+    store_tile((kt + 1) & 1, rB);
+    __syncthreads();
+    if (kt + 1 >= n_kt) break;
+    rB = load_tile(kt + 3);
+    compute(kt + 1);
+    store_tile(kt & 1, rA);
     __syncthreads();
   }
 
