@@ -235,6 +235,31 @@ def layer_major_prefill(kvc, torch, dev, s=65536, chunk=2048, w=32, budget=4096)
         if name == "layer_major_evict":
             out["final_cache_bytes"] = int(drv.cache.k.numel() * 2 + drv.cache.v.numel() * 2)
         del drv, x
+    # the chunk attention kernel alone against the bf16 MFMA peak: the last
+    # 2048-token chunk of the prompt over the whole layer's K/V (random rows)
+    pdesc = kvc.PrefillDesc(s=s, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, rope_base=cfg.rope_base, scale=0.0)
+    kc = torch.randn((s, cfg.hkv, cfg.d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn((s, cfg.hkv, cfg.d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((chunk, cfg.hq, cfg.d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    c0 = s - chunk
+    kvc.kvc_chunk_attention(pdesc, q, kc, vc, c0, o)
+    torch.cuda.synchronize()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kvc.kvc_chunk_attention(pdesc, q, kc, vc, c0, o)
+    e1.record()
+    torch.cuda.synchronize()
+    att_ms = e0.elapsed_time(e1) / reps
+    keys = sum(c0 + t + 1 for t in range(chunk))      # causal (query, key) pairs per head
+    flops = 4.0 * cfg.hq * cfg.d * keys                # QK^T and PV
+    out["chunk_attention"] = {"c0": c0, "n": chunk, "us": round(att_ms * 1e3, 1), "tflops": round(flops / att_ms / 1e9, 1),
+                              "mfma_frac": round(flops / att_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"chunk attention (last {chunk} queries over {s} keys): {att_ms * 1e3:.0f} us, "
+        f"{flops / att_ms / 1e9:.0f} TFLOP/s ({out['chunk_attention']['mfma_frac'] * 100:.1f}% of the bf16 MFMA peak)")
+    del kc, vc, q, o
     ev, base = out["layer_major_evict"]["ttft_ms"], out["layer_major_no_compression"]["ttft_ms"]
     out["compression_overhead_frac"] = round((ev - base) / base, 5)
     out["transient_reduction_frac"] = round(

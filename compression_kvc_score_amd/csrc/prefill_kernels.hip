@@ -176,6 +176,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int VP = 36;            // keys per row of V^T (18 dwords: 16 rows of 8-byte reads hit 32 banks)
   constexpr int NT = 64 * G;
   constexpr int PER = (32 * CH + NT - 1) / NT;  // staged chunks per thread per matrix
+  constexpr bool FULL = (32 * CH) % NT == 0;    // every thread stages PER chunks (no guard)
   __shared__ __align__(16) uint16_t ks[2][32 * PITCH];
   __shared__ __align__(16) uint16_t vt[2][D * VP];
 
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = threadIdx.x + j * NT;
-      if (u < 32 * CH) {
+      if (FULL || u < 32 * CH) {
         // 16 keys per wavefront, each key row read in runs of 64 bytes
         int64_t key = (int64_t)kt * 32 + u % 16 + 16 * (u / (16 * CH));
         key = key < kmax ? key : kmax;
@@ -225,7 +226,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = threadIdx.x + j * NT;
-      if (u < 32 * CH) {
+      if (FULL || u < 32 * CH) {
         const int key = u % 16 + 16 * (u / (16 * CH)), c = (u / 16) % CH;
         *reinterpret_cast<uint4*>(&ks[b][key * PITCH + c * 8]) = r.k[j];
         const uint32_t w[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
