@@ -108,6 +108,34 @@ def cpu_baseline(cfg, host_layers, budgets_of, seconds: float):
     }
 
 
+def cpu_baseline_one_thread(cfg, host_layers, budgets_of, seconds: float):
+    """The same oracle sample with the BLAS pool limited to one thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        r = cpu_baseline(cfg, host_layers, budgets_of, seconds)
+    r["cores"] = 1
+    return r
+
+
+def achievable_hbm_gbs(torch, dev) -> float:
+    """Read + write bandwidth of a 1 GiB device-to-device copy (the achievable
+    streaming rate on this machine, beside the 8 TB/s spec peak)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
 def copy_probe():
     """A device-to-device copy of exactly 256 MiB, five times: the reference a
     profiler's fetch/write byte counters are scaled against."""
@@ -484,6 +512,9 @@ def main(argv=None):
                   for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
     prefill_detail = layer_major_prefill(kvc, torch, dev, s=cfg.s) if args.prefill else None
 
+    copy_gbs = achievable_hbm_gbs(torch, dev)
+    log(f"device copy of 1 GiB: {copy_gbs:.0f} GB/s read + write")
+
     ms_per_step = wall * 1e3 / K
     value = cfg.s * K / wall
 
@@ -517,6 +548,9 @@ def main(argv=None):
         "staged_step_us": round(staged_ms * 1e3, 2),
         "layer_alg_bytes": total_alg,
         "layer_hbm_frac": round(total_alg / (step_gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbs": round(copy_gbs, 1),
+        "layer_frac_of_copy_rate": round(total_alg / (step_gpu_ms * 1e-3) / 1e9 / copy_gbs, 4),
+        "roofline_kernel_frac_of_copy_rate": round(achieved / copy_gbs, 4),
         "evicted_tokens_per_s": round((cfg.s - cfg.budget) * K / wall, 1),
         "pass_mfma_tflops": {n: round(mfma_flops(cfg) / (stage_ms[n] * 1e-3) / 1e12, 1)
                              for n in ("pass1", "pass2")},
@@ -544,6 +578,9 @@ def main(argv=None):
         log(f"CPU oracle baseline (about {args.cpu_seconds:.0f} s) ...")
         cpu = cpu_baseline(cfg, host_layers, [l[3] for l in layers], args.cpu_seconds)
         log(f"CPU oracle: {cpu['value']:.1f} tokens/s with {cpu['cores']} BLAS threads; {cpu['sample']}")
+        cpu1 = cpu_baseline_one_thread(cfg, host_layers, [l[3] for l in layers], max(2.0, args.cpu_seconds / 3))
+        extras["cpu_baseline_one_thread"] = cpu1
+        log(f"CPU oracle, one thread: {cpu1['value']:.1f} tokens/s; {cpu1['sample']}")
 
     line = {
         "metric": METRIC,
