@@ -464,6 +464,29 @@ def main(argv=None):
     log("staged breakdown (back-to-back batches): " + ", ".join(f"{n} {stage_ms[n] * 1e3:.1f} us" for n in stage_names)
         + f" (sum {staged_ms * 1e3:.1f} us)")
 
+    # ---- the two scans in the order the layer runs them: per layer pass 1,
+    # pass 2, select, gather, with HIP events between the calls, so each scan
+    # sees the cache state it has inside a layer (pass 2 right after pass 1
+    # read the same K); the event span also holds the scan's dispatch gap
+    ctx_ev = {"pass1": [], "pass2": []}
+    for i in range(K + 1):
+        p = prepared[i % n_layers]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        marks[0].record(stream)
+        p.kvc_score_pass1(sp)
+        marks[1].record(stream)
+        p.kvc_score_pass2(sp)
+        marks[2].record(stream)
+        p.kvc_select_topk(sp)
+        p.kvc_gather_retained(sp)
+        if i > 0:  # the first layer is a warm-up
+            ctx_ev["pass1"].append((marks[0], marks[1]))
+            ctx_ev["pass2"].append((marks[1], marks[2]))
+    torch.cuda.synchronize()
+    ctx_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in evs])) for n, evs in ctx_ev.items()}
+    log(f"scans in layer order (events between calls): pass1 {ctx_ms['pass1'] * 1e3:.1f} us, "
+        f"pass2 {ctx_ms['pass2'] * 1e3:.1f} us")
+
     # ---- the raw inner-product score modes on the same layers: the warm
     # whole-layer loop, their one-pass scan (K back-to-back kvc_score_pass2
     # calls) against the HBM peak, and how much their retained sets overlap
@@ -544,6 +567,7 @@ def main(argv=None):
     total_alg = sum(alg.values())
     extras = {
         "stage_us": {n: round(stage_ms[n] * 1e3, 2) for n in stage_names},
+        "scan_us_in_layer_order": {n: round(ctx_ms[n] * 1e3, 2) for n in ctx_ms},
         "step_gpu_us": round(step_gpu_ms * 1e3, 2),
         "staged_step_us": round(staged_ms * 1e3, 2),
         "layer_alg_bytes": total_alg,
