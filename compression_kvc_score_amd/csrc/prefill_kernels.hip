@@ -155,8 +155,8 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluArgs a) {
 // P straight from the registers (k-slot j of lane half `half` in k-slice s is
 // the key 16s + 8(j/4) + 4 half + j%4 held in register 8s + j), the A operand
 // reads V^T from LDS in that same key order: V is staged transposed
-// ([d][key], rows padded to 36 keys), so each lane's eight keys are two
-// 8-byte reads. Tiles are double-buffered through registers and LDS; the
+// ([d][key slot], rows padded to 40 slots) with the keys of each lane half's
+// k-slice adjacent, so each lane's eight keys are one 16-byte read. Tiles are double-buffered through registers and LDS; the
 // causal mask is applied on tiles that reach past the workgroup's first
 // query. The running max is only raised when a tile's max exceeds it by more
 // than 8 in base-2 units (weights up to 2^8 stay exact in fp32 and bf16), so
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int NST = D / 16;       // MFMA k-steps over D
   constexpr int DT = D / 32;        // 32-row tiles of O^T
   constexpr int PITCH = D + 8;      // +16 B per row: row-strided b128 reads stay conflict free
-  constexpr int VP = 36;            // keys per row of V^T (18 dwords: 16 rows of 8-byte reads hit 32 banks)
+  constexpr int VP = 40;            // key slots per row of V^T (80 bytes: rows stay 16-byte aligned)
   constexpr int NT = 64 * G;
   constexpr int PER = (32 * CH + NT - 1) / NT;  // staged chunks per thread per matrix
   constexpr bool FULL = (32 * CH) % NT == 0;    // every thread stages PER chunks (no guard)
@@ -229,13 +229,33 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
       if (FULL || u < 32 * CH) {
         const int key = u % 16 + 16 * (u / (16 * CH)), c = (u / 16) % CH;
         *reinterpret_cast<uint4*>(&ks[b][key * PITCH + c * 8]) = r.k[j];
-        const uint32_t w[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
-        uint16_t* col = &vt[b][(c * 8) * VP + key];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          col[(2 * i) * VP] = (uint16_t)(w[i] & 0xFFFFu);
-          col[(2 * i + 1) * VP] = (uint16_t)(w[i] >> 16);
+        // The four lanes of a quad hold keys k0..k0+3 (same eight d values):
+        // transpose their 4x4 dwords across the quad (two DPP swap steps) so
+        // that lane q holds d values 2q, 2q + 1 of all four keys, then write
+        // two 8-byte rows of V^T.
+        uint32_t w[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
+        const int q = threadIdx.x & 3;
+        {
+          const uint32_t s0 = (q & 1) ? w[0] : w[1], s1 = (q & 1) ? w[2] : w[3];
+          const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, false);
+          const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
+          if (q & 1) { w[0] = r0; w[2] = r1; } else { w[1] = r0; w[3] = r1; }
         }
+        {
+          const uint32_t s0 = (q & 2) ? w[0] : w[2], s1 = (q & 2) ? w[1] : w[3];
+          const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x4E, 0xF, 0xF, false);
+          const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x4E, 0xF, 0xF, false);
+          if (q & 2) { w[0] = r0; w[1] = r1; } else { w[2] = r0; w[3] = r1; }
+        }
+        const int k0 = key & ~3;
+        // key slot of k0 in a V^T row: keys 16s + 8a + 4h + i sit at 16s + 8h + 4a + i,
+        // so the eight keys a lane half feeds one MFMA k-slice are adjacent
+        const int slot = (k0 & ~15) | (((k0 >> 2) & 1) << 3) | (((k0 >> 3) & 1) << 2);
+        uint16_t* row = &vt[b][(c * 8 + 2 * q) * VP + slot];
+        *reinterpret_cast<uint2*>(row) =
+            make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+        *reinterpret_cast<uint2*>(row + VP) =
+            make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
       }
     }
   };
@@ -292,10 +312,9 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
       for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * ks_ + j];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vrow = &vt[b][(dt * 32 + l32) * VP + 16 * ks_ + 4 * half];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);      // keys 16s + 4 half + 0..3
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);  // keys 16s + 8 + 4 half + 0..3
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        // slots 16s + 8 half + 0..7 hold keys 16s + 8(j/4) + 4 half + j%4
+        const bf16x8_t va =
+            *reinterpret_cast<const bf16x8_t*>(&vt[b][(dt * 32 + l32) * VP + 16 * ks_ + 8 * half]);
         o[dt] = mfma32(va, pb, o[dt]);
       }
     }
