@@ -56,9 +56,9 @@ def setup(s=512, chunk=128, w=16, seed=3, **kw):
     return cfg, host_w, x
 
 
-def run_driver(cfg, host_w, x, s, chunk, w, budgets, overlap=True, keep_full_kv=False, per_layer=None):
+def run_driver(cfg, host_w, x, s, chunk, w, budgets, overlap=True, keep_full_kv=False, per_layer=None, block=64):
     model = pf.SyntheticModel(cfg, host_weights=host_w)
-    drv = pf.LayerMajorPrefill(model, s, chunk, w, budgets, 4, 16, block=64, overlap=overlap,
+    drv = pf.LayerMajorPrefill(model, s, chunk, w, budgets, 4, 16, block=block, overlap=overlap,
                                keep_full_kv=keep_full_kv)
     xb = to_dev_bf16(x)
     if per_layer is None:
@@ -169,3 +169,32 @@ def test_chunk_size_changes_only_gemm_rounding():
     _, c_small, b_small = run_driver(cfg, host_w, x, s, 64, w, [32, 32])
     _, c_one, b_one = run_driver(cfg, host_w, x, s, s, w, [32, 32])
     close_in_ulps(b_small, oracle.bf16_to_f64(b_one), "bridge, chunk 64 vs one shot", max_ulps=16, rms_ulps=1.0)
+
+
+def test_llama8b_layer_shape_last_chunk_against_the_oracle():
+    """The Llama-3.1-8B layer shape (hidden 4096, 32/8 heads of 128, FFN
+    14336) through the driver; the last chunk of the layer is recomputed by the
+    oracle from the GPU's own input bridge and K/V of the earlier chunks."""
+    s, chunk, w = 1024, 256, 32
+    cfg = pf.ModelConfig(layers=1)
+    host_w = model_weights(cfg.hidden, cfg.hq, cfg.hkv, cfg.d, cfg.ffn, 1, 11)
+    x = prompt_hidden(s, cfg.hidden, 11)
+    shp = oracle.ModelShape(hidden=cfg.hidden, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, ffn=cfg.ffn, rope_base=cfg.rope_base)
+    got = {}
+
+    def keep(l, before, after, k_bits, v_bits, qw_bits):
+        got.update(before=before, after=after, k=k_bits, v=v_bits, qw=qw_bits)
+
+    say("llama8b layer shape: driver")
+    drv, cache, _ = run_driver(cfg, host_w, x, s, chunk, w, [512] * cfg.hkv, per_layer=keep)
+    c0 = s - chunk
+    kc = oracle.bf16_to_f64(got["k"]).copy()
+    vc = oracle.bf16_to_f64(got["v"]).copy()
+    say("llama8b layer shape: oracle on the last chunk")
+    out, q = oracle.layer_chunk(oracle.bf16_to_f64(got["before"][c0:]), host_w[0], shp, c0, kc, vc)
+    close_in_ulps(got["k"][c0:], kc[c0:], "K rows of the last chunk")
+    close_in_ulps(got["v"][c0:], vc[c0:], "V rows of the last chunk")
+    close_in_ulps(got["qw"], q[chunk - w:], "window queries")
+    close_in_ulps(got["after"][c0:], out, "output rows of the last chunk")
+    # earlier rows of the bridge are the earlier chunks' outputs, untouched by the last chunk
+    assert cache.committed[0]
