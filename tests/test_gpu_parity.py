@@ -411,3 +411,22 @@ def test_full_size_llama8b_128k_pool7_sampled():
 
 def test_full_size_qwen14b_hetero_sampled():
     full_size_case("qwen14b_hetero_64k", 1, heads=[2])
+
+
+# --------------------------------------------------------------------------- the largest prompt
+
+def test_maximum_prompt_length():
+    """S = 2^23, the library's limit (every sub-chunk tag in use): one KV head
+    and two window rows, so the oracle stays cheap; 20000 keys retained."""
+    cfg = get_config("tiny").with_(name="max_prompt", s=1 << 23, w=2, hq=1, hkv=1, d=64, block=256, n_sink=4,
+                                   n_recent=2, n_heavy=2000, budget=20000, sink_scale=4.0, seed_base=888)
+    say("max prompt: generating 2^23 keys")
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev_inputs(x)
+    b = np.array([cfg.budget])
+    desc = desc_from(cfg, q, k, v)
+    say("max prompt: GPU")
+    got = run_fused(desc, q, k, v, b)
+    np.testing.assert_allclose(got["scores"].sum(axis=1, dtype=np.float64), cfg.w * cfg.group, rtol=1e-4)
+    say("max prompt: oracle")
+    check_layer(x, got, b)

@@ -261,3 +261,23 @@ def test_overlap_coefficient_synthetic_sets_both_paths():
     torch.cuda.synchronize()
     want = np.array([oracle.overlap_coefficient(a_sets[g], b_sets[g]) for g in range(hkv)], dtype=np.float32)
     np.testing.assert_array_equal(res.cpu().numpy(), want)
+
+
+def test_logit_mode_at_its_maximum_prompt_length():
+    """S = 2^22, the limit of the signed-score selection: INT8 scores and the
+    selection are exact against the oracle."""
+    cfg = get_config("tiny").with_(name="max_prompt_int8", s=1 << 22, w=2, hq=2, hkv=1, d=64, block=256, n_sink=4,
+                                   n_recent=2, n_heavy=1000, budget=30000, sink_scale=4.0, seed_base=889)
+    say("int8 max prompt: generating 2^22 keys")
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev(x)
+    b = np.array([cfg.budget])
+    desc = desc_from(cfg, q, k, v, score_mode=MODES["int8"])
+    say("int8 max prompt: GPU")
+    got = run_fused(desc, q, k, v, b)
+    want = oracle.logit_scores_int8(x.q, x.k)
+    np.testing.assert_array_equal(got["scores"].astype(np.float64), want.astype(np.float64))
+    np.testing.assert_array_equal(got["idx"], oracle.select_head(want[0].astype(np.float64), cfg.budget, 4, 2))
+    kh, vh, pos = oracle.gather(x.k, x.v, [got["idx"]])
+    np.testing.assert_array_equal(got["k_hat"], kh)
+    np.testing.assert_array_equal(got["pos"], pos)
