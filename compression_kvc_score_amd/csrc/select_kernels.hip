@@ -775,7 +775,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
 #pragma unroll
       for (int i = 0; i < kCopyUnroll; ++i) {
         const int rr = r + i * rpp;
-        if (rr < nr) *reinterpret_cast<u32x4*>(dst + (int64_t)rr * a.d) = buf[i];
+        if (rr < nr) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4*>(dst + (int64_t)rr * a.d));
       }
     }
 #pragma unroll

@@ -597,10 +597,17 @@ __device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr
   float s0 = 0.f, s1 = 0.f;
   if constexpr (NRTW <= 2) {
     f32x16_t acc[2];
+    // the MFMA chains run at raised wave priority, so that the other
+    // wavefront on the SIMD fills the matrix pipe's gaps with its VALU work
+    // instead of both contending for issue
+    __builtin_amdgcn_s_setprio(1);
     acc[0] = contract<D, NRTW, false>(qr, kf, 0);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < NRTW; ++i) {
+      __builtin_amdgcn_s_setprio(1);
       if (i + 1 < NRTW && i + 1 < ntile) acc[(i + 1) & 1] = contract<D, NRTW, false>(qr, kf, i + 1);
+      __builtin_amdgcn_s_setprio(0);
       if (i < ntile) weight_sum<EDGE>(a, acc[i & 1], bias, qpos, rg + RS * i, key, half, s0, s1);
       __builtin_amdgcn_sched_barrier(0);
     }
