@@ -559,7 +559,8 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // bias / qpos: per row of the head, log2 of the normaliser and the prompt
 // position of its query (-1 for padding rows), read from LDS inside the loop
-// so that nothing per row lives in registers.
+// (the wide-row path, where registers are short; with up to two row tiles
+// per wavefront the biases stay in registers, see weight_sum_r).
 template <bool EDGE>
 __device__ __forceinline__ void weight_sum(const ScoreArgs& a, const f32x16_t& acc, const float* bias,
                                            const int* qpos, int t, int key, int half, float& s0, float& s1) {
@@ -590,10 +591,34 @@ __device__ __forceinline__ void weight_sum(const ScoreArgs& a, const f32x16_t& a
   }
 }
 
+// As weight_sum, with this lane's 16 row biases of the tile in registers.
+template <bool EDGE>
+__device__ __forceinline__ void weight_sum_r(const ScoreArgs& a, const f32x16_t& acc, const float (&b)[16],
+                                             const int* qpos, int t, int key, int half, float& s0, float& s1) {
+  const int o = t * kRowTile + 4 * half;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    u32x4_t qv = {0u, 0u, 0u, 0u};
+    if constexpr (EDGE) {
+      u32x4_t qq[1] = {lds_read_b128(qpos + o + 8 * q4)};
+      lds_settle(qq);
+      qv = qq[0];
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      float p = exp2_raw(fmaf(acc[4 * q4 + e4], a.c, -b[4 * q4 + e4]));
+      if constexpr (EDGE) {
+        if (key >= a.s || key > (int)qv[e4]) p = 0.f;
+      }
+      if (e4 & 1) s1 += p; else s0 += p;
+    }
+  }
+}
+
 template <int D, int NRTW, int RS, bool EDGE>
 __device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr)[NRTW][D / 16],
                                             const uint4 (&kf)[D / 16], const float* bias, const int* qpos,
-                                            int key, int half, int rg, int ntile) {
+                                            int key, int half, int rg, int ntile, const float (&breg)[NRTW][16]) {
   float s0 = 0.f, s1 = 0.f;
   if constexpr (NRTW <= 2) {
     f32x16_t acc[2];
@@ -608,7 +633,7 @@ __device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr
       __builtin_amdgcn_s_setprio(1);
       if (i + 1 < NRTW && i + 1 < ntile) acc[(i + 1) & 1] = contract<D, NRTW, false>(qr, kf, i + 1);
       __builtin_amdgcn_s_setprio(0);
-      if (i < ntile) weight_sum<EDGE>(a, acc[i & 1], bias, qpos, rg + RS * i, key, half, s0, s1);
+      if (i < ntile) weight_sum_r<EDGE>(a, acc[i & 1], breg[i], qpos, rg + RS * i, key, half, s0, s1);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -711,6 +736,23 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
     }
   };
 
+  // this lane's row biases of its row tiles, once
+  float breg[NRTW][16];
+  if constexpr (NRTW <= 2) {
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NRTW; ++i) {
+      const int o = (ro.rg + R::RS * i) * kRowTile + 4 * half;
+      u32x4_t bq[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) bq[q4] = lds_read_b128(bias + o + 8 * q4);
+      lds_settle(bq);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) breg[i][4 * q4 + e4] = __uint_as_float(bq[q4][e4]);
+    }
+  }
   for (int n = 0; n < rg.nst; ++n) {
     ring_advance<D, HG>(a, h0, rg, n, wave, lane, off, smem);
     if constexpr (R::RS > 1) {
@@ -723,8 +765,8 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
       load_key_regs<D, HG>(slot, ro.hl, ro.kt, half, l32, kf);
       const int key = kbase + l32;
       const float sum = kbase + kKeyTile <= first_hidden
-                            ? pass2_tile<D, NRTW, R::RS, false>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile)
-                            : pass2_tile<D, NRTW, R::RS, true>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile);
+                            ? pass2_tile<D, NRTW, R::RS, false>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile, breg)
+                            : pass2_tile<D, NRTW, R::RS, true>(a, qr, kf, bias, qpos, key, half, ro.rg, ntile, breg);
       if constexpr (R::RS > 1) {
         if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
       } else {
