@@ -222,6 +222,58 @@ def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
     return out
 
 
+OTHER_CONFIGS = ["llama8b_16k", "llama8b_128k", "llama8b_128k_pool7", "qwen14b_hetero_64k"]
+
+
+def other_configs(kvc, torch, dev, names, reps, sp, stream):
+    """kvc_compress_layer on the other layer shapes: two resident layers of
+    each, `reps` calls alternating between them after two warm calls, HIP
+    events around the calls. Reports time per layer, throughput and the HBM
+    fraction over the layer's algorithmic bytes."""
+    from synth import get_config, layer_inputs
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    out = {}
+    for name in names:
+        cfg = get_config(name)
+        preps = []
+        rows = 0
+        for l in range(2):
+            x = layer_inputs(cfg, l)
+            budgets = (kvc.kvc_budgets_inverse_stability(x.s_stable, cfg.total_budget) if cfg.hetero
+                       else np.full(cfg.hkv, cfg.budget, dtype=np.int32))
+            q, k, v = dev_bf16(x.q), dev_bf16(x.k), dev_bf16(x.v)
+            del x
+            desc = kvc.desc_for(q, k, v, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool)
+            o = kvc.alloc_outputs(desc, budgets, dev, with_intermediates=False)
+            rows = max(rows, int(o.offsets[-1]))
+            preps.append(kvc.PreparedLayer(desc, q, k, v, budgets, o, kvc.alloc_workspace(desc, dev)))
+        for p in preps:
+            p.kvc_compress_layer(sp)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            preps[i % 2].kvc_compress_layer(sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        alg = sum(algorithmic_bytes(cfg, rows).values())
+        rows_per_head = cfg.group * cfg.w
+        out[name] = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "pool": cfg.pool,
+                     "hetero": bool(cfg.hetero), "us_per_layer": round(us, 2),
+                     "tokens_per_s": round(cfg.s / (us * 1e-6), 1), "alg_bytes": alg,
+                     "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "scans": "streaming (K staged in LDS)" if rows_per_head <= 128 else "per-head (K in VGPRs)"}
+        log(f"{name}: {us:.1f} us per layer, {out[name]['hbm_frac'] * 100:.1f}% of the HBM peak, "
+            f"{out[name]['scans']} scans")
+        del preps
+        torch.cuda.empty_cache()
+    return out
+
+
 def layer_major_prefill(kvc, torch, dev, s=65536, chunk=2048, w=32, budget=4096):
     """The compressor inside the schedule it serves: a random-weight
     Llama-3.1-8B-shaped stack (32 layers) prefilled layer-major in chunks with
@@ -308,6 +360,8 @@ def main(argv=None):
                     help="CPU-oracle baseline sample length in seconds (0: skip)")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="skip the layer-major prefill run (random-weight model around the compressor)")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip timing the other layer shapes (16K, 128K, 128K with pool 7, Qwen-shaped)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (to calibrate HBM byte counters)")
     args = ap.parse_args(argv)
@@ -563,6 +617,7 @@ def main(argv=None):
     # keys, each against the one-shot layer-end compressor on the same tensors
     imm_detail = {name: immediate_eviction(kvc, torch, dev, name, max(4, K // 4), sp, stream)
                   for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
+    configs_detail = other_configs(kvc, torch, dev, OTHER_CONFIGS, max(8, K // 4), sp, stream) if args.configs else None
     prefill_detail = layer_major_prefill(kvc, torch, dev, s=cfg.s) if args.prefill else None
 
     copy_gbs = achievable_hbm_gbs(torch, dev)
@@ -616,6 +671,7 @@ def main(argv=None):
                           "note": "a 512 MiB read before each layer evicts the memory-side cache; "
                                   "HIP events around one kvc_compress_layer call"},
         "score_modes": mode_detail,
+        "other_configs": configs_detail,
         "immediate_eviction": imm_detail,
         "layer_major_prefill": prefill_detail,
         "sweep": {
