@@ -768,7 +768,7 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
   if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   e = hipEventRecord(ev, lanes[0]);
   for (int j = 1; j < kSweepStreams && e == hipSuccess; ++j) e = hipStreamWaitEvent(lanes[j], ev, 0);
-  hipEventDestroy(ev);
+  (void)hipEventDestroy(ev);
   if (e != hipSuccess) return hip_fail(e, "sweep fork");
   int status = KVC_OK;
   for (int32_t i = 0; i < n_layers && status == KVC_OK; ++i) {
@@ -784,7 +784,7 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
     if (e == hipSuccess) {
       e = hipEventRecord(jv, lanes[j]);
       if (e == hipSuccess) e = hipStreamWaitEvent(lanes[0], jv, 0);
-      hipEventDestroy(jv);
+      (void)hipEventDestroy(jv);
     }
     if (e != hipSuccess && status == KVC_OK) status = hip_fail(e, "sweep join");
   }

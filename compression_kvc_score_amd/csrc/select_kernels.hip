@@ -250,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   using KF = KeyFmt<SIGNED>;
   __shared__ uint32_t scratch[kWaves];
   __shared__ uint32_t w_in[kWaves], w_above[kWaves];
-  __shared__ uint32_t s_b, s_hit;
+  __shared__ uint32_t s_b;
   const int head = blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
   const HeadGeom h = head_geom(a, head);
   if (h.keep_all || h.k_sel == 0) return;

@@ -321,7 +321,6 @@ __device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int tok
 template <int D, int HG>
 __device__ __forceinline__ void ring_fill(const ScoreArgs& a, int h0, const Range& rg, int wave, int lane,
                                           const uint32_t* off, unsigned char* smem) {
-  using R = Ring<D, HG>;
 #pragma unroll
   for (int n = 0; n < kRingSlots - 1; ++n)
     if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
