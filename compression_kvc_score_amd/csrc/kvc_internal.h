@@ -168,12 +168,16 @@ hipError_t launch_overlap(const OverlapArgs& a, int hkv, hipStream_t st);
 // also the signed-key histogram of the candidates (cleared beforehand).
 hipError_t launch_logit_scan(const Layer& L, const LogitArgs& a, bool int8, hipStream_t st);
 
-// Wavefronts per scan workgroup: one per 32-key tile of a block, at most 8;
-// larger blocks give each wavefront block / 256 tiles per block.
+// Wavefronts per scan workgroup: the largest count up to 8 that divides the
+// block's 32-key tiles, so that every wavefront visits the same number of
+// tiles per block and together they cover all of them (a block of 11 tiles
+// runs on one wavefront, 12 on six, 16 on eight).
 constexpr int kMaxScanWaves = 8;
 inline int scan_waves(const Layer& L) {
   const int t = L.block / kKeyTile;
-  return t < kMaxScanWaves ? t : kMaxScanWaves;
+  for (int w = t < kMaxScanWaves ? t : kMaxScanWaves; w > 1; --w)
+    if (t % w == 0) return w;
+  return 1;
 }
 
 // Streaming scans (G*W <= 128): head-group workgroups with K staged in LDS.

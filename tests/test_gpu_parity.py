@@ -132,6 +132,23 @@ def test_block_size_invariance(block):
     check_layer(x, got, b)
 
 
+@pytest.mark.parametrize("block", [32, 96, 224, 256, 288, 352, 416, 480, 512])
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_size_invariance_wide_rows(block, d):
+    """The per-head scans (more than 128 query rows per KV head) cover every
+    key of every block, whatever the block's count of 32-key tiles (a block
+    of 11 tiles once left 3 of them unscored)."""
+    cfg = get_config("tiny").with_(s=3001, hq=8, hkv=1, d=d, w=32, budget=300, n_heavy=20)
+    x = layer_inputs(cfg, 2)
+    q, k, v = dev_inputs(x)
+    desc = desc_from(cfg, q, k, v, block=block)
+    b = budgets_for(cfg, x)
+    say(f"wide rows, block {block}, d {d}")
+    got = run_fused(desc, q, k, v, b)
+    check_layer(x, got, b)
+    np.testing.assert_allclose(got["scores"].sum(axis=1), cfg.w * cfg.group, rtol=1e-4)
+
+
 EDGE_CASES = {
     # name: (config overrides, budgets or None for uniform, extra desc options)
     "one_key": (dict(s=1, w=1, hq=1, hkv=1, d=64, n_sink=0, n_recent=0, n_heavy=0, budget=1), None, {}),
