@@ -61,12 +61,17 @@ def random_cases(n=40, seed=20261202):
 CASES = random_cases()
 
 
-@pytest.mark.parametrize("i", range(len(CASES)))
-def test_random_shape(i):
+def _case_cfg(i):
     c = dict(CASES[i])
     budgets = np.asarray(c.pop("budgets"), dtype=np.int64)
     seed = c.pop("seed")
     cfg = get_config("tiny").with_(name=f"random_{i}", sink_scale=4.0, seed_base=seed, budget=int(budgets[0]), **c)
+    return cfg, budgets, seed
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_random_shape(i):
+    cfg, budgets, _ = _case_cfg(i)
     print(f"random shape {i}: s={cfg.s} w={cfg.w} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} block={cfg.block} "
           f"sink={cfg.n_sink} recent={cfg.n_recent} pool={cfg.pool} budgets={list(budgets)}", flush=True, file=sys.stderr)
     x = layer_inputs(cfg, 0)
@@ -74,3 +79,76 @@ def test_random_shape(i):
     desc = desc_from(cfg, q, k, v)
     got = run_fused(desc, q, k, v, budgets)
     check_layer(x, got, budgets)
+
+
+
+@pytest.mark.parametrize("i", range(0, len(CASES), 3))
+def test_random_shape_strided_offset_and_staged(i):
+    """The same layer read through strided views (K, V and Q_win embedded
+    among other heads) with a position offset: the staged calls equal the
+    whole-layer call bit for bit, and both equal the contiguous run with the
+    positions shifted by the offset."""
+    from gpu_util import from_dev_bits, run_staged, to_dev_bf16
+    cfg, budgets, seed = _case_cfg(i)
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev_inputs(x)
+    base = run_fused(desc_from(cfg, q, k, v), q, k, v, budgets)
+    rng = np.random.default_rng(seed)
+    pos_offset = int(rng.integers(0, 1 << 20))
+    g = cfg.group
+    kb = torch.zeros((cfg.s, cfg.hkv + 2, cfg.d), dtype=torch.bfloat16, device="cuda")
+    vb = torch.zeros_like(kb)
+    qb = torch.zeros((cfg.w, cfg.hq + g, cfg.d), dtype=torch.bfloat16, device="cuda")
+    kb[:, 1:1 + cfg.hkv] = k
+    vb[:, 1:1 + cfg.hkv] = v
+    qb[:, g:g + cfg.hq] = q
+    ks, vs, qs = kb[:, 1:1 + cfg.hkv], vb[:, 1:1 + cfg.hkv], qb[:, g:g + cfg.hq]
+    desc = desc_from(cfg, qs, ks, vs, pos_offset=pos_offset)
+    print(f"strided case {i}: pos_offset={pos_offset}", flush=True, file=sys.stderr)
+    fu = run_fused(desc, qs, ks, vs, budgets)
+    st = run_staged(desc, qs, ks, vs, budgets)
+    for key in ["m", "z", "scores", "idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(fu[key], st[key], err_msg=f"staged != whole layer: {key}")
+    for key in ["m", "z", "scores", "idx", "k_hat", "v_hat"]:
+        np.testing.assert_array_equal(fu[key], base[key], err_msg=f"strided != contiguous: {key}")
+    np.testing.assert_array_equal(fu["pos"], base["pos"] + pos_offset)
+
+
+@pytest.mark.parametrize("mode", ["logit", "int8"])
+@pytest.mark.parametrize("i", range(1, len(CASES), 3))
+def test_random_shape_score_modes(i, mode):
+    """The raw inner-product modes on the random shapes: whole layer equal to
+    the staged calls, INT8 scores and selection exactly the oracle's, fp32
+    scores within their rounding bound and the selection exact outside it,
+    the gather bit for bit."""
+    from gpu_util import split_heads
+    from test_gpu_score_modes import MODES, check_selection_signed, logit_error_bound, run_staged_modes
+    import oracle
+    cfg, budgets, _ = _case_cfg(i)
+    if cfg.s > (1 << 22):
+        pytest.skip("raw modes take at most 2^22 keys")
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev_inputs(x)
+    desc = desc_from(cfg, q, k, v, score_mode=MODES[mode])
+    print(f"score mode {mode} case {i}", flush=True, file=sys.stderr)
+    fu = run_fused(desc, q, k, v, budgets)
+    st = run_staged_modes(desc, q, k, v, budgets)
+    for key in ["scores", "idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(fu[key], st[key], err_msg=f"fused != staged: {key}")
+    pool = cfg.pool
+    if mode == "int8":
+        want = oracle.logit_scores_int8(x.q, x.k)
+        np.testing.assert_array_equal(fu["scores"], want)
+        vals = oracle.maxpool(want.astype(np.float64), pool) if pool > 1 else want.astype(np.float64)
+        want_idx = oracle.select(vals, budgets, cfg.n_sink, cfg.n_recent)
+        np.testing.assert_array_equal(fu["idx"], np.concatenate(want_idx))
+    else:
+        want = oracle.logit_scores(oracle.bf16_to_f64(x.q), oracle.bf16_to_f64(x.k))
+        err = logit_error_bound(x.q, x.k)
+        assert np.all(np.abs(fu["scores"] - want) <= err)
+        check_selection_signed(fu["idx"], fu["scores"], want, err, budgets, cfg.n_sink, cfg.n_recent, pool=pool)
+    idx = split_heads(fu["idx"], fu["offsets"])
+    k_hat, v_hat, pos = oracle.gather(x.k, x.v, idx)
+    np.testing.assert_array_equal(fu["k_hat"], k_hat)
+    np.testing.assert_array_equal(fu["v_hat"], v_hat)
+    np.testing.assert_array_equal(fu["pos"], pos)
