@@ -152,3 +152,42 @@ def test_random_shape_score_modes(i, mode):
     np.testing.assert_array_equal(fu["k_hat"], k_hat)
     np.testing.assert_array_equal(fu["v_hat"], v_hat)
     np.testing.assert_array_equal(fu["pos"], pos)
+
+
+def random_chunked_cases(n=10, seed=20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 5]))
+        w = int(rng.choice([2, 8, 16, 32]))
+        s = int(rng.integers(4 * w, 5000))
+        chunk = int(rng.integers(w, max(w + 1, s // 2)))
+        if s - ((s - 1) // chunk) * chunk < w:  # the last chunk must hold a window
+            continue
+        n_sink = int(rng.integers(0, 5))
+        n_recent = int(rng.integers(0, w + 1))
+        budget = int(rng.integers(max(n_sink + n_recent, 1), max(n_sink + n_recent + 2, s // 2)))
+        cases.append(dict(s=s, w=w, hq=g * hkv, hkv=hkv, d=d, block=128, n_sink=n_sink, n_recent=n_recent,
+                          n_heavy=int(rng.integers(0, 1 + s // 200)), chunk=chunk, budget=budget,
+                          pool=int(rng.choice([1, 1, 3])), pos_offset=int(rng.integers(0, 1 << 16)),
+                          mode=str(rng.choice(["softmax", "softmax", "logit", "int8"])),
+                          seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+CHUNKED = random_chunked_cases()
+
+
+@pytest.mark.parametrize("i", range(len(CHUNKED)))
+def test_random_immediate_eviction(i):
+    """Immediate (chunk-boundary) eviction on random shapes: every boundary
+    checked on the GPU's own state against the oracle, the whole-prompt call
+    equal to the boundary chain, and the final cache equal to the oracle's
+    chunked compressor when no boundary decision fell inside a tie band."""
+    from test_gpu_chunked import check_case
+    c = dict(CHUNKED[i])
+    budget, pool, pos_offset, mode, seed = c.pop("budget"), c.pop("pool"), c.pop("pos_offset"), c.pop("mode"), c.pop("seed")
+    cfg = get_config("tiny").with_(name=f"random_chunked_{i}", sink_scale=4.0, seed_base=seed, budget=budget, **c)
+    check_case(cfg, budget, mode=mode, pool=pool, pos_offset=pos_offset)
