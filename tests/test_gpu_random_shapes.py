@@ -191,3 +191,40 @@ def test_random_immediate_eviction(i):
     budget, pool, pos_offset, mode, seed = c.pop("budget"), c.pop("pool"), c.pop("pos_offset"), c.pop("mode"), c.pop("seed")
     cfg = get_config("tiny").with_(name=f"random_chunked_{i}", sink_scale=4.0, seed_base=seed, budget=budget, **c)
     check_case(cfg, budget, mode=mode, pool=pool, pos_offset=pos_offset)
+
+
+def random_attention_cases(n=10, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        c0 = int(rng.integers(0, 3000))
+        n_q = int(rng.integers(1, 300))
+        s = c0 + n_q + int(rng.integers(0, 50))
+        out.append((g * hkv, hkv, d, c0, n_q, s, int(rng.integers(1, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv,d,c0,n,s,seed", random_attention_cases())
+def test_random_chunk_attention(hq, hkv, d, c0, n, s, seed):
+    """Causal GQA chunk attention on random shapes and offsets against the
+    exact attention, within the bf16 bound of the fixed-shape test."""
+    import oracle
+    from test_gpu_prefill import ULP, attention_bound, bits, f64
+    from gpu_util import from_dev_bits, to_dev_bf16
+    rng = np.random.default_rng(seed)
+    pd = kvc.PrefillDesc(s=s, hq=hq, hkv=hkv, d=d, rope_base=10000.0, scale=0.0)
+    q = bits(rng, (n, hq, d), 1.5)
+    k = bits(rng, (s, hkv, d), 1.5)
+    v = bits(rng, (s, hkv, d))
+    o = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    kvc.kvc_chunk_attention(pd, to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), c0, o)
+    torch.cuda.synchronize()
+    pos = np.arange(c0, c0 + n)
+    kk, vv = f64(k)[: c0 + n], f64(v)[: c0 + n]
+    want = oracle.attention(f64(q), kk, vv, pos)
+    bound = ULP * np.abs(want) + 2 * 2.0 ** -8 * attention_bound(f64(q), kk, vv, pos) + 1e-6
+    err = np.abs(f64(from_dev_bits(o)) - want)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3f}"
