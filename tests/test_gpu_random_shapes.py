@@ -228,3 +228,27 @@ def test_random_chunk_attention(hq, hkv, d, c0, n, s, seed):
     bound = ULP * np.abs(want) + 2 * 2.0 ** -8 * attention_bound(f64(q), kk, vv, pos) + 1e-6
     err = np.abs(f64(from_dev_bits(o)) - want)
     assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3f}"
+
+
+@pytest.mark.parametrize("i", range(2, len(CASES), 8))
+def test_random_shape_layer_sweep(i):
+    """kvc_compress_layers (two layers in flight) over 1-5 layers of a random
+    shape with per-layer budgets writes exactly what one kvc_compress_layer
+    call per layer writes."""
+    cfg, budgets, seed = _case_cfg(i)
+    rng = np.random.default_rng(seed + 1)
+    n_layers = int(rng.integers(1, 6))
+    xs = [layer_inputs(cfg, l) for l in range(n_layers)]
+    layers = [dev_inputs(x) for x in xs]
+    bl = np.stack([rng.permutation(budgets) for _ in range(n_layers)])
+    desc = desc_from(cfg, *layers[0])
+    want = [run_fused(desc, *layers[l], bl[l], intermediates=False) for l in range(n_layers)]
+    outs = [kvc.alloc_outputs(desc, bl[l], with_intermediates=False) for l in range(n_layers)]
+    kvc.kvc_compress_layers(desc, layers, bl, outs, kvc.alloc_sweep_workspace(desc))
+    torch.cuda.synchronize()
+    from gpu_util import from_dev_bits
+    for l in range(n_layers):
+        np.testing.assert_array_equal(outs[l].idx.cpu().numpy(), want[l]["idx"], err_msg=f"layer {l} idx")
+        np.testing.assert_array_equal(from_dev_bits(outs[l].k_hat), want[l]["k_hat"], err_msg=f"layer {l} k_hat")
+        np.testing.assert_array_equal(from_dev_bits(outs[l].v_hat), want[l]["v_hat"], err_msg=f"layer {l} v_hat")
+        np.testing.assert_array_equal(outs[l].pos.cpu().numpy(), want[l]["pos"], err_msg=f"layer {l} pos")
