@@ -252,3 +252,58 @@ def test_random_shape_layer_sweep(i):
         np.testing.assert_array_equal(from_dev_bits(outs[l].k_hat), want[l]["k_hat"], err_msg=f"layer {l} k_hat")
         np.testing.assert_array_equal(from_dev_bits(outs[l].v_hat), want[l]["v_hat"], err_msg=f"layer {l} v_hat")
         np.testing.assert_array_equal(outs[l].pos.cpu().numpy(), want[l]["pos"], err_msg=f"layer {l} pos")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_prefill_row_kernels(case):
+    """RMSNorm, the rotary append and SwiGLU on random sizes: one bf16 ulp of
+    the exact result (the pair norm for the rotation), copies bit for bit,
+    and cache rows outside the written range untouched."""
+    import oracle
+    from test_gpu_prefill import ULP, bits, f64
+    from gpu_util import from_dev_bits, to_dev_bf16
+    rng = np.random.default_rng(9000 + case)
+    # RMSNorm
+    rows, dim = int(rng.integers(1, 70)), 8 * int(rng.integers(1, 700))
+    x, w = bits(rng, (rows, dim), 3.0), bits(rng, dim)
+    y = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
+    kvc.kvc_rmsnorm(to_dev_bf16(x), to_dev_bf16(w), y, eps=1e-5)
+    torch.cuda.synchronize()
+    want = oracle.rmsnorm(f64(x), f64(w), 1e-5)
+    assert np.all(np.abs(f64(from_dev_bits(y)) - want) <= ULP * np.abs(want) + 1e-30), "rmsnorm"
+    # rotary append
+    g = int(rng.choice([1, 2, 4, 8]))
+    hkv, d = int(rng.choice([1, 2, 4])), int(rng.choice([64, 128]))
+    hq = g * hkv
+    n = int(rng.integers(1, 90))
+    c0 = int(rng.integers(0, 200000))
+    s = c0 + n + int(rng.integers(0, 9))
+    base = float(rng.choice([10000.0, 500000.0]))
+    pd = kvc.PrefillDesc(s=s, hq=hq, hkv=hkv, d=d, rope_base=base, scale=0.0)
+    qkv = bits(rng, (n, (hq + 2 * hkv) * d), 2.0)
+    q = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    sentinel = 0x3F80
+    kc = torch.full((s, hkv, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = torch.full((s, hkv, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    kvc.kvc_rope_append(pd, to_dev_bf16(qkv), c0, q, kc, vc)
+    torch.cuda.synchronize()
+    pos = np.arange(c0, c0 + n)
+    xx = f64(qkv)
+    for name, got, heads, off in [("q", from_dev_bits(q), hq, 0), ("k", from_dev_bits(kc)[c0:c0 + n], hkv, hq * d)]:
+        src = xx[:, off:off + heads * d].reshape(n, heads, d)
+        want = oracle.rope(src, pos, base)
+        norm = np.sqrt(src[..., : d // 2] ** 2 + src[..., d // 2:] ** 2)
+        norm = np.concatenate([norm, norm], axis=-1)
+        assert np.all(np.abs(f64(got) - want) <= ULP * norm + 1e-30), name
+    np.testing.assert_array_equal(from_dev_bits(vc)[c0:c0 + n], qkv[:, (hq + hkv) * d:].reshape(n, hkv, d))
+    for t in (kc, vc):
+        b = from_dev_bits(t)
+        assert np.all(b[:c0] == sentinel) and np.all(b[c0 + n:] == sentinel)
+    # SwiGLU
+    rows, ffn = int(rng.integers(1, 40)), 8 * int(rng.integers(1, 400))
+    gu = bits(rng, (rows, 2 * ffn), 3.0)
+    a = torch.empty((rows, ffn), dtype=torch.bfloat16, device="cuda")
+    kvc.kvc_swiglu(to_dev_bf16(gu), a)
+    torch.cuda.synchronize()
+    want = oracle.swiglu(f64(gu))
+    assert np.all(np.abs(f64(from_dev_bits(a)) - want) <= ULP * np.abs(want) + 1e-30), "swiglu"
