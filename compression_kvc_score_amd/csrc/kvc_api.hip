@@ -624,9 +624,16 @@ int kvc_budgets_inverse_stability(const double* s_stable, int32_t hkv, int64_t t
   }
   double wsum = 0.0;
   for (int h = 0; h < hkv; ++h) wsum += w[h];
+  // stabilities so spread (or so small) that the double arithmetic overflows
+  // cannot be turned into exact budgets: refuse rather than return a wrong sum
+  if (!std::isfinite(wsum))
+    return fail(KVC_ERR_INVALID_ARG, "s_stable too small: the inverse weights overflow");
   int64_t used = 0;
   for (int h = 0; h < hkv; ++h) {
     const double exact = (double)total * w[h] / wsum;
+    if (!std::isfinite(exact))
+      return fail(KVC_ERR_INVALID_ARG, "s_stable[%d] too small for total=%lld: the product overflows", h,
+                  (long long)total);
     base[h] = (int64_t)std::floor(exact);
     frac[h] = exact - (double)base[h];
     used += base[h];
@@ -635,6 +642,9 @@ int kvc_budgets_inverse_stability(const double* s_stable, int32_t hkv, int64_t t
   for (int h = 0; h < hkv; ++h) order[h] = h;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return frac[a] > frac[b]; });
   const int64_t rem = total - used;
+  if (rem < 0 || rem > hkv)
+    return fail(KVC_ERR_INVALID_ARG, "s_stable values too extreme: the budgets would not sum to total=%lld",
+                (long long)total);
   for (int64_t r = 0; r < rem && r < hkv; ++r) base[order[r]] += 1;
   for (int h = 0; h < hkv; ++h) budgets[h] = (int32_t)base[h];
   return KVC_OK;

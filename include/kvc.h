@@ -173,6 +173,9 @@ int kvc_retained_offsets(const kvc_layer_desc* desc, const int32_t* budgets, int
  * fractional parts, lower head index first among equals. Sums run in head
  * order, in double precision. s_stable: host array of hkv finite values > 0;
  * budgets: host output of hkv entries; 0 <= total <= 2^31 - 1. Pure host.
+ * Returns KVC_ERR_INVALID_ARG (writing nothing) when the values are so small
+ * or so spread that the double arithmetic overflows and the budgets could
+ * not sum to total.
  */
 int kvc_budgets_inverse_stability(const double* s_stable, int32_t hkv, int64_t total,
                                   int32_t* budgets);
