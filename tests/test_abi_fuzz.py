@@ -90,3 +90,43 @@ def test_inverse_stability_budgets_fuzz():
             np.testing.assert_array_equal(out[:hkv], want)
         else:
             assert st < 0
+
+
+def test_device_entry_points_refuse_fuzzed_arguments_before_any_launch():
+    """kvc_compress_layer, the staged calls and the chunk-boundary call with
+    fuzzed descriptors and pointer sets: each call lacks its workspace or an
+    output (or has a misaligned one), so the host must refuse it with an
+    error status before touching the device; no combination may crash."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("host-only fuzz: never run where kernels could launch")
+    rng = np.random.default_rng(10)
+    lib = kvc.lib()
+    P = ctypes.c_void_p
+    fake = [None, P(0x10000), P(0x10001), P(0x10004)]
+    budgets = np.full(kvc.KVC_MAX_KV_HEADS + 1, 64, dtype=np.int32)
+    bp = budgets.ctypes.data_as(P)
+    for _ in range(3000):
+        d = random_desc(rng)
+        dd = ctypes.byref(d)
+        ptrs = [fake[int(rng.integers(0, 4))] for _ in range(8)]
+        bad = int(rng.integers(0, 3))
+        if bad == 0:
+            ws, wsb = None, int(rng.integers(0, 1 << 30))           # no workspace
+        elif bad == 1:
+            ws, wsb = P(0x10000), int(rng.integers(0, 1 << 30))
+            ptrs[3] = None                                            # no idx_out
+        else:
+            ws, wsb = P(0x10010), int(rng.integers(0, 1 << 30))     # misaligned workspace
+        st = lib.kvc_compress_layer(dd, ptrs[0], ptrs[1], ptrs[2], bp, None, None, None, ptrs[3], ptrs[4],
+                                    ptrs[5], ptrs[6], ws, wsb, None)
+        assert st < 0
+        st = lib.kvc_score_pass1(dd, ptrs[0], ptrs[1], ptrs[2], ptrs[3], ws if bad != 1 else None, wsb, None)
+        assert st < 0
+        st = lib.kvc_select_topk(dd, ptrs[0], bp, ptrs[1], ws if bad != 1 else None, wsb, None)
+        assert st < 0
+        # no current arena: refused whether or not the boundary would evict
+        st = lib.kvc_evict_chunk(dd, ptrs[0], ptrs[1], ptrs[2], int(rng.integers(-1, 5000)),
+                                 int(rng.integers(-1, 5000)), int(rng.integers(-1, 20000)), None, ptrs[4],
+                                 ptrs[5], ptrs[6], ptrs[7], ptrs[0], None, wsb, None)
+        assert st < 0
