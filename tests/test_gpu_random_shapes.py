@@ -307,3 +307,23 @@ def test_random_prefill_row_kernels(case):
     torch.cuda.synchronize()
     want = oracle.swiglu(f64(gu))
     assert np.all(np.abs(f64(from_dev_bits(a)) - want) <= ULP * np.abs(want) + 1e-30), "swiglu"
+
+
+def test_positions_at_the_int32_limit():
+    """pos_offset + s = 2^31 - 1 (the largest the descriptor accepts): every
+    retained position is offset + index exactly, in the whole-layer call and
+    in the staged gather."""
+    from gpu_util import run_staged, split_heads
+    cfg = get_config("tiny").with_(name="max_pos", s=2000, w=16, hq=8, hkv=2, d=64, n_sink=4, n_recent=16,
+                                   n_heavy=10, budget=300)
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev_inputs(x)
+    off = (1 << 31) - 1 - cfg.s
+    b = np.array([300, 2000])
+    desc = desc_from(cfg, q, k, v, pos_offset=off)
+    fu = run_fused(desc, q, k, v, b)
+    st = run_staged(desc, q, k, v, b)
+    idx = np.concatenate(split_heads(fu["idx"], fu["offsets"])).astype(np.int64)
+    np.testing.assert_array_equal(fu["pos"].astype(np.int64), idx + off)
+    np.testing.assert_array_equal(st["pos"], fu["pos"])
+    assert int(fu["pos"].max()) == (1 << 31) - 2  # head 1 keeps every key, the last at 2^31 - 2
