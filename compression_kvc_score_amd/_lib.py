@@ -29,6 +29,9 @@ KVC_MAX_POOL = 31
 KVC_SCORE_SOFTMAX = 0
 KVC_SCORE_LOGIT = 1
 KVC_SCORE_LOGIT_INT8 = 2
+KVC_SCAN_STREAM = 1
+KVC_SCAN_PER_HEAD = 2
+KVC_SCAN_LOGIT = 3
 
 
 class KvcError(RuntimeError):
@@ -58,6 +61,18 @@ class LayerDesc(ctypes.Structure):
         ("k_head_stride", ctypes.c_int64),
         ("v_tok_stride", ctypes.c_int64),
         ("v_head_stride", ctypes.c_int64),
+    ]
+
+
+class LayerPlan(ctypes.Structure):
+    """Mirror of ``kvc_layer_plan``."""
+    _fields_ = [
+        ("scan", ctypes.c_int32),
+        ("heads_per_wg", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("hist_in_scan", ctypes.c_int32),
+        ("keys_per_wg", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -106,6 +121,7 @@ def _load():
         "kvc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "kvc_last_error": (ctypes.c_char_p, []),
         "kvc_workspace_size": (SZ, [D]),
+        "kvc_plan_layer": (ctypes.c_int, [D, ctypes.POINTER(LayerPlan)]),
         "kvc_retained_offsets": (ctypes.c_int, [D, P, P]),
         "kvc_budgets_inverse_stability": (ctypes.c_int, [P, I32, I64, P]),
         "kvc_score_pass1": (ctypes.c_int, [D, P, P, P, P, P, SZ, P]),
@@ -211,6 +227,12 @@ def kvc_workspace_size(desc: LayerDesc) -> int:
     if n == 0:
         _check(KVC_ERR_INVALID_ARG)
     return n
+
+
+def kvc_plan_layer(desc: LayerDesc) -> LayerPlan:
+    plan = LayerPlan()
+    _check(_load().kvc_plan_layer(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan
 
 
 def kvc_retained_offsets(desc: LayerDesc, budgets) -> np.ndarray:

@@ -151,6 +151,16 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   return KVC_OK;
 }
 
+// The streaming pass 2 counts its histogram in 16-bit LDS halves: it may
+// build the selection histogram only while one workgroup sees fewer than 2^16
+// keys of a head (identical scores all land in one bin). Otherwise the
+// selection's own histogram kernel (32-bit counters) runs instead.
+int64_t stream_keys_per_wg(const Layer& L) {
+  return L.stream_hg ? (int64_t)L.blocks_per_wg * stream_tokens(L.d, L.stream_hg) : 0;
+}
+
+bool hist_fits_scan(const Layer& L) { return L.stream_hg == 0 || stream_keys_per_wg(L) < 65536; }
+
 int64_t mandatory_count(int64_t s, int n_sink, int n_recent) {
   const int64_t sink_end = std::min<int64_t>(n_sink, s);
   const int64_t rec_begin = std::max<int64_t>(s - n_recent, sink_end);
@@ -346,7 +356,7 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
 
 // Raw inner-product scores (the non-softmax score modes) into `scores`; with
 // hist (cleared beforehand) also the selection histogram.
-int run_logit(const Layer& L, const void* q, const void* k, float* scores, uint32_t* hist, hipStream_t st) {
+LogitArgs logit_args(const Layer& L, const void* q, const void* k) {
   LogitArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -361,11 +371,16 @@ int run_logit(const Layer& L, const void* q, const void* k, float* scores, uint3
   const int64_t prefix = L.s - L.w + 1;  // keys seen by every window row
   a.n_split = (int)std::max<int64_t>(1, std::min<int64_t>(stream_wg_target() / L.hkv, (prefix + 255) / 256));
   a.keys_per_wg = (int)((prefix + a.n_split - 1) / a.n_split);
-  a.scores = scores;
-  a.hist = hist;
   const int64_t sink_end = std::min<int64_t>(L.n_sink, L.s);
   a.sink_end = (int)sink_end;
   a.rec_begin = (int)std::max<int64_t>(L.s - L.n_recent, sink_end);
+  return a;
+}
+
+int run_logit(const Layer& L, const void* q, const void* k, float* scores, uint32_t* hist, hipStream_t st) {
+  LogitArgs a = logit_args(L, q, k);
+  a.scores = scores;
+  a.hist = hist;
   const hipError_t e = launch_logit_scan(L, a, L.score_mode == KVC_SCORE_LOGIT_INT8, st);
   if (e != hipSuccess) return hip_fail(e, "raw inner-product scan launch");
   return KVC_OK;
@@ -420,8 +435,9 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
   float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
   float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
   float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
-  // the last scan builds the selection histogram unless ranking uses pooled values
-  const bool hist_in_pass2 = L.pool == 1;
+  // the last scan builds the selection histogram unless ranking uses pooled
+  // values or its 16-bit workgroup counters could wrap
+  const bool hist_in_pass2 = L.pool == 1 && hist_fits_scan(L);
   if (L.score_mode != KVC_SCORE_SOFTMAX) {
     uint32_t* hist = nullptr;
     if (hist_in_pass2) {
@@ -598,6 +614,30 @@ size_t kvc_workspace_size(const kvc_layer_desc* desc) {
   Layer L;
   if (normalize(desc, L) != KVC_OK) return 0;
   return ws_layout(L).total;
+}
+
+int kvc_plan_layer(const kvc_layer_desc* desc, kvc_layer_plan* plan) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  if (plan == nullptr) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  kvc_layer_plan p{};
+  if (L.score_mode != KVC_SCORE_SOFTMAX) {
+    LogitArgs a = logit_args(L, nullptr, nullptr);
+    p.scan = KVC_SCAN_LOGIT;
+    p.heads_per_wg = 1;
+    p.splits = a.n_split;
+    p.keys_per_wg = a.keys_per_wg;
+    p.hist_in_scan = L.pool == 1;
+  } else {
+    p.scan = L.stream_hg ? KVC_SCAN_STREAM : KVC_SCAN_PER_HEAD;
+    p.heads_per_wg = L.stream_hg ? L.stream_hg : 1;
+    p.splits = L.n_split;
+    p.keys_per_wg = L.stream_hg ? stream_keys_per_wg(L) : (int64_t)L.blocks_per_wg * L.block;
+    p.hist_in_scan = L.pool == 1 && hist_fits_scan(L);
+  }
+  p.workspace_bytes = ws_layout(L).total;
+  *plan = p;
+  return KVC_OK;
 }
 
 int kvc_retained_offsets(const kvc_layer_desc* desc, const int32_t* budgets, int64_t* offsets) {

@@ -255,6 +255,9 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   const HeadGeom h = head_geom(a, head);
   if (h.keep_all || h.k_sel == 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // no bin reached: b* stays this value (a histogram that undercounts), and
+  // the chunk then sends the compaction to the exact whole-row radix
+  if (threadIdx.x == 0) s_b = 0xFFFFFFFFu;
   // this thread's four values, loaded before the histogram scan so that the
   // two memory round trips overlap
   const float* vals = a.vals + (int64_t)head * h.s;
@@ -285,6 +288,17 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   }
   __syncthreads();
   const uint32_t bstar = s_b;
+  uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotStride;
+  if (bstar == 0xFFFFFFFFu) {
+    // an overflowing list count makes every compaction of the head resolve
+    // from the scores themselves
+    if (threadIdx.x < kSubsPerChunk) {
+      slot[threadIdx.x] = threadIdx.x == 0 ? (uint32_t)kSlotCap + 1u : 0u;
+      slot[kSubsPerChunk + threadIdx.x] = 0u;
+    }
+    if (threadIdx.x == 0) slot[2 * kSubsPerChunk] = 0u;
+    return;
+  }
 
   uint32_t above = 0, nin = 0;
   bool in[4];
@@ -310,7 +324,6 @@ __global__ void __launch_bounds__(kThreads) filter_kernel(SelectArgs a) {
   for (int w = 0; w < kWaves; ++w) pos += w < wave ? w_in[w] : 0u;
   // listed entries carry their sub-chunk: the keys inside b* share the bits
   // above LOW, so the low LOW bits identify them
-  uint32_t* slot = a.slots + ((int64_t)head * a.n_chunks + chunk) * kSlotStride;
   const uint32_t tag = (uint32_t)(chunk * kSubsPerChunk + (int)threadIdx.x / (kSub / 4)) << KF::LOW;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

@@ -158,6 +158,32 @@ const char* kvc_last_error(void);
  */
 size_t kvc_workspace_size(const kvc_layer_desc* desc);
 
+/* Scan designs reported by kvc_plan_layer. */
+typedef enum kvc_scan_kind {
+  KVC_SCAN_STREAM = 1,    /* head-group workgroups, K streamed through LDS rings (G * W <= 128) */
+  KVC_SCAN_PER_HEAD = 2,  /* one KV head per workgroup, K tiles in registers (G * W <= 256) */
+  KVC_SCAN_LOGIT = 3      /* the one-pass raw inner-product scan of the non-softmax score modes */
+} kvc_scan_kind;
+
+/* How a descriptor is executed, for tuning and tests (kvc_plan_layer). */
+typedef struct kvc_layer_plan {
+  int32_t scan;            /* a kvc_scan_kind */
+  int32_t heads_per_wg;    /* KV heads one scan workgroup covers */
+  int32_t splits;          /* scan workgroups per KV head (per head group when streaming) */
+  int32_t hist_in_scan;    /* 1: kvc_compress_layer counts the selection histogram inside
+                              the last scan; 0: a separate histogram kernel does */
+  int64_t keys_per_wg;     /* keys of one KV head that one scan workgroup covers (at most) */
+  size_t workspace_bytes;  /* kvc_workspace_size(desc) */
+} kvc_layer_plan;
+
+/*
+ * The execution plan of desc (validated as every entry point does) into
+ * *plan. The streaming pass 2 counts its histogram in 16-bit LDS halves, so it
+ * builds the selection histogram only while keys_per_wg < 65536. Pure host
+ * function.
+ */
+int kvc_plan_layer(const kvc_layer_desc* desc, kvc_layer_plan* plan);
+
 /*
  * Rows retained per KV head: min(budgets[g], s). Writes the exclusive prefix
  * sums to offsets[0 .. hkv] (host array of hkv + 1 entries), so head g's rows

@@ -365,3 +365,31 @@ def test_prefill_pieces_reject_bad_arguments_before_launch():
     assert lib.kvc_swiglu(good[0], good[1], 4, 100, None) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_swiglu(good[0], _fake(0x10004), 4, 128, None) == kvc.KVC_ERR_ALIGN
     assert "16-byte" in lib.kvc_last_error().decode()
+
+
+def test_plan_histogram_counter_bound():
+    """The streaming pass 2 counts its selection histogram in 16-bit LDS
+    halves, so it may build the histogram only while one workgroup sees fewer
+    than 2^16 keys of a head; beyond that the 32-bit histogram kernel runs."""
+    c3 = kvc.kvc_plan_layer(base_desc(s=65536))
+    assert c3.scan == kvc.KVC_SCAN_STREAM and c3.heads_per_wg == 2
+    assert c3.keys_per_wg == 1024 and c3.hist_in_scan == 1
+    assert c3.workspace_bytes == kvc.kvc_workspace_size(base_desc(s=65536))
+    # 64 heads of D 64, 2 window rows: one workgroup covers 2^16 keys of a head
+    wide = kvc.kvc_plan_layer(base_desc(s=1 << 19, w=2, hq=64, hkv=64, d=64, n_sink=4, n_recent=2))
+    assert wide.scan == kvc.KVC_SCAN_STREAM and wide.keys_per_wg >= 65536 and wide.hist_in_scan == 0
+    # every streaming plan obeys the bound
+    for s in [1024, 65536, 1 << 18, 1 << 20, 1 << 23]:
+        for hkv, hq, d, w in [(8, 32, 128, 32), (64, 64, 64, 2), (1, 1, 64, 2), (2, 8, 128, 16)]:
+            p = kvc.kvc_plan_layer(base_desc(s=s, w=w, hq=hq, hkv=hkv, d=d))
+            if p.scan == kvc.KVC_SCAN_STREAM:
+                assert (p.hist_in_scan == 1) == (p.keys_per_wg < 65536), (s, hkv, hq, d, w)
+            assert p.splits >= 1 and p.keys_per_wg >= 1
+    # per-head scans (G * W > 128) count in 32 bits; pooling ranks pooled
+    # values, which the selection's own histogram kernel counts
+    assert kvc.kvc_plan_layer(base_desc(s=1 << 20, w=64)).scan == kvc.KVC_SCAN_PER_HEAD
+    assert kvc.kvc_plan_layer(base_desc(s=1 << 20, w=64)).hist_in_scan == 1
+    assert kvc.kvc_plan_layer(base_desc(s=65536, pool=7)).hist_in_scan == 0
+    assert kvc.kvc_plan_layer(base_desc(s=65536, score_mode=kvc.KVC_SCORE_LOGIT)).scan == kvc.KVC_SCAN_LOGIT
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_plan_layer(base_desc(s=0))

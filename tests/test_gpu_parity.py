@@ -338,6 +338,50 @@ def test_identical_keys_exact_tie_break():
     check_layer(x, got, b)
 
 
+@pytest.mark.parametrize("log2_s", [18, 19])
+def test_identical_keys_many_per_workgroup(log2_s):
+    """All keys equal with 64 KV heads of D 64 and two window rows: one scan
+    workgroup covers 2^17 (2^18 keys) or 2^16 (2^19 keys) keys of a head, all
+    in one histogram bin. Every prefix key scores 1/(S-1) + 1/S (closed form,
+    bitwise equal), and each head keeps the mandatory keys plus the lowest
+    candidate indices."""
+    s, hkv, d, w, budget, n_sink, n_recent = 1 << log2_s, 64, 64, 2, 4096, 4, 2
+    desc = kvc.make_desc(s=s, w=w, hq=hkv, hkv=hkv, d=d, block=256, n_sink=n_sink, n_recent=n_recent)
+    plan = kvc.kvc_plan_layer(desc)
+    say(f"identical keys S=2^{log2_s}: {plan.keys_per_wg} keys per workgroup, histogram in scan {plan.hist_in_scan}")
+    assert plan.scan == kvc.KVC_SCAN_STREAM and plan.hist_in_scan == (plan.keys_per_wg < 65536)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202 + log2_s)
+    q = torch.randn((w, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    row = torch.randn((1, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    k = row.expand(s, hkv, d).contiguous()
+    # V rows encode (token, head, column) so the gather is checked bit for bit
+    tok = torch.arange(s, device="cuda", dtype=torch.int32).view(s, 1, 1)
+    code = (tok * 7 + torch.arange(hkv, device="cuda", dtype=torch.int32).view(1, hkv, 1) * 3
+            + torch.arange(d, device="cuda", dtype=torch.int32).view(1, 1, d)) & 0x7F7F
+    v = code.to(torch.int16).view(torch.bfloat16)
+    b = np.full(hkv, budget, dtype=np.int64)
+    ws = kvc.alloc_workspace(desc)
+    out = kvc.alloc_outputs(desc, b)
+    kvc.compress_layer(desc, q, k, v, b, out, ws)
+    torch.cuda.synchronize()
+    sc = out.scores.cpu().numpy()
+    prefix = sc[:, : s - w + 1]
+    assert np.all(prefix == prefix[:, :1]), "identical keys must score bitwise equal"
+    closed = 1.0 / (s - 1) + 1.0 / s
+    assert_scores_close(prefix[:, 0], np.full(hkv, closed), what="prefix score")
+    want = np.concatenate([np.arange(budget - n_recent), np.arange(s - n_recent, s)]).astype(np.int32)
+    idx = out.idx.cpu().numpy().reshape(hkv, budget)
+    for g in range(hkv):
+        np.testing.assert_array_equal(idx[g], want, err_msg=f"head {g}")
+    np.testing.assert_array_equal(out.pos.cpu().numpy().reshape(hkv, budget), idx)
+    kh = out.k_hat.view(hkv, budget, d)
+    assert torch.equal(kh.view(torch.int16), row.view(torch.int16).view(hkv, 1, d).expand(hkv, budget, d))
+    vh = out.v_hat.view(hkv, budget, d).view(torch.int16).cpu().numpy()
+    wantv = v.view(torch.int16)[torch.from_numpy(want).long().cuda()].permute(1, 0, 2).cpu().numpy()
+    np.testing.assert_array_equal(vh, wantv)
+
+
 def test_deterministic_repeat():
     cfg = get_config("llama8b_16k").with_(s=8192)
     x = layer_inputs(cfg, 2)
@@ -418,8 +462,12 @@ def full_size_case(name, layer, heads):
     check_layer(x, got, b, heads=heads)
 
 
-def test_full_size_llama8b_64k_sampled():
-    full_size_case("llama8b_64k", 0, heads=[0, 7])
+def test_full_size_llama8b_64k_all_heads():
+    full_size_case("llama8b_64k", 0, heads=list(range(8)))
+
+
+def test_full_size_llama8b_128k_sampled():
+    full_size_case("llama8b_128k", 0, heads=[0, 5])
 
 
 def test_full_size_llama8b_128k_pool7_sampled():

@@ -345,3 +345,51 @@ def test_compress_layer_composes_the_steps():
     pooled = oracle.maxpool(r.scores, 3)
     for g in range(hkv):
         assert list(r.idx[g]) == list(oracle.select_head(pooled[g], [10, 12][g], 2, 4))
+
+
+# ---------------------------------------------------------------- 50-digit brute force
+
+@pytest.mark.parametrize("w,hq,hkv,d,s,scale,seed", [
+    (1, 1, 1, 8, 2, None, 1), (3, 2, 1, 8, 5, None, 2), (4, 6, 2, 16, 9, 0.37, 3),
+    (12, 3, 1, 8, 12, None, 4), (5, 4, 2, 16, 12, 1.9, 5), (7, 3, 3, 8, 11, None, 6),
+])
+def test_normalizers_and_scores_match_50_digit_brute_force(w, hq, hkv, d, s, scale, seed):
+    """O2-O4 written out element by element in 50-digit arithmetic (mpmath):
+    each logit is the exact dot product of the decoded bf16 values times the
+    scale, the causal row's max and sum of exponentials, and the weights summed
+    per key over the window rows and the group's heads. The fp64 oracle agrees
+    to 1e-12."""
+    mpmath = pytest.importorskip("mpmath")
+    mp = mpmath.mp
+    mp.dps = 50
+    rng = np.random.default_rng(700 + seed)
+    qb = f32_to_bf16_bits((rng.standard_normal((w, hq, d)) * 2.0).astype(np.float32))
+    kb = f32_to_bf16_bits((rng.standard_normal((s, hkv, d)) * 2.0).astype(np.float32))
+    # decode through float32 (a bf16 pattern is the top half of a float32)
+    qf = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kf = (kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sc_mp = mp.mpf(1) / mp.sqrt(d) if scale is None else mp.mpf(scale)
+    grp = hq // hkv
+    want_m = np.empty((hq, w))
+    want_z = np.empty((hq, w))
+    want_s = [[mp.mpf(0)] * s for _ in range(hkv)]
+    for h in range(hq):
+        g = h // grp
+        for i in range(w):
+            p = s - w + i
+            logits = [sc_mp * mp.fsum(mp.mpf(qf[i, h, t]) * mp.mpf(kf[j, g, t]) for t in range(d))
+                      for j in range(p + 1)]
+            m = max(logits)
+            e = [mp.exp(x - m) for x in logits]
+            z = mp.fsum(e)
+            want_m[h, i] = float(m)
+            want_z[h, i] = float(z)
+            for j in range(p + 1):
+                want_s[g][j] += e[j] / z
+    q = oracle.bf16_to_f64(qb)
+    k = oracle.bf16_to_f64(kb)
+    got_m, got_z = oracle.normalizers(q, k, scale)
+    got_s = oracle.scores(q, k, scale)
+    np.testing.assert_allclose(got_m, want_m, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got_z, want_z, rtol=1e-12)
+    np.testing.assert_allclose(got_s, np.array([[float(x) for x in row] for row in want_s]), rtol=1e-12)
