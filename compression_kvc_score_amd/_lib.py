@@ -26,6 +26,7 @@ KVC_ERR_HIP = -5
 KVC_MAX_KV_HEADS = 64
 KVC_MAX_ROWS = 256
 KVC_MAX_POOL = 31
+KVC_NOALLOC_SCRATCH_BYTES = 16 << 20
 KVC_SCORE_SOFTMAX = 0
 KVC_SCORE_LOGIT = 1
 KVC_SCORE_LOGIT_INT8 = 2
@@ -130,6 +131,7 @@ def _load():
         "kvc_gather_retained": (ctypes.c_int, [D, P, P, P, P, P, P, P, P]),
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "kvc_compress_layer_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvc_overlap_coefficient": (ctypes.c_int, [D, P, P, P, P, P]),
         "kvc_chunk_workspace_size": (SZ, [D, I64]),
         "kvc_evict_chunk": (ctypes.c_int, [D, P, P, P, I32, I64, I64, P, P, P, P, P, P, P, SZ, P]),
@@ -295,6 +297,20 @@ def kvc_compress_layer(desc, q_win, k, v, budgets, idx_out, k_out, v_out, pos_ou
                                 _dev_ptr(idx_out, "idx_out", 4), _bf16_ptr(k_out, "k_out"),
                                 _bf16_ptr(v_out, "v_out"), _dev_ptr(pos_out, "pos_out", 4),
                                 _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+
+
+def kvc_compress_layer_noalloc(desc, q_win, k, v, budgets, idx_out, k_out, v_out, pos_out,
+                               m_out=None, z_out=None, scores_out=None):
+    """kvc_compress_layer with the library's fixed per-device scratch as the
+    workspace (no allocation anywhere)."""
+    L = _load()
+    b = _host_i32(budgets, desc.hkv, "budgets")
+    _check(L.kvc_compress_layer_noalloc(ctypes.byref(desc), _bf16_ptr(q_win, "q_win"), _bf16_ptr(k, "k"),
+                                        _bf16_ptr(v, "v"), b.ctypes.data_as(ctypes.c_void_p),
+                                        _dev_ptr(m_out, "m_out", 4), _dev_ptr(z_out, "z_out", 4),
+                                        _dev_ptr(scores_out, "scores_out", 4),
+                                        _dev_ptr(idx_out, "idx_out", 4), _bf16_ptr(k_out, "k_out"),
+                                        _bf16_ptr(v_out, "v_out"), _dev_ptr(pos_out, "pos_out", 4), _stream()))
 
 
 def kvc_overlap_coefficient(desc, idx_a, idx_b, budgets, out):

@@ -18,6 +18,12 @@
 
 using namespace kvc;
 
+// Workspace of kvc_compress_layer_noalloc: one copy per device, held until the
+// process ends. Host code must not pass this name to a kernel or a copy (on
+// the host it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -572,6 +578,27 @@ int aux_stream(int j, hipStream_t& out) {
   return KVC_OK;
 }
 
+// Device address of this device's scratch array, looked up on the first call
+// on each device (with that device current) and kept.
+int noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KVC_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(KVC_ERR_HIP, "scratch address %p not usable", p);
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return KVC_OK;
+}
+
 }  // namespace
 
 namespace kvc {
@@ -763,6 +790,29 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
   KVC_TRY(head_table(L, budgets, ht));
   KVC_TRY(check_ws(L, ws, ws_bytes));
   KVC_TRY(check_lds(L));
+  return enqueue_layer(L, q_win, k, v, ht, m_out, z_out, scores_out, idx_out, k_out, v_out, pos_out, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+int kvc_compress_layer_noalloc(const kvc_layer_desc* desc, const void* q_win, const void* k, const void* v,
+                               const int32_t* budgets, float* m_out, float* z_out, float* scores_out,
+                               int32_t* idx_out, void* k_out, void* v_out, int32_t* pos_out,
+                               kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_layer_ptrs(q_win, k, v, idx_out, k_out, v_out, pos_out));
+  if (m_out) KVC_TRY(check_ptr(m_out, 4, "m_out"));
+  if (z_out) KVC_TRY(check_ptr(z_out, 4, "z_out"));
+  if (scores_out) KVC_TRY(check_ptr(scores_out, 4, "scores_out"));
+  HeadTable ht;
+  KVC_TRY(head_table(L, budgets, ht));
+  const size_t need = ws_layout(L).total;
+  if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES)
+    return fail(KVC_ERR_WORKSPACE, "layer needs %zu bytes of workspace; the fixed scratch holds %zu "
+                "(call kvc_compress_layer with a workspace)", need, (size_t)KVC_NOALLOC_SCRATCH_BYTES);
+  KVC_TRY(check_lds(L));
+  void* ws = nullptr;
+  KVC_TRY(noalloc_scratch(&ws));
   return enqueue_layer(L, q_win, k, v, ht, m_out, z_out, scores_out, idx_out, k_out, v_out, pos_out, ws,
                        static_cast<hipStream_t>(stream));
 }

@@ -59,6 +59,7 @@ extern "C" {
 #define KVC_MAX_KV_HEADS 64    /* hkv limit */
 #define KVC_MAX_ROWS 256       /* limit on G * W (query rows per KV head) */
 #define KVC_MAX_POOL 31        /* largest max-pool width */
+#define KVC_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of kvc_compress_layer_noalloc per device */
 
 typedef enum kvc_status {
   KVC_OK = 0,
@@ -265,6 +266,26 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
                        float* m_out, float* z_out, float* scores_out, int32_t* idx_out,
                        void* k_out, void* v_out, int32_t* pos_out,
                        void* ws, size_t ws_bytes, kvc_stream_t stream);
+
+/*
+ * kvc_compress_layer for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same kernels, outputs and argument rules as kvc_compress_layer,
+ * without the ws / ws_bytes arguments: the workspace is a fixed scratch array
+ * of KVC_NOALLOC_SCRATCH_BYTES that the library keeps on every device it runs
+ * on until the process ends (its address is looked up once per device, on
+ * the first call there). Nothing is allocated or freed, by the library or
+ * through another library. Returns KVC_ERR_WORKSPACE, enqueueing nothing,
+ * when kvc_workspace_size(desc) exceeds the scratch. Every call on a device
+ * shares that device's scratch, which keeps the last call's contents (the
+ * kernels clear what they count into): calls that may run at the same time on
+ * one device -- different streams without an order between them, or
+ * different threads -- race and give wrong results, so order them.
+ */
+int kvc_compress_layer_noalloc(const kvc_layer_desc* desc, const void* q_win, const void* k,
+                               const void* v, const int32_t* budgets,
+                               float* m_out, float* z_out, float* scores_out, int32_t* idx_out,
+                               void* k_out, void* v_out, int32_t* pos_out, kvc_stream_t stream);
 
 /*
  * Overlap coefficient between two retained index sets of one layer shape
