@@ -21,7 +21,17 @@
 // The MFMA k-slot assignment matches the per-head scans: at step st, lane
 // half h feeds head-dimension chunk 2*st + h of both operands.
 
+#include <type_traits>
+
 #include "kvc_internal.h"
+
+// 0 selects the job-at-a-time loops everywhere (for comparisons).
+#ifndef KVC_SLOT_PIPE
+#define KVC_SLOT_PIPE 1
+#endif
+#ifndef KVC_LATE_FILL
+#define KVC_LATE_FILL 1
+#endif
 
 namespace kvc {
 namespace {
@@ -202,7 +212,8 @@ __device__ __forceinline__ void copy_offsets(const ScoreArgs& a, int wave, int l
     const int r = p / R::R16, q = p % R::R16;
     const int lc = q ^ (r & (R::XS - 1));
     const int h = lc / R::CPH, c = lc % R::CPH;
-    off[j] = (uint32_t)(((int64_t)r * a.k_tok + (int64_t)h * a.k_head + c * 8) * 2);
+    // the host takes this path only when a slot's span fits in 32 bits
+    off[j] = ((uint32_t)r * (uint32_t)a.k_tok + (uint32_t)h * (uint32_t)a.k_head + (uint32_t)(c * 8)) * 2u;
   }
 }
 
@@ -213,22 +224,20 @@ template <int D, int HG>
 __device__ __forceinline__ void slot_issue(const ScoreArgs& a, int h0, int tok0, int wave, int lane,
                                            const uint32_t* off, unsigned char* dst) {
   using R = Ring<D, HG>;
+  const char* base = reinterpret_cast<const char*>(a.k + (int64_t)tok0 * a.k_tok + (int64_t)h0 * a.k_head);
   if (tok0 + R::TOKS <= a.s) {
-    const char* base = reinterpret_cast<const char*>(a.k + (int64_t)tok0 * a.k_tok + (int64_t)h0 * a.k_head);
 #pragma unroll
     for (int j = 0; j < R::NI; ++j)
       __builtin_amdgcn_global_load_lds(base + off[j], (lds_void*)(dst + (wave * R::NI + j) * 1024), 16, 0, 0);
   } else {
+    // the same copies with the token of every lane past the prompt moved back
+    // to the last key (a copy instruction covers 64 / R16 whole tokens)
+    const int rl = lane / R::R16;
 #pragma unroll
     for (int j = 0; j < R::NI; ++j) {
-      const int p = (wave * R::NI + j) * 64 + lane;
-      const int r = p / R::R16, q = p % R::R16;
-      const int lc = q ^ (r & (R::XS - 1));
-      const int h = lc / R::CPH, c = lc % R::CPH;
-      int tok = tok0 + r;
-      tok = tok < a.s ? tok : a.s - 1;
-      const uint16_t* src = a.k + (int64_t)tok * a.k_tok + (int64_t)(h0 + h) * a.k_head + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (wave * R::NI + j) * 1024), 16, 0, 0);
+      const int tok = tok0 + (wave * R::NI + j) * (64 / R::R16) + rl;
+      const int64_t back = tok < a.s ? 0 : (int64_t)(a.s - 1 - tok) * a.k_tok * 2;
+      __builtin_amdgcn_global_load_lds(base + off[j] + back, (lds_void*)(dst + (wave * R::NI + j) * 1024), 16, 0, 0);
     }
   }
 }
@@ -242,12 +251,18 @@ __device__ __forceinline__ void load_query_regs(const ScoreArgs& a, int head, in
   for (int i = 0; i < NRTW; ++i) {
     const int t = rg + RS * i;
     const int r = t * kRowTile + l32;
+    const bool full = t < nrt && (t + 1) * kRowTile <= a.rows;  // wavefront-uniform
     const bool ok = t < nrt && r < a.rows;
     const int hh = ok ? r / a.w : 0, wi = ok ? r % a.w : 0;
     const uint16_t* src = a.q + (int64_t)wi * a.q_tok + (int64_t)(head * a.g + hh) * a.q_head;
+    if (full) {
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      qr[i][st] = ok ? *reinterpret_cast<const uint4*>(src + (2 * st + half) * 8) : make_uint4(0u, 0u, 0u, 0u);
+      for (int st = 0; st < D / 16; ++st) qr[i][st] = *reinterpret_cast<const uint4*>(src + (2 * st + half) * 8);
+    } else {
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        qr[i][st] = ok ? *reinterpret_cast<const uint4*>(src + (2 * st + half) * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
 }
 
@@ -262,6 +277,39 @@ __device__ __forceinline__ void key_issue(const unsigned char* slot, int hl, int
   for (int st = 0; st < D / 16; ++st) {
     const int chunk = r * R::R16 + ((hl * R::CPH + 2 * st + half) ^ (r & (R::XS - 1)));
     raw[st] = lds_read_b128(slot + chunk * 16);
+  }
+}
+
+// This lane's MFMA operand chunks of key tile kt of head hl in a slot, read
+// and waited for in one statement: the registers are defined only after the
+// wait, so a copy the compiler makes of them can never read a register that an
+// LDS read has not yet written.
+template <int D, int HG>
+__device__ __forceinline__ void key_read(const unsigned char* slot, int hl, int kt, int half, int l32,
+                                         u32x4_t (&kf)[D / 16]) {
+  using R = Ring<D, HG>;
+  const int r = kt * kKeyTile + l32;
+  uint32_t ad[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    ad[st] = lds_addr(slot + (r * R::R16 + ((hl * R::CPH + 2 * st + half) ^ (r & (R::XS - 1)))) * 16);
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]), "=&v"(kf[6]),
+          "=&v"(kf[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+  } else {
+    static_assert(D == 64, "head dimension");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
   }
 }
 
@@ -298,6 +346,244 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
   return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), v[15]));
 }
 
+// x + (x of lane l ^ 32): one swap of the wavefront halves in the VALU (a
+// __shfl_xor is an LDS permute round trip).
+__device__ __forceinline__ float add_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Slot-level software pipeline, for wavefronts that own at most two row
+// tiles: iteration n works through the exponentials of slot n's dot products
+// (already in registers) while the MFMAs of slot n+1 run beside them, the row
+// tiles' MFMA chains alternating so that no MFMA waits for the one before it
+// in its chain. The key fragments of slot n+1 are read from LDS at the top of
+// iteration n and waited for only after the first VALU work of slot n. Per
+// row and per key the arithmetic runs in the same order as one job at a time,
+// so the results are bitwise those of the job-at-a-time form.
+// ---------------------------------------------------------------------------
+
+// MFMA m of a slot (m = step * NRTW + tile) into the next accumulators.
+template <int D, int NRTW, bool KROWS, int M>
+__device__ __forceinline__ void slot_mfma(f32x16_t (&nxt)[NRTW], const uint4 (&qr)[NRTW][D / 16],
+                                          const u32x4_t (&kf)[D / 16]) {
+  constexpr int CH = M % NRTW, ST = M / NRTW;
+  const f32x16_t c = ST == 0 ? f32x16_t{} : nxt[CH];
+  const uint4 k = __builtin_bit_cast(uint4, kf[ST]);
+  nxt[CH] = KROWS ? mfma32x32x16(k, qr[CH][ST], c) : mfma32x32x16(qr[CH][ST], k, c);
+}
+
+// Scheduling pattern of a slot's arithmetic: NMF groups of one MFMA followed
+// by the VALU and transcendental instructions of its logits, so that the
+// matrix pipe and the VALU of one wavefront run side by side. (Without it the
+// scheduler issued half of the MFMAs back to back and left a row tile's
+// exponentials for after the last one.)
+template <int NMF, int NVALU, int NTRANS>
+__device__ __forceinline__ void slot_schedule() {
+#pragma unroll
+  for (int m = 0; m < NMF; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x400, NTRANS, 0);  // v_exp
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);   // other VALU
+  }
+}
+
+template <int... I>
+struct Seq {};
+template <int N, int... I>
+struct MakeSeq : MakeSeq<N - 1, N - 1, I...> {};
+template <int... I>
+struct MakeSeq<0, I...> {
+  using type = Seq<I...>;
+};
+
+// One group of a slot's arithmetic, in this order: the MFMA of the next
+// slot's contraction (FIRST: its chain starts from zero) and, for two logits
+// x0, x1 of the current slot, p = 2^(x * c - b) added to s0 and s1. Inline
+// assembly fixes the interleaving (the compiler's scheduler issued the MFMAs
+// back to back and the exponentials after them). Every exponential has one
+// instruction between it and the add that reads it; the hazards with the
+// MFMAs are covered by slot_nops() before the first and after the last group
+// of a slot.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_exp_group(f32x16_t& acc, const uint4& qa, const u32x4_t& kb, bool krows,
+                                               float x0, float x1, float b0, float b1, float c, float& s0,
+                                               float& s1) {
+  float t0, t1;
+  const u32x4_t q = __builtin_bit_cast(u32x4_t, qa);
+  const u32x4_t A = krows ? kb : q, B = krows ? q : kb;
+  if constexpr (FIRST) {
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %5, %6, 0\n\t"
+        "v_fma_f32 %3, %7, %11, -%9\n\t"
+        "v_fma_f32 %4, %8, %11, -%10\n\t"
+        "v_exp_f32 %3, %3\n\t"
+        "v_exp_f32 %4, %4\n\t"
+        "v_add_f32 %1, %1, %3\n\t"
+        "v_add_f32 %2, %2, %4"
+        : "=&v"(acc), "+v"(s0), "+v"(s1), "=&v"(t0), "=&v"(t1)
+        : "v"(A), "v"(B), "v"(x0), "v"(x1), "v"(b0), "v"(b1), "s"(c));
+  } else {
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %5, %6, %0\n\t"
+        "v_fma_f32 %3, %7, %11, -%9\n\t"
+        "v_fma_f32 %4, %8, %11, -%10\n\t"
+        "v_exp_f32 %3, %3\n\t"
+        "v_exp_f32 %4, %4\n\t"
+        "v_add_f32 %1, %1, %3\n\t"
+        "v_add_f32 %2, %2, %4"
+        : "+v"(acc), "+v"(s0), "+v"(s1), "=&v"(t0), "=&v"(t1)
+        : "v"(A), "v"(B), "v"(x0), "v"(x1), "v"(b0), "v"(b1), "s"(c));
+  }
+}
+
+// As mfma_exp_group without the MFMA (a slot's first logits in pass 2) or
+// without the logits (its last MFMA).
+__device__ __forceinline__ void exp_group(float x0, float x1, float b0, float b1, float c, float& s0, float& s1) {
+  float t0, t1;
+  asm volatile(
+      "v_fma_f32 %2, %4, %8, -%6\n\t"
+      "v_fma_f32 %3, %5, %8, -%7\n\t"
+      "v_exp_f32 %2, %2\n\t"
+      "v_exp_f32 %3, %3\n\t"
+      "v_add_f32 %0, %0, %2\n\t"
+      "v_add_f32 %1, %1, %3"
+      : "+v"(s0), "+v"(s1), "=&v"(t0), "=&v"(t1)
+      : "v"(x0), "v"(x1), "v"(b0), "v"(b1), "s"(c));
+}
+
+__device__ __forceinline__ void mfma_group(f32x16_t& acc, const uint4& qa, const u32x4_t& kb, bool krows) {
+  const u32x4_t q = __builtin_bit_cast(u32x4_t, qa);
+  const u32x4_t A = krows ? kb : q, B = krows ? q : kb;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(A), "v"(B));
+}
+
+// 24 wait states: more than any MFMA-result or MFMA-operand hazard needs, so
+// that code the compiler places around a slot's groups never sees one.
+__device__ __forceinline__ void slot_nops() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+// The prologue's contraction of slot 0 in the same alternating order.
+template <int D, int NRTW, bool KROWS, int... M>
+__device__ __forceinline__ void slot_contract(f32x16_t (&acc)[NRTW], const uint4 (&qr)[NRTW][D / 16],
+                                              const u32x4_t (&kf)[D / 16], Seq<M...>) {
+  (slot_mfma<D, NRTW, KROWS, M>(acc, qr, kf), ...);
+}
+
+// Pass 1, slot n: cur holds its dot products (key rows x query columns); the
+// lane's query row of tile i sits at prompt position qpos[i].
+template <int D, int NRTW, bool EDGE, int... M>
+__device__ __forceinline__ void pass1_slot(const ScoreArgs& a, f32x16_t (&cur)[NRTW], f32x16_t (&nxt)[NRTW],
+                                           const uint4 (&qr)[NRTW][D / 16], u32x4_t (&kf)[D / 16],
+                                           int kbase, int half, const int (&qpos)[NRTW],
+                                           float (&mrun)[NRTW], float (&zrun)[NRTW], Seq<M...>) {
+  constexpr int LPM = 16 / (D / 16);  // logits of the tile-major sequence per MFMA
+  float mnew[NRTW], mc[NRTW], s0[NRTW], s1[NRTW];
+  bool dead[NRTW];
+#pragma unroll
+  for (int i = 0; i < NRTW; ++i) {
+    if constexpr (EDGE) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key >= a.s || key > qpos[i]) cur[i][e] = -INFINITY;
+      }
+    }
+    mnew[i] = fmaxf(mrun[i], max16(cur[i]));
+    dead[i] = EDGE && mnew[i] == -INFINITY;  // every key masked: contributes nothing
+    mc[i] = dead[i] ? 0.f : mnew[i] * a.c;
+    s0[i] = 0.f;
+    s1[i] = 0.f;
+  }
+  slot_nops();
+  auto group = [&](auto m_tag) {
+    constexpr int MM = decltype(m_tag)::value;
+    constexpr int CH = MM % NRTW, ST = MM / NRTW;
+#pragma unroll
+    for (int j = 0; j < LPM; j += 2) {
+      const int L = MM * LPM + j, t = L / 16, e = L % 16;
+      if (j == 0)
+        mfma_exp_group<ST == 0>(nxt[CH], qr[CH][ST], kf[ST], true, cur[t][e], cur[t][e + 1], mc[t], mc[t], a.c,
+                                s0[t], s1[t]);
+      else
+        exp_group(cur[t][e], cur[t][e + 1], mc[t], mc[t], a.c, s0[t], s1[t]);
+    }
+  };
+  (group(std::integral_constant<int, M>{}), ...);
+  slot_nops();
+#pragma unroll
+  for (int i = 0; i < NRTW; ++i) {
+    if (!dead[i]) {
+      zrun[i] = zrun[i] * exp2_raw((mrun[i] - mnew[i]) * a.c) + (s0[i] + s1[i]);
+      mrun[i] = mnew[i];
+    }
+  }
+}
+
+// Pass 2, slot n: cur holds its dot products (query rows x key columns); the
+// lane's key is `key`; returns the key's weight summed over this wavefront's
+// rows (both lane halves).
+template <int D, int NRTW, int RS, bool EDGE, int... M>
+__device__ __forceinline__ float pass2_slot(const ScoreArgs& a, const f32x16_t (&cur)[NRTW], f32x16_t (&nxt)[NRTW],
+                                            const uint4 (&qr)[NRTW][D / 16], u32x4_t (&kf)[D / 16],
+                                            const float (&breg)[NRTW][16], const int* qpos,
+                                            int rg, int key, int half, Seq<M...>) {
+  constexpr int NMF = NRTW * (D / 16);
+  constexpr int LPM = 16 / (D / 16);
+  float s0 = 0.f, s1 = 0.f;
+  if constexpr (!EDGE) {
+    slot_nops();
+#pragma unroll
+    for (int j = 0; j < LPM; j += 2) exp_group(cur[0][j], cur[0][j + 1], breg[0][j], breg[0][j + 1], a.c, s0, s1);
+    auto group = [&](auto m_tag) {
+      constexpr int MM = decltype(m_tag)::value;
+      constexpr int CH = MM % NRTW, ST = MM / NRTW;
+      if constexpr (MM + 1 < NMF) {
+#pragma unroll
+        for (int j = 0; j < LPM; j += 2) {
+          const int L = (MM + 1) * LPM + j, t = L / 16, e = L % 16;
+          if (j == 0)
+            mfma_exp_group<ST == 0>(nxt[CH], qr[CH][ST], kf[ST], false, cur[t][e], cur[t][e + 1], breg[t][e],
+                                    breg[t][e + 1], a.c, s0, s1);
+          else
+            exp_group(cur[t][e], cur[t][e + 1], breg[t][e], breg[t][e + 1], a.c, s0, s1);
+        }
+      } else {
+        mfma_group(nxt[CH], qr[CH][ST], kf[ST], false);
+      }
+    };
+    (group(std::integral_constant<int, M>{}), ...);
+    slot_nops();
+    return add_other_half(s0 + s1);
+  }
+  auto logits = [&](int m) {
+#pragma unroll
+    for (int j = 0; j < LPM; j += 2) {
+      const int L = m * LPM + j, t = L / 16, e = L % 16;
+      float p0 = exp2_raw(fmaf(cur[t][e], a.c, -breg[t][e]));
+      float p1 = exp2_raw(fmaf(cur[t][e + 1], a.c, -breg[t][e + 1]));
+      if constexpr (EDGE) {
+        // positions of the query rows (e, e + 1 share a group of four), read
+        // when needed: edge slots are rare and registers are not
+        u32x4_t qq[1] = {lds_read_b128(qpos + (rg + RS * t) * kRowTile + 4 * half + 8 * (e >> 2))};
+        lds_settle(qq);
+        if (key >= a.s || key > (int)qq[0][e & 3]) p0 = 0.f;
+        if (key >= a.s || key > (int)qq[0][(e + 1) & 3]) p1 = 0.f;
+      }
+      s0 += p0;
+      s1 += p1;
+    }
+  };
+  logits(0);
+  auto group = [&](auto m_tag) {
+    constexpr int MM = decltype(m_tag)::value;
+    slot_mfma<D, NRTW, false, MM>(nxt, qr, kf);
+    if constexpr (MM + 1 < NMF) logits(MM + 1);
+  };
+  (group(std::integral_constant<int, M>{}), ...);
+  return add_other_half(s0 + s1);
+}
+
 struct Range {
   int t0, nst;  // first token, slots
   int toks;     // tokens per slot
@@ -317,13 +603,33 @@ __device__ __forceinline__ Range wg_range(const ScoreArgs& a, int split, int tok
   return r;
 }
 
-// Ring prologue: copies of slots 0 .. kRingSlots-2.
+// Ring prologue: copies of slots n0 .. kRingSlots-2 (slot 0 goes out first,
+// before the query loads, so that a workgroup's first data is requested as
+// early as possible; slots 1 and 2 follow them).
 template <int D, int HG>
 __device__ __forceinline__ void ring_fill(const ScoreArgs& a, int h0, const Range& rg, int wave, int lane,
-                                          const uint32_t* off, unsigned char* smem) {
+                                          const uint32_t* off, unsigned char* smem, int n0 = 0, int n1 = kRingSlots - 1) {
 #pragma unroll
   for (int n = 0; n < kRingSlots - 1; ++n)
+    if (n >= n0 && n < n1 && n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
+}
+
+// Late fill: the prologue requested slot 0 only (with the query rows), so
+// that each workgroup's first data returns before the bulk of the other
+// workgroups' requests; once slot 0 is in for the whole workgroup, slots 1 ..
+// kRingSlots-1 go out together.
+template <int D, int HG>
+__device__ __forceinline__ void ring_start(const ScoreArgs& a, int h0, const Range& rg, int wave, int lane,
+                                           const uint32_t* off, unsigned char* smem) {
+  lds_barrier();
+#pragma unroll
+  for (int n = 1; n < kRingSlots; ++n)
     if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
+}
+
+// Slots issued after the query loads by the prologue (slots 1 and 2).
+__device__ __forceinline__ int slots_after_queries(const Range& rg) {
+  return rg.nst < kRingSlots - 1 ? (rg.nst > 1 ? rg.nst - 1 : 0) : kRingSlots - 2;
 }
 
 // Top of ring iteration n: slot n has landed for the whole workgroup, and
@@ -455,12 +761,15 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
   if (a.hist != nullptr && split == 0)
     for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x) a.hist[(int64_t)h0 * kHistBins + i] = 0u;
 
+  constexpr bool PIPE = NRT % R::RS == 0;
+  constexpr bool SLOT_PIPE = PIPE && NRTW <= 2 && KVC_SLOT_PIPE;
   uint32_t off[R::NI];
   copy_offsets<D, HG>(a, wave, lane, off);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
   uint4 qr[NRTW][D / 16];
   load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem);
-  vm_settle_after<R::NI>(qr, min(rg.nst, kRingSlots - 1));
+  if constexpr (!SLOT_PIPE || !KVC_LATE_FILL) ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, SLOT_PIPE && KVC_LATE_FILL ? 0 : slots_after_queries(rg));
 
   float mrun[NRTW], zrun[NRTW];
   int qpos[NRTW];
@@ -472,8 +781,37 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
     qpos[i] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
   }
 
-  constexpr bool PIPE = NRT % R::RS == 0;
-  if constexpr (PIPE) {
+  if constexpr (SLOT_PIPE) {
+    using Ms = typename MakeSeq<NRTW * (D / 16)>::type;
+    const int kt_off = ro.kt * kKeyTile;
+    u32x4_t kf[D / 16];
+    f32x16_t accA[NRTW], accB[NRTW];
+    if (rg.nst > 0) {
+      if constexpr (KVC_LATE_FILL) ring_start<D, HG>(a, h0, rg, wave, lane, off, smem);
+      else ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
+      key_read<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
+      using M0 = typename MakeSeq<NRTW * (D / 16)>::type;
+      slot_contract<D, NRTW, true>(accA, qr, kf, M0{});
+    }
+    // slot n: its dot products in cur; the MFMAs of slot n+1 go to nxt (on
+    // the last slot they redo slot n's keys into accumulators never read)
+    auto step = [&](int n, f32x16_t (&cur)[NRTW], f32x16_t (&nxt)[NRTW]) {
+      const int kbase = rg.tok(n) + kt_off;
+      // the last slot re-reads its own fragments (its buffer is not refilled)
+      // so that the fragment registers are redefined in every iteration
+      const bool more = n + 1 < rg.nst;
+      if (more) ring_advance<D, HG>(a, h0, rg, n + 1, wave, lane, off, smem);
+      key_read<D, HG>(smem + ((more ? n + 1 : n) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, kf);
+      if (kbase + kKeyTile > first_hidden)
+        pass1_slot<D, NRTW, true>(a, cur, nxt, qr, kf, kbase, half, qpos, mrun, zrun, Ms{});
+      else
+        pass1_slot<D, NRTW, false>(a, cur, nxt, qr, kf, kbase, half, qpos, mrun, zrun, Ms{});
+    };
+    for (int n = 0; n < rg.nst; n += 2) {
+      step(n, accA, accB);
+      if (n + 1 < rg.nst) step(n + 1, accB, accA);
+    }
+  } else if constexpr (PIPE) {
     // Jobs (slot n, row tile i) in order; the MFMAs of each job run beside
     // the VALU work of the one before, across slot boundaries too. Jobs past
     // the prompt compute on clamped keys and are masked out.
@@ -682,6 +1020,7 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
 
   uint32_t off[R::NI];
   copy_offsets<D, HG>(a, wave, lane, off);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
   uint4 qr[NRTW][D / 16];
   load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
   // this thread's normaliser (one bias entry per thread)
@@ -698,8 +1037,9 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
       real_row = true;
     }
   }
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem);
-  vm_settle_after<R::NI>(qr, min(rg.nst, kRingSlots - 1));
+  constexpr bool SLOT_PIPE = NRT % R::RS == 0 && NRTW <= 2 && KVC_SLOT_PIPE;
+  if constexpr (!SLOT_PIPE || !KVC_LATE_FILL) ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, SLOT_PIPE && KVC_LATE_FILL ? 0 : slots_after_queries(rg));
   vm_settle(mv);
   vm_settle(zv);
 
@@ -735,10 +1075,10 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
     }
   };
 
-  // this lane's row biases of its row tiles, once
+  // this lane's row biases of its row tiles, once, after a barrier that makes
+  // every thread's bias entry visible
   float breg[NRTW][16];
-  if constexpr (NRTW <= 2) {
-    lds_barrier();
+  auto load_breg = [&]() {
 #pragma unroll
     for (int i = 0; i < NRTW; ++i) {
       const int o = (ro.rg + R::RS * i) * kRowTile + 4 * half;
@@ -751,7 +1091,47 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) breg[i][4 * q4 + e4] = __uint_as_float(bq[q4][e4]);
     }
+  };
+  if constexpr (NRTW <= 2 && !SLOT_PIPE) {
+    lds_barrier();
+    load_breg();
   }
+  if constexpr (SLOT_PIPE) {
+    using Ms = typename MakeSeq<NRTW * (D / 16)>::type;
+    u32x4_t kf[D / 16];
+    f32x16_t accA[NRTW], accB[NRTW];
+    if (rg.nst > 0) {
+      // (the first barrier also publishes the biases)
+      if constexpr (KVC_LATE_FILL) ring_start<D, HG>(a, h0, rg, wave, lane, off, smem);
+      else ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
+      load_breg();
+      key_read<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
+      slot_contract<D, NRTW, false>(accA, qr, kf, Ms{});
+    }
+    auto step = [&](int n, f32x16_t (&cur)[NRTW], f32x16_t (&nxt)[NRTW]) {
+      const int kbase = rg.tok(n) + ro.kt * kKeyTile;
+      const int key = kbase + l32;
+      // the last slot re-reads its own fragments (its buffer is not refilled)
+      // so that the fragment registers are redefined in every iteration
+      const bool more = n + 1 < rg.nst;
+      if (more) ring_advance<D, HG>(a, h0, rg, n + 1, wave, lane, off, smem);
+      else if constexpr (R::RS > 1) lds_barrier();  // the other row groups' partial sums of slot n-1
+      key_read<D, HG>(smem + ((more ? n + 1 : n) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, kf);
+      const float sum = kbase + kKeyTile > first_hidden
+                            ? pass2_slot<D, NRTW, R::RS, true>(a, cur, nxt, qr, kf, breg, qpos, ro.rg, key, half, Ms{})
+                            : pass2_slot<D, NRTW, R::RS, false>(a, cur, nxt, qr, kf, breg, qpos, ro.rg, key, half, Ms{});
+      if constexpr (R::RS > 1) {
+        if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
+        if (n > 0) finish(n - 1);
+      } else {
+        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum);
+      }
+    };
+    for (int n = 0; n < rg.nst; n += 2) {
+      step(n, accA, accB);
+      if (n + 1 < rg.nst) step(n + 1, accB, accA);
+    }
+  } else {
   for (int n = 0; n < rg.nst; ++n) {
     ring_advance<D, HG>(a, h0, rg, n, wave, lane, off, smem);
     if constexpr (R::RS > 1) {
@@ -772,6 +1152,7 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
         if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum);
       }
     }
+  }
   }
   if constexpr (R::RS > 1) {
     lds_barrier();
