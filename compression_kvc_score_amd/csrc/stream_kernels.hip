@@ -29,9 +29,6 @@
 #ifndef KVC_SLOT_PIPE
 #define KVC_SLOT_PIPE 1
 #endif
-#ifndef KVC_LATE_FILL
-#define KVC_LATE_FILL 1
-#endif
 
 namespace kvc {
 namespace {
@@ -614,19 +611,6 @@ __device__ __forceinline__ void ring_fill(const ScoreArgs& a, int h0, const Rang
     if (n >= n0 && n < n1 && n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
 }
 
-// Late fill: the prologue requested slot 0 only (with the query rows), so
-// that each workgroup's first data returns before the bulk of the other
-// workgroups' requests; once slot 0 is in for the whole workgroup, slots 1 ..
-// kRingSlots-1 go out together.
-template <int D, int HG>
-__device__ __forceinline__ void ring_start(const ScoreArgs& a, int h0, const Range& rg, int wave, int lane,
-                                           const uint32_t* off, unsigned char* smem) {
-  lds_barrier();
-#pragma unroll
-  for (int n = 1; n < kRingSlots; ++n)
-    if (n < rg.nst) slot_issue<D, HG>(a, h0, rg.tok(n), wave, lane, off, smem + n * kSlotBytes);
-}
-
 // Slots issued after the query loads by the prologue (slots 1 and 2).
 __device__ __forceinline__ int slots_after_queries(const Range& rg) {
   return rg.nst < kRingSlots - 1 ? (rg.nst > 1 ? rg.nst - 1 : 0) : kRingSlots - 2;
@@ -768,8 +752,8 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
   ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
   uint4 qr[NRTW][D / 16];
   load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
-  if constexpr (!SLOT_PIPE || !KVC_LATE_FILL) ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
-  vm_settle_after<R::NI>(qr, SLOT_PIPE && KVC_LATE_FILL ? 0 : slots_after_queries(rg));
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
 
   float mrun[NRTW], zrun[NRTW];
   int qpos[NRTW];
@@ -787,8 +771,7 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
     u32x4_t kf[D / 16];
     f32x16_t accA[NRTW], accB[NRTW];
     if (rg.nst > 0) {
-      if constexpr (KVC_LATE_FILL) ring_start<D, HG>(a, h0, rg, wave, lane, off, smem);
-      else ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
+      ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
       key_read<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
       using M0 = typename MakeSeq<NRTW * (D / 16)>::type;
       slot_contract<D, NRTW, true>(accA, qr, kf, M0{});
@@ -1038,8 +1021,8 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
     }
   }
   constexpr bool SLOT_PIPE = NRT % R::RS == 0 && NRTW <= 2 && KVC_SLOT_PIPE;
-  if constexpr (!SLOT_PIPE || !KVC_LATE_FILL) ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
-  vm_settle_after<R::NI>(qr, SLOT_PIPE && KVC_LATE_FILL ? 0 : slots_after_queries(rg));
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
   vm_settle(mv);
   vm_settle(zv);
 
@@ -1102,8 +1085,7 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
     f32x16_t accA[NRTW], accB[NRTW];
     if (rg.nst > 0) {
       // (the first barrier also publishes the biases)
-      if constexpr (KVC_LATE_FILL) ring_start<D, HG>(a, h0, rg, wave, lane, off, smem);
-      else ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
+      ring_advance<D, HG>(a, h0, rg, 0, wave, lane, off, smem);
       load_breg();
       key_read<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
       slot_contract<D, NRTW, false>(accA, qr, kf, Ms{});
