@@ -72,6 +72,7 @@ class LayerPlan(ctypes.Structure):
         ("heads_per_wg", ctypes.c_int32),
         ("splits", ctypes.c_int32),
         ("hist_in_scan", ctypes.c_int32),
+        ("fused_scans", ctypes.c_int32),
         ("keys_per_wg", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
     ]

@@ -3,12 +3,15 @@
 // check runs before the first launch of a call.
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <random>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -78,6 +81,52 @@ bool stream_scans_enabled() {
     return !(e && e[0] == '0');
   }();
   return v;
+}
+
+// KVC_FUSED=0 keeps the streaming scans as separate launches (pass 1, the
+// split combine, pass 2) even where one fused launch would do.
+bool fused_scans_enabled() {
+  static const bool v = [] {
+    const char* e = std::getenv("KVC_FUSED");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+
+// Compute units of the current device (0 if it cannot be read), cached per device.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
+// A fresh 64-bit stamp per fused launch: successive values of the SplitMix64
+// sequence (Steele, Lea, Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014) from a seed drawn once per process, so that no
+// flag left in a workspace by an earlier launch, or by other data, matches.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> ctr{[] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ rd() ^ (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }()};
+  uint64_t x = ctr.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// The layer's scans run as one launch (softmax scores, streaming scans,
+// every workgroup resident at once).
+bool use_fused_scans(const Layer& L) {
+  if (L.score_mode != KVC_SCORE_SOFTMAX || L.stream_hg == 0 || !fused_scans_enabled()) return false;
+  const int cus = device_cus();
+  return cus > 0 && stream_fused_ok(L, std::min(cus, kMaxFusedWgs));
 }
 
 int normalize(const kvc_layer_desc* d, Layer& L) {
@@ -195,7 +244,7 @@ int n_chunks(const Layer& L) { return (int)((L.s + kSelectChunk - 1) / kSelectCh
 int n_subs(const Layer& L) { return (int)((L.s + kSub - 1) / kSub); }
 
 struct WsLayout {
-  size_t part, m, z, scores, pooled;
+  size_t sync, part, m, z, scores, pooled;
   size_t hist, slots;
   size_t total;
 };
@@ -204,6 +253,8 @@ WsLayout ws_layout(const Layer& L) {
   WsLayout w{};
   size_t off = 0;
   const size_t nc = (size_t)n_chunks(L);
+  w.sync = off;  // arrival flags of the fused scans (stamped per launch: never cleared)
+  off += align_up(kSyncBytes, 256);
   w.hist = off;
   off += align_up((size_t)L.hkv * kHistBins * 4, 256);
   w.slots = off;
@@ -431,11 +482,15 @@ int check_layer_ptrs(const void* q_win, const void* k, const void* v, const int3
 
 // One validated layer onto one stream; m, z, scores NULL: in the workspace.
 // pos_in non-null: retained positions are looked up there (per head, stride
-// pos_in_head) instead of pos_offset + index.
+// pos_in_head) instead of pos_offset + index. scan_gate non-null: a fused
+// scan launch waits for the event's last record and records it afterwards,
+// so that the fused scans of calls on several streams never overlap (their
+// workgroups wait for each other and must all be resident).
 int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* v, const HeadTable& ht,
                   float* m_out, float* z_out, float* scores_out, int32_t* idx_out, void* k_out,
                   void* v_out, int32_t* pos_out, void* ws, hipStream_t st,
-                  const int32_t* pos_in = nullptr, int64_t pos_in_head = 0) {
+                  const int32_t* pos_in = nullptr, int64_t pos_in_head = 0,
+                  hipEvent_t scan_gate = nullptr) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
@@ -457,8 +512,31 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
     return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
                       pos_in_head);
   }
-  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
-  KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
+  if (use_fused_scans(L)) {
+    ScoreArgs a = score_args(L, q_win, k);
+    a.part = reinterpret_cast<float*>(wsb + lay.part);
+    if (hist_in_pass2) a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+    a.m_out = m;
+    a.z_out = z;
+    a.m_in = m;
+    a.z_in = z;
+    a.scores = sc;
+    a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
+    a.epoch = next_epoch();
+    if (scan_gate != nullptr) {
+      const hipError_t e = hipStreamWaitEvent(st, scan_gate, 0);
+      if (e != hipSuccess) return hip_fail(e, "scan gate wait");
+    }
+    hipError_t e = launch_stream_fused(L, a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused scan launch");
+    if (scan_gate != nullptr) {
+      e = hipEventRecord(scan_gate, st);
+      if (e != hipSuccess) return hip_fail(e, "scan gate record");
+    }
+  } else {
+    KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
+    KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
+  }
   // the compaction of the selection copies the retained rows as it goes
   return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
                     pos_in_head);
@@ -661,6 +739,7 @@ int kvc_plan_layer(const kvc_layer_desc* desc, kvc_layer_plan* plan) {
     p.splits = L.n_split;
     p.keys_per_wg = L.stream_hg ? stream_keys_per_wg(L) : (int64_t)L.blocks_per_wg * L.block;
     p.hist_in_scan = L.pool == 1 && hist_fits_scan(L);
+    p.fused_scans = use_fused_scans(L);
   }
   p.workspace_bytes = ws_layout(L).total;
   *plan = p;
@@ -870,12 +949,22 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
   for (int j = 1; j < kSweepStreams && e == hipSuccess; ++j) e = hipStreamWaitEvent(lanes[j], ev, 0);
   (void)hipEventDestroy(ev);
   if (e != hipSuccess) return hip_fail(e, "sweep fork");
-  int status = KVC_OK;
+  // fused scans of successive layers run one after another (each needs the
+  // whole device resident); the selections still overlap the next scan
+  hipEvent_t gate = nullptr;
+  if (use_fused_scans(L)) {
+    e = hipEventCreateWithFlags(&gate, hipEventDisableTiming);
+    if (e != hipSuccess) gate = nullptr;
+    else e = hipEventRecord(gate, lanes[0]);  // recorded before the first wait
+  }
+  int status = e == hipSuccess ? KVC_OK : hip_fail(e, "sweep scan gate");
   for (int32_t i = 0; i < n_layers && status == KVC_OK; ++i) {
     const int j = i % kSweepStreams;
     status = enqueue_layer(L, q_win[i], k[i], v[i], hts[(size_t)i], nullptr, nullptr, nullptr, idx_out[i],
-                           k_out[i], v_out[i], pos_out[i], static_cast<char*>(ws) + j * one, lanes[j]);
+                           k_out[i], v_out[i], pos_out[i], static_cast<char*>(ws) + j * one, lanes[j], nullptr, 0,
+                           gate);
   }
+  if (gate != nullptr) (void)hipEventDestroy(gate);
   // join: later work on the caller's stream waits for every lane (also after
   // a failed launch, so that nothing of this call outlives the caller's order)
   for (int j = 1; j < kSweepStreams; ++j) {

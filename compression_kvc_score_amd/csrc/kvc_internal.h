@@ -60,7 +60,14 @@ struct ScoreArgs {
   float* scores;    // [hkv][s]
   uint32_t* hist;   // [hkv][kHistBins]: pass 1 clears it, pass 2 fills it (null: skip)
   int sink_end, rec_begin;  // candidate keys [sink_end, rec_begin) for the histogram
+  // fused scans only: arrival flags [2][workgroups], stamped with the launch's
+  // epoch (a value no earlier launch used), so they need no clearing
+  uint64_t* sync;
+  uint64_t epoch;
 };
+
+constexpr int kMaxFusedWgs = 1024;  // workgroups of one fused scan launch (one per compute unit)
+constexpr size_t kSyncBytes = (size_t)2 * kMaxFusedWgs * sizeof(uint64_t);
 
 // Arguments of the raw inner-product scan (score modes other than softmax).
 struct LogitArgs {
@@ -186,6 +193,11 @@ bool stream_offsets_fit(const Layer& L, int hg);  // a slot's copy offsets fit i
 size_t pass1_stream_lds_bytes(const Layer& L);
 size_t pass2_stream_lds_bytes(const Layer& L);
 hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStream_t st);
+// Both streaming scans and the split combine in one launch (a.sync, a.epoch
+// set): true when the layer's shape has a fused kernel and its workgroups
+// can all be resident at once on a device of `cus` compute units.
+bool stream_fused_ok(const Layer& L, int cus);
+hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, hipStream_t st);
 
 // Dynamic LDS bytes of the scans.
 size_t pass1_lds_bytes(const Layer& L);

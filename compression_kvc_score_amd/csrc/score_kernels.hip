@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(512) pass2_kernel(ScoreArgs a) {
     if (r < a.rows) {
       const int hh = r / a.w, i = r % a.w;
       const int64_t o = (int64_t)(head * a.g + hh) * a.w + i;
-      bv = a.m_in[o] * kLog2e + __log2f(a.z_in[o]);
+      bv = fmaf(a.m_in[o], kLog2e, __log2f(a.z_in[o]));
     }
     bias[r] = bv;
   }

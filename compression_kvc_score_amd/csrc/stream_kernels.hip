@@ -21,6 +21,7 @@
 // The MFMA k-slot assignment matches the per-head scans: at step st, lane
 // half h feeds head-dimension chunk 2*st + h of both operands.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kvc_internal.h"
@@ -724,47 +725,49 @@ __device__ __forceinline__ void pass1_tile(const ScoreArgs& a, const uint4 (&qr)
   }
 }
 
+// A streaming-scan workgroup: its head group and token split, and the
+// roles of this thread's wavefront.
+template <int D, int HG>
+struct WgCtx {
+  int grp, split, h0, lane, wave, half, l32, head, ntile, first_hidden;
+  Role ro;
+};
+
 template <int D, int NRT, int HG>
-__global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
+__device__ __forceinline__ WgCtx<D, HG> wg_ctx(const ScoreArgs& a) {
+  using R = Ring<D, HG>;
+  WgCtx<D, HG> c;
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  c.grp = work / a.n_split;
+  c.split = work % a.n_split;
+  c.h0 = c.grp * HG;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront-uniform: SGPRs
+  c.half = c.lane >> 5;
+  c.l32 = c.lane & 31;
+  c.ro = role_of<D, HG>(c.wave);
+  c.head = c.h0 + c.ro.hl;
+  c.ntile = (NRT - c.ro.rg + R::RS - 1) / R::RS;  // the last row groups may own one fewer
+  c.first_hidden = a.s - a.w + 1;
+  return c;
+}
+
+// The pass-1 loop over a workgroup's slots: online (max, sum of
+// exponentials) of every row the wavefront owns, per lane.
+template <int D, int NRT, int HG>
+__device__ __forceinline__ void pass1_loops(const ScoreArgs& a, const WgCtx<D, HG>& c, const Range& rg,
+                                            const uint32_t* off, unsigned char* smem,
+                                            const uint4 (&qr)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS][D / 16],
+                                            const int (&qpos)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS],
+                                            float (&mrun)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS],
+                                            float (&zrun)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS]) {
   using R = Ring<D, HG>;
   constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
-  constexpr int ROWS_PAD = NRT * kRowTile;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = work / a.n_split, split = work % a.n_split;
-  const int h0 = grp * HG;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront-uniform: SGPRs
-  const int half = lane >> 5, l32 = lane & 31;
-  const Role ro = role_of<D, HG>(wave);
-  const int head = h0 + ro.hl;
-  const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;  // the last row groups may own one fewer
-  const int first_hidden = a.s - a.w + 1;
-  const Range rg = wg_range(a, split, R::TOKS, false);
-
-  if (a.hist != nullptr && split == 0)
-    for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x) a.hist[(int64_t)h0 * kHistBins + i] = 0u;
-
   constexpr bool PIPE = NRT % R::RS == 0;
   constexpr bool SLOT_PIPE = PIPE && NRTW <= 2 && KVC_SLOT_PIPE;
-  uint32_t off[R::NI];
-  copy_offsets<D, HG>(a, wave, lane, off);
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
-  uint4 qr[NRTW][D / 16];
-  load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
-  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
-
-  float mrun[NRTW], zrun[NRTW];
-  int qpos[NRTW];
-#pragma unroll
-  for (int i = 0; i < NRTW; ++i) {
-    mrun[i] = -INFINITY;
-    zrun[i] = 0.f;
-    const int r = (ro.rg + R::RS * i) * kRowTile + l32;
-    qpos[i] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
-  }
-
+  const int h0 = c.h0, wave = c.wave, lane = c.lane, half = c.half, l32 = c.l32, ntile = c.ntile;
+  const int first_hidden = c.first_hidden;
+  const Role ro = c.ro;
   if constexpr (SLOT_PIPE) {
     using Ms = typename MakeSeq<NRTW * (D / 16)>::type;
     const int kt_off = ro.kt * kKeyTile;
@@ -846,6 +849,20 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
     }
   }
 
+}
+
+// Pass-1 epilogue: merge the lanes and wavefronts that share rows and write
+// the workgroup's partial (max, sum) of every row (COHERENT: stores that
+// other workgroups of the same launch can read).
+template <int D, int NRT, int HG, bool COHERENT>
+__device__ __forceinline__ void pass1_finish(const ScoreArgs& a, const WgCtx<D, HG>& c, unsigned char* smem,
+                                             float (&mrun)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS],
+                                             float (&zrun)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS]) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
+  constexpr int ROWS_PAD = NRT * kRowTile;
+  const int h0 = c.h0, split = c.split, half = c.half, l32 = c.l32, ntile = c.ntile;
+  const Role ro = c.ro;
   // lanes l and l+32 share a query row; then the KT wavefronts of a head
   // that own the same rows
 #pragma unroll
@@ -870,8 +887,49 @@ __global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
       const float2 p = red[(h * R::KT + k) * ROWS_PAD + r];
       lse_merge(m, z, p.x, p.y, a.c);
     }
-    reinterpret_cast<float2*>(a.part)[((int64_t)(h0 + h) * a.n_split + split) * ROWS_PAD + r] = make_float2(m, z);
+    float2* dst = reinterpret_cast<float2*>(a.part) + ((int64_t)(h0 + h) * a.n_split + split) * ROWS_PAD + r;
+    if constexpr (COHERENT)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), __builtin_bit_cast(uint64_t, make_float2(m, z)),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *dst = make_float2(m, z);
   }
+}
+
+template <int D, int NRT, int HG>
+__global__ void __launch_bounds__(8 * kWave) pass1_stream_kernel(ScoreArgs a) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const WgCtx<D, HG> c = wg_ctx<D, NRT, HG>(a);
+  const int split = c.split, h0 = c.h0, lane = c.lane, wave = c.wave, half = c.half, l32 = c.l32;
+  const Role ro = c.ro;
+  const int head = c.head;
+  const Range rg = wg_range(a, split, R::TOKS, false);
+
+  if (a.hist != nullptr && split == 0)
+    for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x) a.hist[(int64_t)h0 * kHistBins + i] = 0u;
+
+  uint32_t off[R::NI];
+  copy_offsets<D, HG>(a, wave, lane, off);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
+  uint4 qr[NRTW][D / 16];
+  load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
+
+  float mrun[NRTW], zrun[NRTW];
+  int qpos[NRTW];
+#pragma unroll
+  for (int i = 0; i < NRTW; ++i) {
+    mrun[i] = -INFINITY;
+    zrun[i] = 0.f;
+    const int r = (ro.rg + R::RS * i) * kRowTile + l32;
+    qpos[i] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
+  }
+
+  pass1_loops<D, NRT, HG>(a, c, rg, off, smem, qr, qpos, mrun, zrun);
+  pass1_finish<D, NRT, HG, false>(a, c, smem, mrun, zrun);
 }
 
 // ---------------------------------------------------------------------------
@@ -977,58 +1035,30 @@ __device__ __forceinline__ void emit_score(const ScoreArgs& a, float* out, uint3
   }
 }
 
+// Pass 2 after its prologue: the ring's first slots are requested, qr holds
+// the wavefront's query rows and (mv, zv) this thread's row normaliser.
 template <int D, int NRT, int HG>
-__global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
+__device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG>& c, const Range& rg,
+                                           const uint32_t* off, unsigned char* smem,
+                                           const uint4 (&qr)[(NRT + Ring<D, HG>::RS - 1) / Ring<D, HG>::RS][D / 16],
+                                           float mv, float zv, bool real_row) {
   using R = Ring<D, HG>;
   constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
   constexpr int ROWS_PAD = NRT * kRowTile;
-  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr bool SLOT_PIPE = NRT % R::RS == 0 && NRTW <= 2 && KVC_SLOT_PIPE;
   float* bias_all = reinterpret_cast<float*>(smem + kRingBytes);            // [HG][ROWS_PAD]
   int* qpos_all = reinterpret_cast<int*>(bias_all + HG * ROWS_PAD);         // [HG][ROWS_PAD]
   uint32_t* hist2 = reinterpret_cast<uint32_t*>(qpos_all + HG * ROWS_PAD);  // [HG][kHistBins/2], u16 pairs
   float* psum = reinterpret_cast<float*>(hist2 + HG * (kHistBins / 2));     // [2][HG][KT][RS][32]
-
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = work / a.n_split, split = work % a.n_split;
-  const int h0 = grp * HG;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront-uniform: SGPRs
-  const int half = lane >> 5, l32 = lane & 31;
-  const Role ro = role_of<D, HG>(wave);
-  const int head = h0 + ro.hl;
-  const int ntile = (NRT - ro.rg + R::RS - 1) / R::RS;
-  const int first_hidden = a.s - a.w + 1;
-  // the K that pass 1 read last (still in the memory-side cache) goes first
-  const Range rg = wg_range(a, split, R::TOKS, true);
-
-  uint32_t off[R::NI];
-  copy_offsets<D, HG>(a, wave, lane, off);
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
-  uint4 qr[NRTW][D / 16];
-  load_query_regs<D, NRTW, R::RS>(a, head, ro.rg, NRT, half, l32, qr);
-  // this thread's normaliser (one bias entry per thread)
-  static_assert(HG * ROWS_PAD <= R::WAVES * kWave, "one bias entry per thread");
+  const int h0 = c.h0, lane = c.lane, wave = c.wave, half = c.half, l32 = c.l32, ntile = c.ntile;
+  const int head = c.head, first_hidden = c.first_hidden;
+  const Role ro = c.ro;
   const int bidx = threadIdx.x;
-  float mv = 0.f, zv = 1.f;
-  bool real_row = false;
+  // p = 2^(dot * c - (m * log2 e + log2 Z)); padding rows get +inf (p = 0).
+  // One explicit fused multiply-add, so every kernel that runs this pass
+  // rounds the bias alike.
   if (bidx < HG * ROWS_PAD) {
-    const int h = bidx / ROWS_PAD, r = bidx % ROWS_PAD;
-    if (r < a.rows) {
-      const int64_t o = (int64_t)((h0 + h) * a.g + r / a.w) * a.w + r % a.w;
-      mv = a.m_in[o];
-      zv = a.z_in[o];
-      real_row = true;
-    }
-  }
-  constexpr bool SLOT_PIPE = NRT % R::RS == 0 && NRTW <= 2 && KVC_SLOT_PIPE;
-  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
-  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
-  vm_settle(mv);
-  vm_settle(zv);
-
-  // p = 2^(dot * c - (m * log2 e + log2 Z)); padding rows get +inf (p = 0)
-  if (bidx < HG * ROWS_PAD) {
-    bias_all[bidx] = real_row ? mv * kLog2e + __log2f(zv) : INFINITY;
+    bias_all[bidx] = real_row ? fmaf(mv, kLog2e, __log2f(zv)) : INFINITY;
     qpos_all[bidx] = real_row ? a.s - a.w + (bidx % ROWS_PAD) % a.w : -1;
   }
   const bool with_hist = a.hist != nullptr;
@@ -1153,6 +1183,205 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
   }
 }
 
+template <int D, int NRT, int HG>
+__global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
+  constexpr int ROWS_PAD = NRT * kRowTile;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const WgCtx<D, HG> c = wg_ctx<D, NRT, HG>(a);
+  const int h0 = c.h0, lane = c.lane, wave = c.wave, half = c.half, l32 = c.l32;
+  const Role ro = c.ro;
+  // the K that pass 1 read last (still in the memory-side cache) goes first
+  const Range rg = wg_range(a, c.split, R::TOKS, true);
+
+  uint32_t off[R::NI];
+  copy_offsets<D, HG>(a, wave, lane, off);
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 0, 1);
+  uint4 qr[NRTW][D / 16];
+  load_query_regs<D, NRTW, R::RS>(a, c.head, ro.rg, NRT, half, l32, qr);
+  // this thread's normaliser (one bias entry per thread)
+  static_assert(HG * ROWS_PAD <= R::WAVES * kWave, "one bias entry per thread");
+  const int bidx = threadIdx.x;
+  float mv = 0.f, zv = 1.f;
+  bool real_row = false;
+  if (bidx < HG * ROWS_PAD) {
+    const int h = bidx / ROWS_PAD, r = bidx % ROWS_PAD;
+    if (r < a.rows) {
+      const int64_t o = (int64_t)((h0 + h) * a.g + r / a.w) * a.w + r % a.w;
+      mv = a.m_in[o];
+      zv = a.z_in[o];
+      real_row = true;
+    }
+  }
+  ring_fill<D, HG>(a, h0, rg, wave, lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, slots_after_queries(rg));
+  vm_settle(mv);
+  vm_settle(zv);
+
+  pass2_main<D, NRT, HG>(a, c, rg, off, smem, qr, mv, zv, real_row);
+}
+
+// ---------------------------------------------------------------------------
+// Both scans in one launch. Each workgroup runs its pass-1 split, publishes
+// its partial (max, sum) rows and requests its first pass-2 slots (the K it
+// has just read). When every workgroup of its head group has published, it
+// merges a share of the group's rows in the split combine's order (so the
+// normalisers are bitwise those of the separate kernels) and publishes them;
+// when all have done that, it runs its pass-2 split. Publishing is a flag per
+// workgroup set to the launch's epoch after the data stores are acknowledged;
+// data and flags go through device-coherent (cross-XCD) loads and stores. The
+// host takes this path only when every workgroup of the launch can be
+// resident at once, and a wait gives up after kSpinLimit polls (then the
+// outputs are not valid) rather than spin for ever.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Publish flag `flag` once this workgroup's device-coherent stores are
+// acknowledged (vmcnt) and every thread has issued its own (barrier).
+__device__ __forceinline__ void group_arrive(const ScoreArgs& a, uint64_t* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the n_split flags from `flags` hold the epoch: wavefront 0 polls
+// them (a lane per flag), the others wait at an LDS-only barrier, so ring
+// copies in flight stay in flight.
+__device__ __forceinline__ void group_wait(const ScoreArgs& a, const uint64_t* flags) {
+  if (threadIdx.x < kWave) {
+    for (uint32_t spins = 0; spins < kSpinLimit; ++spins) {
+      bool ok = true;
+      for (int i = threadIdx.x; i < a.n_split; i += kWave)
+        ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+      if (__all(ok)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  lds_barrier();
+}
+
+// This workgroup's share of its head group's rows: the partials of every
+// split merged as the split combine merges them (eight strided runs, then
+// runs 1..7 into run 0), written as the normalisers (m in natural-log units).
+template <int NRT, int HG>
+__device__ __forceinline__ void group_merge(const ScoreArgs& a, int h0, int split, float2* red) {
+  constexpr int ROWS_PAD = NRT * kRowTile;
+  constexpr int RPR = kWave;  // rows per round: eight threads per row
+  const int total = HG * a.rows;
+  const int per = (total + a.n_split - 1) / a.n_split;
+  const int r0 = split * per;
+  const int nr = min(per, total - r0);
+  const int sl = threadIdx.x & 7, rl = threadIdx.x >> 3;
+  for (int base = 0; base < nr; base += RPR) {
+    const int lr = base + rl;
+    const bool ok = lr < nr;
+    const int gr = r0 + (ok ? lr : 0);
+    const int h = gr / a.rows, r = gr % a.rows;
+    const uint64_t* part = reinterpret_cast<const uint64_t*>(a.part) + (int64_t)(h0 + h) * a.n_split * ROWS_PAD;
+    float2 v[kMaxSplit / 8];
+#pragma unroll
+    for (int u = 0; u < kMaxSplit / 8; ++u) {
+      const int sp = sl + 8 * u;
+      v[u] = ok && sp < a.n_split
+                 ? __builtin_bit_cast(float2, __hip_atomic_load(part + (int64_t)sp * ROWS_PAD + r, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT))
+                 : make_float2(-INFINITY, 0.f);
+    }
+    float m = -INFINITY, z = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMaxSplit / 8; ++u) lse_merge(m, z, v[u].x, v[u].y, a.c);
+    red[sl * RPR + rl] = make_float2(m, z);
+    __syncthreads();
+    if (sl == 0 && ok) {
+      for (int k = 1; k < 8; ++k) lse_merge(m, z, red[k * RPR + rl].x, red[k * RPR + rl].y, a.c);
+      const int hh = r / a.w, i = r % a.w;
+      const int64_t o = (int64_t)((h0 + h) * a.g + hh) * a.w + i;
+      __hip_atomic_store(a.m_out + o, m * a.scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.z_out + o, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int NRT, int HG>
+__global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a) {
+  using R = Ring<D, HG>;
+  constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
+  constexpr int ROWS_PAD = NRT * kRowTile;
+  static_assert(NRT % R::RS == 0 && NRTW <= 2, "fused scans use the slot pipeline");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const WgCtx<D, HG> c = wg_ctx<D, NRT, HG>(a);
+  const Range rg1 = wg_range(a, c.split, R::TOKS, false);
+  const Range rg2 = wg_range(a, c.split, R::TOKS, true);  // pass 2 starts on the K read last
+  const int wg = c.grp * a.n_split;  // the head group's first flag
+  uint64_t* pub1 = a.sync + wg;                 // partials written
+  uint64_t* pub2 = a.sync + kMaxFusedWgs + wg;  // normalisers written
+
+  // pass 2 of every workgroup adds to the head group's histogram during this
+  // launch, so the clear goes straight to memory
+  if (a.hist != nullptr && c.split == 0)
+    for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x)
+      __hip_atomic_store(a.hist + (int64_t)c.h0 * kHistBins + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  uint32_t off[R::NI];
+  copy_offsets<D, HG>(a, c.wave, c.lane, off);
+  ring_fill<D, HG>(a, c.h0, rg1, c.wave, c.lane, off, smem, 0, 1);
+  uint4 qr[NRTW][D / 16];
+  load_query_regs<D, NRTW, R::RS>(a, c.head, c.ro.rg, NRT, c.half, c.l32, qr);
+  ring_fill<D, HG>(a, c.h0, rg1, c.wave, c.lane, off, smem, 1);
+  vm_settle_after<R::NI>(qr, slots_after_queries(rg1));
+  float mrun[NRTW], zrun[NRTW];
+  int qpos[NRTW];
+#pragma unroll
+  for (int i = 0; i < NRTW; ++i) {
+    mrun[i] = -INFINITY;
+    zrun[i] = 0.f;
+    const int r = (c.ro.rg + R::RS * i) * kRowTile + c.l32;
+    qpos[i] = r < a.rows ? a.s - a.w + (r % a.w) : -1;
+  }
+  pass1_loops<D, NRT, HG>(a, c, rg1, off, smem, qr, qpos, mrun, zrun);
+  pass1_finish<D, NRT, HG, true>(a, c, smem, mrun, zrun);
+
+  group_arrive(a, pub1 + c.split);
+  ring_fill<D, HG>(a, c.h0, rg2, c.wave, c.lane, off, smem);  // (the reduction above is done with the ring)
+  group_wait(a, pub1);
+  group_merge<NRT, HG>(a, c.h0, c.split, reinterpret_cast<float2*>(smem + kRingBytes));
+  group_arrive(a, pub2 + c.split);
+  group_wait(a, pub2);
+
+  // this thread's normaliser (one bias entry per thread), as pass 2 reads it
+  const int bidx = threadIdx.x;
+  float mv = 0.f, zv = 1.f;
+  bool real_row = false;
+  if (bidx < HG * ROWS_PAD) {
+    const int h = bidx / ROWS_PAD, r = bidx % ROWS_PAD;
+    if (r < a.rows) {
+      const int64_t o = (int64_t)((c.h0 + h) * a.g + r / a.w) * a.w + r % a.w;
+      mv = __hip_atomic_load(a.m_in + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      zv = __hip_atomic_load(a.z_in + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      real_row = true;
+    }
+  }
+  pass2_main<D, NRT, HG>(a, c, rg2, off, smem, qr, mv, zv, real_row);
+}
+
+template <int D, int HG>
+const void* fused_fn(int nrt) {
+  constexpr int RS = Ring<D, HG>::RS;
+  switch (nrt) {
+    case 1: if constexpr (1 % RS == 0) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 1, HG>); else return nullptr;
+    case 2: return reinterpret_cast<const void*>(&scan_fused_kernel<D, 2, HG>);
+    case 4: if constexpr ((4 + RS - 1) / RS <= 2) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 4, HG>); else return nullptr;
+    default: return nullptr;
+  }
+}
+
+const void* stream_fused_fn(const Layer& L) {
+  if (L.d == 128) return L.stream_hg == 2 ? fused_fn<128, 2>(L.row_tiles) : fused_fn<128, 1>(L.row_tiles);
+  return L.stream_hg == 2 ? fused_fn<64, 2>(L.row_tiles) : fused_fn<64, 1>(L.row_tiles);
+}
+
 template <int D, int HG>
 const void* pass1_stream_fn(int nrt) {
   switch (nrt) {
@@ -1209,6 +1438,26 @@ size_t pass2_stream_lds_bytes(const Layer& L) {
   const size_t psum = (size_t)2 * 8 * kKeyTile * sizeof(float);  // [2][HG][KT][RS][32]
   return kRingBytes + L.stream_hg * rows_pad * (sizeof(float) + sizeof(int)) +
          (size_t)L.stream_hg * (kHistBins / 2) * sizeof(uint32_t) + psum;
+}
+
+bool stream_fused_ok(const Layer& L, int cus) {
+  if (L.stream_hg == 0 || stream_fused_fn(L) == nullptr) return false;
+  const int64_t wgs = (int64_t)(L.hkv / L.stream_hg) * L.n_split;
+  return wgs <= cus && wgs <= kMaxFusedWgs;
+}
+
+hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, hipStream_t st) {
+  const void* fn = stream_fused_fn(L);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  // pass 1's reduction, the merge's (kWave rows x 8 partials past the ring) and pass 2's
+  const size_t merge = (size_t)kRingBytes + (size_t)8 * kWave * sizeof(float2);
+  const size_t lds = std::max({pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L), merge});
+  const hipError_t e = ensure_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  ScoreArgs args = a;
+  void* kargs[] = {&args};
+  const dim3 grid((unsigned)(L.hkv / L.stream_hg * L.n_split));
+  return hipLaunchKernel(fn, grid, dim3(8 * kWave), kargs, lds, st);
 }
 
 hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStream_t st) {

@@ -173,6 +173,8 @@ typedef struct kvc_layer_plan {
   int32_t splits;          /* scan workgroups per KV head (per head group when streaming) */
   int32_t hist_in_scan;    /* 1: kvc_compress_layer counts the selection histogram inside
                               the last scan; 0: a separate histogram kernel does */
+  int32_t fused_scans;     /* 1: kvc_compress_layer runs pass 1, the split merge and
+                              pass 2 as one launch on the current device */
   int64_t keys_per_wg;     /* keys of one KV head that one scan workgroup covers (at most) */
   size_t workspace_bytes;  /* kvc_workspace_size(desc) */
 } kvc_layer_plan;
@@ -180,8 +182,9 @@ typedef struct kvc_layer_plan {
 /*
  * The execution plan of desc (validated as every entry point does) into
  * *plan. The streaming pass 2 counts its histogram in 16-bit LDS halves, so it
- * builds the selection histogram only while keys_per_wg < 65536. Pure host
- * function.
+ * builds the selection histogram only while keys_per_wg < 65536. Host
+ * function; only fused_scans looks at the current device (its compute-unit
+ * count), and reads 0 where there is none.
  */
 int kvc_plan_layer(const kvc_layer_desc* desc, kvc_layer_plan* plan);
 
@@ -260,6 +263,19 @@ int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v
  * kernel). m_out, z_out and scores_out may be NULL (they then live in the
  * workspace); idx_out, k_out, v_out and pos_out are required. Results equal
  * those of the four staged calls bit for bit.
+ *
+ * With softmax scores on the streaming scans (kvc_plan_layer: scan ==
+ * KVC_SCAN_STREAM, fused_scans == 1) pass 1, the merge of its split
+ * partials and pass 2 run as ONE launch whose workgroups wait for the others
+ * of their head group between the phases. That launch is used only when all
+ * of its workgroups (one per compute unit) can be resident at once; each wait
+ * is bounded (about a second), so the launch always ends, but if other work
+ * holds the device's compute units for that long the call's outputs are not
+ * valid. Calls that overlap on several streams of one device should not
+ * both take this path (kvc_compress_layers orders its own lanes so); setting
+ * the environment variable KVC_FUSED=0 before the first call keeps the scans
+ * as separate launches. The workspace needs no initialisation: the waits
+ * use flags stamped with a value that is new for every launch.
  */
 int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void* k,
                        const void* v, const int32_t* budgets,

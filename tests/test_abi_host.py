@@ -393,3 +393,14 @@ def test_plan_histogram_counter_bound():
     assert kvc.kvc_plan_layer(base_desc(s=65536, score_mode=kvc.KVC_SCORE_LOGIT)).scan == kvc.KVC_SCAN_LOGIT
     with pytest.raises(kvc.KvcError):
         kvc.kvc_plan_layer(base_desc(s=0))
+
+
+def test_plan_fused_scans_need_a_device():
+    """Whether the scans run as one launch depends on the device's compute
+    units, so a plan made without a device says they do not; modes other
+    than softmax never fuse."""
+    import os
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present: the plan reflects that device")
+    assert kvc.kvc_plan_layer(base_desc(s=65536)).fused_scans == 0
+    assert kvc.kvc_plan_layer(base_desc(s=65536, score_mode=kvc.KVC_SCORE_LOGIT)).fused_scans == 0

@@ -17,7 +17,7 @@ import compression_kvc_score_amd as kvc  # noqa: E402
 import oracle  # noqa: E402
 from synth import LayerConfig, get_config, layer_inputs  # noqa: E402
 
-from gpu_util import desc_from, from_dev_bits, run_fused, run_staged, split_heads, to_dev_bf16  # noqa: E402
+from gpu_util import desc_from, from_dev_bits, host, run_fused, run_staged, split_heads, to_dev_bf16  # noqa: E402
 from parity import (  # noqa: E402
     assert_normalizers_close, assert_scores_close, assert_selection_consistent,
     assert_selection_matches,
@@ -392,6 +392,36 @@ def test_deterministic_repeat():
     a2 = run_fused(desc, q, k, v, b)
     for key in ["m", "z", "scores", "idx", "k_hat", "v_hat", "pos"]:
         np.testing.assert_array_equal(a1[key], a2[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name,s", [("tiny", None), ("llama8b_16k", 8192), ("llama8b_64k", None)])
+def test_fused_scans_need_no_workspace_init(name, s):
+    """Where the scans run as one launch (pass 1, split merge, pass 2 with
+    waits between workgroups), the outputs equal the staged calls' bit for
+    bit whatever the workspace held before: zeros, all ones, random bytes,
+    or a previous call's state."""
+    cfg = get_config(name) if s is None else get_config(name).with_(s=s)
+    x = layer_inputs(cfg, 5)
+    q, k, v = dev_inputs(x)
+    b = budgets_for(cfg, x)
+    desc = desc_from(cfg, q, k, v)
+    plan = kvc.kvc_plan_layer(desc)
+    say(f"{name} s={cfg.s}: fused scans {plan.fused_scans}, splits {plan.splits}, heads per workgroup {plan.heads_per_wg}")
+    assert plan.scan == kvc.KVC_SCAN_STREAM and plan.fused_scans == 1
+    st = run_staged(desc, q, k, v, b)
+    ws = kvc.alloc_workspace(desc)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    fills = [("zeros", lambda: ws.zero_()), ("ones", lambda: ws.fill_(255)),
+             ("random", lambda: ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=gen))),
+             ("previous call", lambda: None)]
+    for label, fill in fills:
+        fill()
+        out = kvc.alloc_outputs(desc, b)
+        kvc.compress_layer(desc, q, k, v, b, out, ws)
+        torch.cuda.synchronize()
+        got = host(out)
+        for key in ["m", "z", "scores", "idx", "k_hat", "v_hat", "pos"]:
+            np.testing.assert_array_equal(got[key], st[key], err_msg=f"{label}: {key}")
 
 
 @pytest.mark.parametrize("name,s,n_layers", [("llama8b_16k", 8192, 5), ("qwen14b_hetero_64k", 8192, 4)])
