@@ -62,6 +62,24 @@ def algorithmic_bytes(cfg, rows_total: int) -> dict:
     }
 
 
+def fused_scan_bytes(cfg) -> int:
+    """Algorithmic bytes of both scans as one launch: K read twice, Q_win read
+    once (it stays in registers), (m, Z) and the scores written once."""
+    k_bytes = cfg.s * cfg.hkv * cfg.d * 2
+    return 2 * k_bytes + cfg.w * cfg.hq * cfg.d * 2 + 2 * cfg.hq * cfg.w * 4 + cfg.hkv * cfg.s * 4
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def mfma_flops(cfg) -> float:
     """Q_win.K^T flops of one pass (all KV heads)."""
     return 2.0 * cfg.w * cfg.hq * cfg.s * cfg.d
@@ -102,6 +120,7 @@ def cpu_baseline(cfg, host_layers, budgets_of, seconds: float):
         "value": cfg.s * layers_done / dt,
         "unit": "tokens/s",
         "cores": blas_threads(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": (f"{heads} KV-head compressions ({layers_done:.2f} layers of {cfg.name}, "
                    f"{dt:.1f} s); fp64 numpy oracle, dense W x S softmax per head"),
@@ -222,19 +241,28 @@ def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
     return out
 
 
-OTHER_CONFIGS = ["llama8b_16k", "llama8b_128k", "llama8b_128k_pool7", "qwen14b_hetero_64k"]
+OTHER_CONFIGS = ["llama8b_16k", "llama8b_128k", "llama8b_128k_pool7"]
+SWEEP_CONFIG = "qwen14b_hetero_64k"
+
+
+def _pct(us):
+    us = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2)}
 
 
 def other_configs(kvc, torch, dev, names, reps, sp, stream):
-    """kvc_compress_layer on the other layer shapes: two resident layers of
-    each, `reps` calls alternating between them after two warm calls, HIP
-    events around the calls. Reports time per layer, throughput and the HBM
-    fraction over the layer's algorithmic bytes."""
+    """kvc_compress_layer on the other single-layer shapes: two resident layers
+    of each, two warm calls, then `reps` calls alternating between them, each
+    after a 512 MiB read that evicts the memory-side cache, with HIP events
+    around each call. Reports median / p10 / p90 per layer, throughput and the
+    HBM fraction over the layer's algorithmic bytes (at the median)."""
     from synth import get_config, layer_inputs
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     out = {}
     for name in names:
         cfg = get_config(name)
@@ -252,25 +280,86 @@ def other_configs(kvc, torch, dev, names, reps, sp, stream):
             preps.append(kvc.PreparedLayer(desc, q, k, v, budgets, o, kvc.alloc_workspace(desc, dev)))
         for p in preps:
             p.kvc_compress_layer(sp)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
+        evs = []
         for i in range(reps):
+            flush.amax()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             preps[i % 2].kvc_compress_layer(sp)
-        e1.record(stream)
+            e1.record(stream)
+            evs.append((e0, e1))
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        med = float(np.median(us))
         alg = sum(algorithmic_bytes(cfg, rows).values())
         rows_per_head = cfg.group * cfg.w
+        plan = kvc.kvc_plan_layer(preps[0].desc)
         out[name] = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "pool": cfg.pool,
-                     "hetero": bool(cfg.hetero), "us_per_layer": round(us, 2),
-                     "tokens_per_s": round(cfg.s / (us * 1e-6), 1), "alg_bytes": alg,
-                     "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "scans": "streaming (K staged in LDS)" if rows_per_head <= 128 else "per-head (K in VGPRs)"}
-        log(f"{name}: {us:.1f} us per layer, {out[name]['hbm_frac'] * 100:.1f}% of the HBM peak, "
-            f"{out[name]['scans']} scans")
+                     "us_per_layer": _pct(us), "reps": reps, "flushed": True,
+                     "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
+                     "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "scans": ("streaming (K staged in LDS)" + (", fused into one launch" if plan.fused_scans else "")
+                               if rows_per_head <= 128 else "per-head (K in VGPRs)")}
+        log(f"{name}: median {med:.1f} us per layer (p10 {out[name]['us_per_layer']['p10']:.1f}, "
+            f"p90 {out[name]['us_per_layer']['p90']:.1f}; {reps} calls after a cache flush), "
+            f"{out[name]['hbm_frac'] * 100:.1f}% of the HBM peak, {out[name]['scans']} scans")
         del preps
         torch.cuda.empty_cache()
+    del flush
+    return out
+
+
+def layer_sweep(kvc, torch, dev, name, sp, stream):
+    """A model's layers in order, each resident with its own seed (and, for
+    heterogeneous budgets, its own S_stable draw), one kvc_compress_layer call
+    per layer into one retained-cache arena, HIP events around each call."""
+    from synth import get_config, layer_inputs
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cfg = get_config(name)
+    t0 = time.perf_counter()
+    preps, rows = [], []
+    ws = None
+    for l in range(cfg.layers):
+        x = layer_inputs(cfg, l)
+        budgets = (kvc.kvc_budgets_inverse_stability(x.s_stable, cfg.total_budget) if cfg.hetero
+                   else np.full(cfg.hkv, cfg.budget, dtype=np.int32))
+        q, k, v = dev_bf16(x.q), dev_bf16(x.k), dev_bf16(x.v)
+        del x
+        desc = kvc.desc_for(q, k, v, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool)
+        if ws is None:
+            ws = kvc.alloc_workspace(desc, dev)
+        o = kvc.alloc_outputs(desc, budgets, dev, with_intermediates=False)
+        rows.append(int(o.offsets[-1]))
+        preps.append(kvc.PreparedLayer(desc, q, k, v, budgets, o, ws))
+    log(f"{name}: generated {cfg.layers} layers ({time.perf_counter() - t0:.0f} s)")
+    arena = sum(p._keep[3].k_hat.nbytes + p._keep[3].v_hat.nbytes for p in preps)
+    preps[-1].kvc_compress_layer(sp)  # warm (the last layer; the sweep starts at the first)
+    torch.cuda.synchronize()
+    evs = []
+    for p in preps:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        p.kvc_compress_layer(sp)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    med = float(np.median(us))
+    alg = sum(algorithmic_bytes(cfg, max(rows)).values())
+    out = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "layers": cfg.layers,
+           "budgets": "inverse stability, total %d per layer" % cfg.total_budget if cfg.hetero else cfg.budget,
+           "retained_arena_bytes": arena, "us_per_layer": _pct(us),
+           "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
+           "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "scans": "per-head (K in VGPRs)" if cfg.group * cfg.w > 128 else "streaming (K staged in LDS)"}
+    log(f"{name} sweep over {cfg.layers} layers: median {med:.1f} us per layer (p10 {out['us_per_layer']['p10']:.1f}, "
+        f"p90 {out['us_per_layer']['p90']:.1f}), retained arena {arena / 2**20:.0f} MiB, "
+        f"{out['hbm_frac'] * 100:.1f}% of the HBM peak")
+    del preps, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -362,6 +451,9 @@ def main(argv=None):
                     help="skip the layer-major prefill run (random-weight model around the compressor)")
     ap.add_argument("--no-configs", dest="configs", action="store_false",
                     help="skip timing the other layer shapes (16K, 128K, 128K with pool 7, Qwen-shaped)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the roofline loop (back-to-back kvc_score_layer calls over the resident "
+                         "layers), for profiling the dominant kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (to calibrate HBM byte counters)")
     args = ap.parse_args(argv)
@@ -424,6 +516,57 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    plan = kvc.kvc_plan_layer(desc)
+
+    def roofline_loop(K, W):
+        """The dominant kernel alone: K back-to-back kvc_score_layer calls over
+        the resident layers after W warm ones, HIP events on the launch stream
+        around the K calls. With fused scans each call is one launch."""
+        for i in range(W):
+            prepared[i % n_layers].kvc_score_layer(sp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            prepared[i % n_layers].kvc_score_layer(sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    def roofline_object(scan_ms):
+        if plan.fused_scans:
+            kernel = ("scan_fused_kernel: pass 1, split merge and pass 2 as one launch "
+                      "(one kvc_score_layer call)")
+            alg_b = fused_scan_bytes(cfg)
+        else:
+            kernel = "pass 1, split combine and pass 2 (three launches of one kvc_score_layer call)"
+            a = algorithmic_bytes(cfg, 0)
+            alg_b = a["pass1"] + a["pass2"]
+        achieved = alg_b / (scan_ms * 1e-3) / 1e9
+        traffic = None
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tf = json.load(f)
+            if tf.get("kernel_hash") == kernel_source_hash() and tf.get("workload") == cfg.name:
+                traffic = tf.get("per_launch_bytes", {}).get("scan")
+        except (OSError, ValueError):
+            traffic = None
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": alg_b, "us_per_launch": round(scan_ms * 1e3, 2),
+                "launches_timed": args.steps,
+                "mfma_tflops": round(2 * mfma_flops(cfg) / (scan_ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(2 * mfma_flops(cfg) / (scan_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    if args.roofline_only:
+        scan_ms = roofline_loop(args.steps, args.warmup)
+        roof = roofline_object(scan_ms)
+        log(f"roofline loop: {scan_ms * 1e3:.2f} us per kvc_score_layer call, {roof['frac'] * 100:.1f}% of the HBM peak")
+        print(json.dumps({"metric": METRIC, "mode": "roofline-only", "steps": args.steps, "warmup": args.warmup,
+                          "config": {"workload": cfg.name, "s": cfg.s, "fused_scans": int(plan.fused_scans)},
+                          "roofline": roof, "kernel_hash": kernel_source_hash()}), flush=True)
+        return 0
+
     stage_calls = {
         "pass1": lambda p: p.kvc_score_pass1(sp),
         "pass2": lambda p: p.kvc_score_pass2(sp),
@@ -451,6 +594,10 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     step_gpu_ms = ev_start.elapsed_time(ev_end) / K
     log(f"timed {K} steps: {wall * 1e3 / K:.4f} ms/step wall, {step_gpu_ms:.4f} ms/step on GPU")
+
+    # ---- the dominant kernel alone, for the roofline
+    scan_ms = roofline_loop(K, args.warmup)
+    log(f"roofline loop: {scan_ms * 1e3:.2f} us per kvc_score_layer call (fused scans: {bool(plan.fused_scans)})")
 
     # ---- the same calls replayed from a HIP graph: one captured
     # kvc_compress_layer per resident layer (the library enqueues only
@@ -595,18 +742,18 @@ def main(argv=None):
             mprep[i % n_layers].kvc_score_pass2(sp)
         e1.record(stream)
         torch.cuda.synchronize()
-        scan_ms = e0.elapsed_time(e1) / K
+        mscan_ms = e0.elapsed_time(e1) / K
         scan_bytes = cfg.s * cfg.hkv * cfg.d * 2 + cfg.w * cfg.hq * cfg.d * 2 + cfg.hkv * cfg.s * 4
         res = torch.empty(cfg.hkv, dtype=torch.float32, device=dev)
         kvc.kvc_overlap_coefficient(desc, prepared[0]._keep[3].idx, mprep[0]._keep[3].idx, layers[0][3], res)
         torch.cuda.synchronize()
         mode_detail[mode_name] = {
             "ms_per_step": round(mwall * 1e3 / K, 5), "value": round(cfg.s * K / mwall, 1),
-            "scan_us": round(scan_ms * 1e3, 2),
-            "scan_hbm_frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "scan_us": round(mscan_ms * 1e3, 2),
+            "scan_hbm_frac": round(scan_bytes / (mscan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "overlap_with_softmax_mean": round(float(res.mean().item()), 4),
         }
-        log(f"score mode {mode_name}: {mwall * 1e3 / K:.4f} ms/layer; scan {scan_ms * 1e3:.1f} us "
+        log(f"score mode {mode_name}: {mwall * 1e3 / K:.4f} ms/layer; scan {mscan_ms * 1e3:.1f} us "
             f"({mode_detail[mode_name]['scan_hbm_frac'] * 100:.1f}% of HBM peak); retained-set overlap with "
             f"softmax {mode_detail[mode_name]['overlap_with_softmax_mean']:.3f}")
         del mprep
@@ -617,7 +764,9 @@ def main(argv=None):
     # keys, each against the one-shot layer-end compressor on the same tensors
     imm_detail = {name: immediate_eviction(kvc, torch, dev, name, max(4, K // 4), sp, stream)
                   for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
-    configs_detail = other_configs(kvc, torch, dev, OTHER_CONFIGS, max(8, K // 4), sp, stream) if args.configs else None
+    configs_detail = other_configs(kvc, torch, dev, OTHER_CONFIGS, 20, sp, stream) if args.configs else None
+    if args.configs:
+        configs_detail[SWEEP_CONFIG] = layer_sweep(kvc, torch, dev, SWEEP_CONFIG, sp, stream)
     prefill_detail = layer_major_prefill(kvc, torch, dev, s=cfg.s) if args.prefill else None
 
     copy_gbs = achievable_hbm_gbs(torch, dev)
@@ -626,29 +775,9 @@ def main(argv=None):
     ms_per_step = wall * 1e3 / K
     value = cfg.s * K / wall
 
-    # ---- roofline of the dominant kernel (the slower K scan; the pass-1 call
-    # also runs its small split-combine kernel, which is counted in its time)
     alg = algorithmic_bytes(cfg, rows_total)
-    dominant = max(("pass1", "pass2"), key=lambda n: stage_ms[n])
-    achieved = alg[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tf = json.load(f)
-        if tf.get("kernel_hash") == kernel_source_hash() and tf.get("workload") == cfg.name:
-            traffic = tf.get("per_launch_bytes", {}).get(dominant)
-    except (OSError, ValueError):
-        traffic = None
-    roofline = {
-        "bound": "hbm",
-        "kernel": {"pass1": "pass 1 scan + split combine (one kvc_score_pass1 call)",
-                   "pass2": "pass 2 scan (one kvc_score_pass2 call)"}[dominant],
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-    }
+    roofline = roofline_object(scan_ms)
+    achieved = roofline["achieved"]
     total_alg = sum(alg.values())
     extras = {
         "stage_us": {n: round(stage_ms[n] * 1e3, 2) for n in stage_names},

@@ -8,7 +8,7 @@ from ._lib import (  # noqa: F401
     LayerOutputs, PreparedLayer, PreparedSweep, SWEEP_STREAMS, alloc_outputs, alloc_sweep_workspace,
     alloc_workspace, compress_layer, desc_for, kvc_budgets_inverse_stability,
     kvc_compress_layer, kvc_compress_layers, kvc_gather_retained, kvc_retained_offsets, kvc_score_pass1,
-    kvc_score_pass2, kvc_select_topk, kvc_strerror, kvc_version, kvc_workspace_size, lib,
+    kvc_score_layer, kvc_score_pass2, kvc_select_topk, kvc_strerror, kvc_version, kvc_workspace_size, lib,
     make_desc, kvc_chunk_workspace_size, kvc_evict_chunk, kvc_chunked_workspace_size, kvc_compress_chunked,
     kvc_plan_layer, LayerPlan, kvc_compress_layer_noalloc, KVC_NOALLOC_SCRATCH_BYTES, KVC_SCAN_STREAM, KVC_SCAN_PER_HEAD, KVC_SCAN_LOGIT,
     alloc_arena, PreparedChunked, PrefillDesc, kvc_rmsnorm, kvc_rope_append, kvc_chunk_attention, kvc_swiglu,

@@ -128,6 +128,7 @@ def _load():
         "kvc_budgets_inverse_stability": (ctypes.c_int, [P, I32, I64, P]),
         "kvc_score_pass1": (ctypes.c_int, [D, P, P, P, P, P, SZ, P]),
         "kvc_score_pass2": (ctypes.c_int, [D, P, P, P, P, P, P]),
+        "kvc_score_layer": (ctypes.c_int, [D, P, P, P, P, P, P, SZ, P]),
         "kvc_select_topk": (ctypes.c_int, [D, P, P, P, P, SZ, P]),
         "kvc_gather_retained": (ctypes.c_int, [D, P, P, P, P, P, P, P, P]),
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -268,6 +269,15 @@ def kvc_score_pass2(desc, q_win, k, m, z, scores):
     _check(L.kvc_score_pass2(ctypes.byref(desc), _bf16_ptr(q_win, "q_win"), _bf16_ptr(k, "k"),
                              _dev_ptr(m, "m", 4), _dev_ptr(z, "z", 4),
                              _dev_ptr(scores, "scores", 4), _stream()))
+
+
+def kvc_score_layer(desc, q_win, k, m_out, z_out, scores_out, ws):
+    """Both scans as kvc_compress_layer runs them; m_out, z_out, scores_out may be None."""
+    L = _load()
+    _check(L.kvc_score_layer(ctypes.byref(desc), _bf16_ptr(q_win, "q_win"), _bf16_ptr(k, "k"),
+                             _dev_ptr(m_out, "m_out", 4), _dev_ptr(z_out, "z_out", 4),
+                             _dev_ptr(scores_out, "scores_out", 4),
+                             _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 
 def kvc_select_topk(desc, scores, budgets, idx_out, ws):
@@ -520,6 +530,7 @@ class PreparedLayer:
         w, wn = _dev_ptr(ws, "ws"), ws.numel() * ws.element_size()
         self._a1 = (self._d, q, kk, m, z, w, wn)
         self._a2 = (self._d, q, kk, m, z, sc)
+        self._as = (self._d, q, kk, m, z, sc, w, wn)
         self._a3 = (self._d, sc, bp, idx, w, wn)
         self._a4 = (self._d, kk, vv, idx, bp, kh, vh, pos)
         self._af = (self._d, q, kk, vv, bp, m, z, sc, idx, kh, vh, pos, w, wn)
@@ -533,6 +544,9 @@ class PreparedLayer:
 
     def kvc_score_pass2(self, stream=None):
         _check(self._L.kvc_score_pass2(*self._a2, self._s(stream)))
+
+    def kvc_score_layer(self, stream=None):
+        _check(self._L.kvc_score_layer(*self._as, self._s(stream)))
 
     def kvc_select_topk(self, stream=None):
         _check(self._L.kvc_select_topk(*self._a3, self._s(stream)))

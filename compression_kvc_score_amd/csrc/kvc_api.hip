@@ -480,25 +480,20 @@ int check_layer_ptrs(const void* q_win, const void* k, const void* v, const int3
   return KVC_OK;
 }
 
-// One validated layer onto one stream; m, z, scores NULL: in the workspace.
-// pos_in non-null: retained positions are looked up there (per head, stride
-// pos_in_head) instead of pos_offset + index. scan_gate non-null: a fused
-// scan launch waits for the event's last record and records it afterwards,
-// so that the fused scans of calls on several streams never overlap (their
-// workgroups wait for each other and must all be resident).
-int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* v, const HeadTable& ht,
-                  float* m_out, float* z_out, float* scores_out, int32_t* idx_out, void* k_out,
-                  void* v_out, int32_t* pos_out, void* ws, hipStream_t st,
-                  const int32_t* pos_in = nullptr, int64_t pos_in_head = 0,
-                  hipEvent_t scan_gate = nullptr) {
+// The scans of one validated layer onto one stream, exactly as the whole-layer
+// call runs them (so they also build the selection histogram where that call
+// counts it in the last scan); m, z, scores NULL: in the workspace. Sets
+// *hist_built. allow_fused false: three launches even where one would do (for
+// callers that overlap layers on several streams: a fused launch needs the
+// whole device resident).
+int enqueue_scans(const Layer& L, const void* q_win, const void* k, float* m, float* z, float* sc, void* ws,
+                  hipStream_t st, bool* hist_built, bool allow_fused = true) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
-  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
-  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
-  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
   // the last scan builds the selection histogram unless ranking uses pooled
   // values or its 16-bit workgroup counters could wrap
   const bool hist_in_pass2 = L.pool == 1 && hist_fits_scan(L);
+  *hist_built = hist_in_pass2;
   if (L.score_mode != KVC_SCORE_SOFTMAX) {
     uint32_t* hist = nullptr;
     if (hist_in_pass2) {
@@ -508,11 +503,9 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
       if (e != hipSuccess) return hip_fail(e, "histogram clear launch");
       hist = sa.hist;
     }
-    KVC_TRY(run_logit(L, q_win, k, sc, hist, st));
-    return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
-                      pos_in_head);
+    return run_logit(L, q_win, k, sc, hist, st);
   }
-  if (use_fused_scans(L)) {
+  if (allow_fused && use_fused_scans(L)) {
     ScoreArgs a = score_args(L, q_win, k);
     a.part = reinterpret_cast<float*>(wsb + lay.part);
     if (hist_in_pass2) a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
@@ -523,22 +516,30 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
     a.scores = sc;
     a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
     a.epoch = next_epoch();
-    if (scan_gate != nullptr) {
-      const hipError_t e = hipStreamWaitEvent(st, scan_gate, 0);
-      if (e != hipSuccess) return hip_fail(e, "scan gate wait");
-    }
-    hipError_t e = launch_stream_fused(L, a, st);
+    const hipError_t e = launch_stream_fused(L, a, st);
     if (e != hipSuccess) return hip_fail(e, "fused scan launch");
-    if (scan_gate != nullptr) {
-      e = hipEventRecord(scan_gate, st);
-      if (e != hipSuccess) return hip_fail(e, "scan gate record");
-    }
-  } else {
-    KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
-    KVC_TRY(run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st));
+    return KVC_OK;
   }
+  KVC_TRY(run_pass1(L, q_win, k, m, z, ws, hist_in_pass2, st));
+  return run_pass2(L, q_win, k, m, z, sc, hist_in_pass2 ? ws : nullptr, st);
+}
+
+// One validated layer onto one stream; m, z, scores NULL: in the workspace.
+// pos_in non-null: retained positions are looked up there (per head, stride
+// pos_in_head) instead of pos_offset + index. allow_fused: as enqueue_scans.
+int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* v, const HeadTable& ht,
+                  float* m_out, float* z_out, float* scores_out, int32_t* idx_out, void* k_out,
+                  void* v_out, int32_t* pos_out, void* ws, hipStream_t st,
+                  const int32_t* pos_in = nullptr, int64_t pos_in_head = 0, bool allow_fused = true) {
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
+  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
+  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
+  bool hist_built = false;
+  KVC_TRY(enqueue_scans(L, q_win, k, m, z, sc, ws, st, &hist_built, allow_fused));
   // the compaction of the selection copies the retained rows as it goes
-  return run_select(L, sc, ht, idx_out, ws, !hist_in_pass2, st, k, v, k_out, v_out, pos_out, pos_in,
+  return run_select(L, sc, ht, idx_out, ws, !hist_built, st, k, v, k_out, v_out, pos_out, pos_in,
                     pos_in_head);
 }
 
@@ -873,6 +874,26 @@ int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void
                        static_cast<hipStream_t>(stream));
 }
 
+int kvc_score_layer(const kvc_layer_desc* desc, const void* q_win, const void* k, float* m_out, float* z_out,
+                    float* scores_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+  Layer L;
+  KVC_TRY(normalize(desc, L));
+  KVC_TRY(check_ptr(q_win, 16, "q_win"));
+  KVC_TRY(check_ptr(k, 16, "k"));
+  if (m_out) KVC_TRY(check_ptr(m_out, 4, "m_out"));
+  if (z_out) KVC_TRY(check_ptr(z_out, 4, "z_out"));
+  if (scores_out) KVC_TRY(check_ptr(scores_out, 4, "scores_out"));
+  KVC_TRY(check_ws(L, ws, ws_bytes));
+  KVC_TRY(check_lds(L));
+  const WsLayout lay = ws_layout(L);
+  char* wsb = static_cast<char*>(ws);
+  float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
+  float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
+  float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
+  bool hist_built = false;
+  return enqueue_scans(L, q_win, k, m, z, sc, ws, static_cast<hipStream_t>(stream), &hist_built);
+}
+
 int kvc_compress_layer_noalloc(const kvc_layer_desc* desc, const void* q_win, const void* k, const void* v,
                                const int32_t* budgets, float* m_out, float* z_out, float* scores_out,
                                int32_t* idx_out, void* k_out, void* v_out, int32_t* pos_out,
@@ -949,22 +970,16 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
   for (int j = 1; j < kSweepStreams && e == hipSuccess; ++j) e = hipStreamWaitEvent(lanes[j], ev, 0);
   (void)hipEventDestroy(ev);
   if (e != hipSuccess) return hip_fail(e, "sweep fork");
-  // fused scans of successive layers run one after another (each needs the
-  // whole device resident); the selections still overlap the next scan
-  hipEvent_t gate = nullptr;
-  if (use_fused_scans(L)) {
-    e = hipEventCreateWithFlags(&gate, hipEventDisableTiming);
-    if (e != hipSuccess) gate = nullptr;
-    else e = hipEventRecord(gate, lanes[0]);  // recorded before the first wait
-  }
-  int status = e == hipSuccess ? KVC_OK : hip_fail(e, "sweep scan gate");
+  // the scans stay three launches here: a fused scan needs the whole device
+  // resident, so two of them must not overlap (and fusing gained nothing
+  // here: 77.8-78.8 against 78.3 us per 64K layer)
+  int status = KVC_OK;
   for (int32_t i = 0; i < n_layers && status == KVC_OK; ++i) {
     const int j = i % kSweepStreams;
     status = enqueue_layer(L, q_win[i], k[i], v[i], hts[(size_t)i], nullptr, nullptr, nullptr, idx_out[i],
                            k_out[i], v_out[i], pos_out[i], static_cast<char*>(ws) + j * one, lanes[j], nullptr, 0,
-                           gate);
+                           false);
   }
-  if (gate != nullptr) (void)hipEventDestroy(gate);
   // join: later work on the caller's stream waits for every lane (also after
   // a failed launch, so that nothing of this call outlives the caller's order)
   for (int j = 1; j < kSweepStreams; ++j) {

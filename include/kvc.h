@@ -233,6 +233,21 @@ int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k
                     kvc_stream_t stream);
 
 /*
+ * Both scans of one layer (TideKV, Fig. 3 caption: pass 1, then pass 2 over
+ * the same key blocks) exactly as kvc_compress_layer runs them: m_out, z_out
+ * and scores_out as kvc_score_pass1 and kvc_score_pass2 define them, bit for
+ * bit. Each may be NULL (it then lives in the workspace). Where
+ * kvc_compress_layer fuses the scans (kvc_plan_layer: fused_scans) this is
+ * one launch; it also counts the selection histogram into the workspace
+ * where the whole-layer call does, so that the launch is the one the
+ * whole-layer call makes. ws: device, kvc_workspace_size(desc) bytes, 256-byte
+ * aligned, no initialisation needed.
+ */
+int kvc_score_layer(const kvc_layer_desc* desc, const void* q_win, const void* k, float* m_out,
+                    float* z_out, float* scores_out, void* ws, size_t ws_bytes,
+                    kvc_stream_t stream);
+
+/*
  * Selection (TideKV, Fig. 3 caption: top K_l - |R_mand| non-mandatory keys
  * plus the mandatory sink/recent set). scores: device fp32 [hkv][S], finite
  * and >= 0 (as pass 2 writes them); if desc->pool > 1 ranking uses the
@@ -272,9 +287,10 @@ int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v
  * is bounded (about a second), so the launch always ends, but if other work
  * holds the device's compute units for that long the call's outputs are not
  * valid. Calls that overlap on several streams of one device should not
- * both take this path (kvc_compress_layers orders its own lanes so); setting
- * the environment variable KVC_FUSED=0 before the first call keeps the scans
- * as separate launches. The workspace needs no initialisation: the waits
+ * both take this path (kvc_compress_layers, which overlaps two layers on two
+ * streams, keeps its scans as three launches); setting the environment
+ * variable KVC_FUSED=0 before the first call keeps the scans as separate
+ * launches everywhere. The workspace needs no initialisation: the waits
  * use flags stamped with a value that is new for every launch.
  */
 int kvc_compress_layer(const kvc_layer_desc* desc, const void* q_win, const void* k,

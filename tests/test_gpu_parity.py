@@ -424,6 +424,35 @@ def test_fused_scans_need_no_workspace_init(name, s):
             np.testing.assert_array_equal(got[key], st[key], err_msg=f"{label}: {key}")
 
 
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("llama8b_16k", {"s": 8192}), ("llama8b_16k", {"s": 3001, "w": 64}),
+                                       ("llama8b_16k", {"s": 4096, "pool": 7})])
+def test_score_layer_equals_staged_and_whole_layer(name, over):
+    """kvc_score_layer (both scans as the whole-layer call runs them: one
+    launch where it fuses them, per-head scans for wide windows) writes the
+    staged passes' m, Z and scores bit for bit, and the whole-layer call's."""
+    cfg = get_config(name).with_(**over) if over else get_config(name)
+    x = layer_inputs(cfg, 6)
+    q, k, v = dev_inputs(x)
+    b = budgets_for(cfg, x)
+    desc = desc_from(cfg, q, k, v)
+    plan = kvc.kvc_plan_layer(desc)
+    say(f"{name} {over}: scan kind {plan.scan}, fused {plan.fused_scans}")
+    st = run_staged(desc, q, k, v, b)
+    fu = run_fused(desc, q, k, v, b)
+    ws = kvc.alloc_workspace(desc)
+    ws.fill_(255)
+    out = kvc.alloc_outputs(desc, b)
+    kvc.kvc_score_layer(desc, q, k, out.m, out.z, out.scores, ws)
+    torch.cuda.synchronize()
+    for key in ["m", "z", "scores"]:
+        got = getattr(out, key).cpu().numpy()
+        np.testing.assert_array_equal(got, st[key], err_msg=f"staged {key}")
+        np.testing.assert_array_equal(got, fu[key], err_msg=f"whole layer {key}")
+    # outputs may live in the workspace
+    kvc.kvc_score_layer(desc, q, k, None, None, None, ws)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name,s,n_layers", [("llama8b_16k", 8192, 5), ("qwen14b_hetero_64k", 8192, 4)])
 def test_sweep_equals_layer_by_layer(name, s, n_layers):
     """kvc_compress_layers over several layers (alternating between the
