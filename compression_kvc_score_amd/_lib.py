@@ -132,7 +132,7 @@ def _load():
         "kvc_select_topk": (ctypes.c_int, [D, P, P, P, P, SZ, P]),
         "kvc_gather_retained": (ctypes.c_int, [D, P, P, P, P, P, P, P, P]),
         "kvc_compress_layer": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
-        "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "kvc_compress_layers": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, SZ, P, P]),
         "kvc_compress_layer_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvc_overlap_coefficient": (ctypes.c_int, [D, P, P, P, P, P]),
         "kvc_chunk_workspace_size": (SZ, [D, I64]),
@@ -361,12 +361,20 @@ def _sweep_args(desc, layers, budgets, outs, ws):
     return args, keep
 
 
-def kvc_compress_layers(desc, layers, budgets, outs, ws):
+def _stream_handle(s):
+    """A torch stream, a raw handle or None as a ctypes pointer (None: NULL)."""
+    if s is None:
+        return None
+    return ctypes.c_void_p(s.cuda_stream if hasattr(s, "cuda_stream") else int(s))
+
+
+def kvc_compress_layers(desc, layers, budgets, outs, ws, aux_stream=None):
     """layers: sequence of (q_win, k, v) tensors of one shape; budgets:
     [n_layers][hkv]; outs: one LayerOutputs per layer; ws: sweep workspace
-    (alloc_sweep_workspace)."""
+    (alloc_sweep_workspace); aux_stream: the caller's second stream (a
+    torch.cuda.Stream) or None (every layer on the current stream)."""
     args, _keep = _sweep_args(desc, layers, budgets, outs, ws)
-    _check(_load().kvc_compress_layers(*args, _stream()))
+    _check(_load().kvc_compress_layers(*args, _stream(), _stream_handle(aux_stream)))
 
 
 # ------------------------------------------------------------------ immediate eviction
@@ -568,6 +576,6 @@ class PreparedSweep:
         self.n_layers = len(layers)
         self._args, self._keep = _sweep_args(desc, layers, budgets, outs, ws)
 
-    def kvc_compress_layers(self, stream=None):
+    def kvc_compress_layers(self, stream=None, aux_stream=None):
         st = ctypes.c_void_p(stream) if stream is not None else _stream()
-        _check(self._L.kvc_compress_layers(*self._args, st))
+        _check(self._L.kvc_compress_layers(*self._args, st, _stream_handle(aux_stream)))

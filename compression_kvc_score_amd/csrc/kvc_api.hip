@@ -634,28 +634,7 @@ int check_arena(const Arena& a, const char* which) {
   return check_ptr(a.pos, 4, name);
 }
 
-// The library's own streams for whole-layer sweeps, one set per device:
-// non-blocking (no implicit order with the null stream), default priority,
-// created on first use and kept until the process ends.
-constexpr int kSweepStreams = 2;
-int aux_stream(int j, hipStream_t& out) {
-  static std::mutex mu;
-  static hipStream_t streams[64][kSweepStreams - 1] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= 64) return fail(KVC_ERR_UNSUPPORTED, "device %d", dev);
-  std::lock_guard<std::mutex> lock(mu);
-  if (streams[dev][j] == nullptr) {
-    e = hipStreamCreateWithFlags(&streams[dev][j], hipStreamNonBlocking);
-    if (e != hipSuccess) {
-      streams[dev][j] = nullptr;
-      return hip_fail(e, "hipStreamCreateWithFlags");
-    }
-  }
-  out = streams[dev][j];
-  return KVC_OK;
-}
+constexpr int kSweepStreams = 2;  // layers in flight in a sweep with a second stream
 
 // Device address of this device's scratch array, looked up on the first call
 // on each device (with that device current) and kept.
@@ -939,17 +918,19 @@ int kvc_overlap_coefficient(const kvc_layer_desc* desc, const int32_t* idx_a, co
 int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void* const* q_win,
                         const void* const* k, const void* const* v, const int32_t* budgets,
                         int32_t* const* idx_out, void* const* k_out, void* const* v_out,
-                        int32_t* const* pos_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
+                        int32_t* const* pos_out, void* ws, size_t ws_bytes, kvc_stream_t stream,
+                        kvc_stream_t aux_stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
   if (n_layers < 0) return fail(KVC_ERR_INVALID_ARG, "n_layers=%d < 0", n_layers);
   if (n_layers == 0) return KVC_OK;
   if (!q_win || !k || !v || !budgets || !idx_out || !k_out || !v_out || !pos_out)
     return fail(KVC_ERR_INVALID_ARG, "a per-layer pointer array is NULL");
+  const int n_lanes = aux_stream != nullptr && aux_stream != stream ? kSweepStreams : 1;
   const size_t one = ws_layout(L).total;  // a multiple of 256
-  if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", kSweepStreams * one);
-  if (ws_bytes < kSweepStreams * one)
-    return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, kSweepStreams * one);
+  if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", n_lanes * one);
+  if (ws_bytes < n_lanes * one)
+    return fail(KVC_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, n_lanes * one);
   if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
   std::vector<HeadTable> hts((size_t)n_layers);
   for (int32_t i = 0; i < n_layers; ++i) {
@@ -959,34 +940,36 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
     if (bt != KVC_OK) return fail(bt, "layer %d: %s", i, g_last_error.c_str());
   }
   KVC_TRY(check_lds(L));
-  hipStream_t lanes[kSweepStreams];
-  lanes[0] = static_cast<hipStream_t>(stream);
-  for (int j = 1; j < kSweepStreams; ++j) KVC_TRY(aux_stream(j - 1, lanes[j]));
-  // fork: the other lanes start after the caller's earlier work
-  hipEvent_t ev;
-  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-  if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-  e = hipEventRecord(ev, lanes[0]);
-  for (int j = 1; j < kSweepStreams && e == hipSuccess; ++j) e = hipStreamWaitEvent(lanes[j], ev, 0);
-  (void)hipEventDestroy(ev);
-  if (e != hipSuccess) return hip_fail(e, "sweep fork");
-  // the scans stay three launches here: a fused scan needs the whole device
-  // resident, so two of them must not overlap (and fusing gained nothing
-  // here: 77.8-78.8 against 78.3 us per 64K layer)
+  hipStream_t lanes[kSweepStreams] = {static_cast<hipStream_t>(stream), static_cast<hipStream_t>(aux_stream)};
+  hipError_t e = hipSuccess;
+  if (n_lanes > 1) {
+    // fork: the second lane starts after the caller's earlier work
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    e = hipEventRecord(ev, lanes[0]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(lanes[1], ev, 0);
+    (void)hipEventDestroy(ev);
+    if (e != hipSuccess) return hip_fail(e, "sweep fork");
+  }
+  // with two lanes the scans stay three launches: a fused scan needs the
+  // whole device resident, so two of them must not overlap (and fusing
+  // gained nothing there: 77.8-78.8 against 78.3 us per 64K layer)
   int status = KVC_OK;
   for (int32_t i = 0; i < n_layers && status == KVC_OK; ++i) {
-    const int j = i % kSweepStreams;
+    const int j = i % n_lanes;
     status = enqueue_layer(L, q_win[i], k[i], v[i], hts[(size_t)i], nullptr, nullptr, nullptr, idx_out[i],
                            k_out[i], v_out[i], pos_out[i], static_cast<char*>(ws) + j * one, lanes[j], nullptr, 0,
-                           false);
+                           n_lanes == 1);
   }
-  // join: later work on the caller's stream waits for every lane (also after
-  // a failed launch, so that nothing of this call outlives the caller's order)
-  for (int j = 1; j < kSweepStreams; ++j) {
+  if (n_lanes > 1) {
+    // join: later work on the caller's stream waits for the second lane (also
+    // after a failed launch, so that nothing of this call outlives the
+    // caller's order)
     hipEvent_t jv;
     e = hipEventCreateWithFlags(&jv, hipEventDisableTiming);
     if (e == hipSuccess) {
-      e = hipEventRecord(jv, lanes[j]);
+      e = hipEventRecord(jv, lanes[1]);
       if (e == hipSuccess) e = hipStreamWaitEvent(lanes[0], jv, 0);
       (void)hipEventDestroy(jv);
     }

@@ -226,7 +226,8 @@ int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k
  * key). m, z as written by kvc_score_pass1. scores: device fp32 [hkv][S],
  * scores[g][j] = sum over window queries i and query heads h of group g of
  * exp(l - m[h][i]) / z[h][i] (0 where key j is after query i). Each head's
- * scores sum to W * G up to rounding. Needs no workspace.
+ * scores sum to W * G up to rounding. Needs no workspace, so it takes none
+ * (unlike pass 1, which keeps its split partials there).
  */
 int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k,
                     const float* m, const float* z, float* scores,
@@ -287,8 +288,8 @@ int kvc_gather_retained(const kvc_layer_desc* desc, const void* k, const void* v
  * is bounded (about a second), so the launch always ends, but if other work
  * holds the device's compute units for that long the call's outputs are not
  * valid. Calls that overlap on several streams of one device should not
- * both take this path (kvc_compress_layers, which overlaps two layers on two
- * streams, keeps its scans as three launches); setting the environment
+ * both take this path (kvc_compress_layers, when it overlaps two layers on
+ * two streams, keeps its scans as three launches); setting the environment
  * variable KVC_FUSED=0 before the first call keeps the scans as separate
  * launches everywhere. The workspace needs no initialisation: the waits
  * use flags stamped with a value that is new for every launch.
@@ -335,22 +336,26 @@ int kvc_overlap_coefficient(const kvc_layer_desc* desc, const int32_t* idx_a, co
  * A layer-major sweep (TideKV, Fig. 2 caption: layers are compressed one
  * after another at their layer boundaries): n_layers layers of the one shape
  * `desc`, layer i compressed exactly as kvc_compress_layer would (same
- * outputs, bit for bit, with m, z and scores kept in the workspace). Layers
- * alternate between `stream` and a second stream that the library creates
- * per device on first use (non-blocking, default priority, kept until the
- * process ends), so that one layer's selection and gather overlap the next
- * layer's scans. The call is ordered after earlier work on `stream`, and
- * later work on `stream` is ordered after all of it.
+ * outputs, bit for bit, with m, z and scores kept in the workspace).
+ * aux_stream: a second stream of the caller's (not `stream`, default
+ * priority), or NULL. With one, layers alternate between the two streams, so
+ * that one layer's selection and gather overlap the next layer's scans (the
+ * scans then stay three launches: two fused scan launches must not overlap);
+ * with NULL every layer runs on `stream`, as kvc_compress_layer would. The
+ * call is ordered after earlier work on `stream` (the second stream waits for
+ * it through an event), and later work on `stream` is ordered after all of
+ * it; the library creates no stream and keeps nothing.
  * q_win, k, v, idx_out, k_out, v_out, pos_out: HOST arrays of n_layers device
  * pointers, each as for kvc_compress_layer; budgets: HOST int32
- * [n_layers][hkv]. ws: at least 2 * kvc_workspace_size(desc) bytes (one
- * workspace per stream), 256-byte aligned. n_layers == 0 enqueues nothing.
+ * [n_layers][hkv]. ws: at least 2 * kvc_workspace_size(desc) bytes with a
+ * second stream (one workspace per stream), kvc_workspace_size(desc) without,
+ * 256-byte aligned. n_layers == 0 enqueues nothing.
  */
 int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers,
                         const void* const* q_win, const void* const* k, const void* const* v,
                         const int32_t* budgets, int32_t* const* idx_out,
                         void* const* k_out, void* const* v_out, int32_t* const* pos_out,
-                        void* ws, size_t ws_bytes, kvc_stream_t stream);
+                        void* ws, size_t ws_bytes, kvc_stream_t stream, kvc_stream_t aux_stream);
 
 /*
  * Immediate (chunk-boundary) eviction, the schedule that TideKV's layer-end

@@ -159,7 +159,8 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
 
 def test_sweep_rejects_bad_arguments_before_launch():
     """kvc_compress_layers checks every layer's pointers and budgets and the
-    doubled workspace before anything is enqueued (no GPU needed)."""
+    workspace (doubled when the caller gives a second stream) before anything
+    is enqueued (no GPU needed)."""
     lib = kvc.lib()
     d = base_desc()
     dd = ctypes.byref(d)
@@ -178,14 +179,20 @@ def test_sweep_rejects_bad_arguments_before_launch():
     cols = [arr(good) for _ in range(7)]
     ws = _fake(0x100000)
 
-    def call(cols=cols, budgets=bp, ws=ws, ws_bytes=2 * ws_n, n_layers=n):
+    aux = _fake(0x7000)  # the caller's second stream (never used: validation fails first)
+
+    def call(cols=cols, budgets=bp, ws=ws, ws_bytes=2 * ws_n, n_layers=n, aux_stream=aux):
         return lib.kvc_compress_layers(dd, n_layers, cols[0], cols[1], cols[2], budgets, cols[3],
-                                       cols[4], cols[5], cols[6], ws, ws_bytes, None)
+                                       cols[4], cols[5], cols[6], ws, ws_bytes, None, aux_stream)
 
     assert call(n_layers=0) == kvc.KVC_OK  # nothing to do, nothing touched
     assert call(n_layers=-1) == kvc.KVC_ERR_INVALID_ARG
     assert call(ws_bytes=2 * ws_n - 1) == kvc.KVC_ERR_WORKSPACE
     assert call(ws_bytes=ws_n) == kvc.KVC_ERR_WORKSPACE  # one workspace per stream
+    # one stream: one workspace is enough (the call then gets past the
+    # workspace check and fails only where it needs a device)
+    assert call(ws_bytes=ws_n - 1, aux_stream=None) == kvc.KVC_ERR_WORKSPACE
+    assert call(ws_bytes=ws_n, aux_stream=None) not in (kvc.KVC_OK, kvc.KVC_ERR_WORKSPACE)
     assert call(ws=_fake(0x100080)) == kvc.KVC_ERR_ALIGN
     assert call(budgets=None) == kvc.KVC_ERR_INVALID_ARG
     for j in range(7):
@@ -404,3 +411,25 @@ def test_plan_fused_scans_need_a_device():
         pytest.skip("a GPU driver is present: the plan reflects that device")
     assert kvc.kvc_plan_layer(base_desc(s=65536)).fused_scans == 0
     assert kvc.kvc_plan_layer(base_desc(s=65536, score_mode=kvc.KVC_SCORE_LOGIT)).fused_scans == 0
+
+
+def test_boundary_deviations_are_as_declared():
+    """The calls whose arguments differ from the proposed boundary, as the
+    header declares them: pass 2 takes no workspace, the sweep takes the
+    caller's optional second stream, and the scans-only call takes a
+    workspace like pass 1."""
+    import re
+    text = open(HEADER).read()
+
+    def params(name):
+        m = re.search(r"\bint\s+" + name + r"\s*\(([^)]*)\)\s*;", text, re.S)
+        assert m, name
+        return [p.strip() for p in m.group(1).split(",")]
+
+    p2 = params("kvc_score_pass2")
+    assert not any("ws" in p.split()[-1] for p in p2), p2
+    assert p2[-1].endswith("stream")
+    sweep = params("kvc_compress_layers")
+    assert sweep[-2].endswith(" stream") and sweep[-1].endswith("aux_stream"), sweep[-2:]
+    sl = params("kvc_score_layer")
+    assert any(p.endswith("ws") for p in sl) and any(p.endswith("ws_bytes") for p in sl)

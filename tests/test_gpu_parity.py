@@ -456,9 +456,9 @@ def test_score_layer_equals_staged_and_whole_layer(name, over):
 @pytest.mark.parametrize("name,s,n_layers", [("llama8b_16k", 8192, 5), ("qwen14b_hetero_64k", 8192, 4)])
 def test_sweep_equals_layer_by_layer(name, s, n_layers):
     """kvc_compress_layers over several layers (alternating between the
-    caller's stream and the library's second stream) writes what one
-    kvc_compress_layer call per layer writes, bit for bit, and later work on
-    the caller's stream sees all of it."""
+    caller's two streams) writes what one kvc_compress_layer call per layer
+    writes, bit for bit, and later work on the caller's stream sees all of
+    it; so does a sweep on one stream."""
     cfg = get_config(name).with_(s=s)
     xs = [layer_inputs(cfg, l) for l in range(n_layers)]
     layers = [dev_inputs(x) for x in xs]
@@ -472,7 +472,7 @@ def test_sweep_equals_layer_by_layer(name, s, n_layers):
         o.k_hat.view(torch.int16).fill_(-7)
     ws = kvc.alloc_sweep_workspace(desc)
     say(f"sweep {name}: one sweep call")
-    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws)
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws, aux_stream=torch.cuda.Stream())
     # ordered after the sweep on the caller's stream, no host synchronisation
     copies = [(o.idx.clone(), o.k_hat.clone(), o.v_hat.clone(), o.pos.clone()) for o in outs]
     torch.cuda.synchronize()
@@ -482,10 +482,18 @@ def test_sweep_equals_layer_by_layer(name, s, n_layers):
         np.testing.assert_array_equal(from_dev_bits(copies[i][2]), want[i]["v_hat"], err_msg=f"v_hat {i}")
         np.testing.assert_array_equal(copies[i][3].cpu().numpy(), want[i]["pos"], err_msg=f"pos {i}")
     # a second sweep into the same buffers gives the same bits again
-    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws)
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws, aux_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     for i in range(n_layers):
         np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"], err_msg=f"repeat idx {i}")
+    # one stream (the scans may then fuse, as in kvc_compress_layer)
+    for o in outs:
+        o.idx.fill_(-7)
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws[:kvc.kvc_workspace_size(desc)])
+    torch.cuda.synchronize()
+    for i in range(n_layers):
+        np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"], err_msg=f"one-stream idx {i}")
+        np.testing.assert_array_equal(from_dev_bits(outs[i].k_hat), want[i]["k_hat"], err_msg=f"one-stream k_hat {i}")
 
 
 def test_binding_errors_on_gpu():

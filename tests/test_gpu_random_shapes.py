@@ -244,7 +244,7 @@ def test_random_shape_layer_sweep(i):
     desc = desc_from(cfg, *layers[0])
     want = [run_fused(desc, *layers[l], bl[l], intermediates=False) for l in range(n_layers)]
     outs = [kvc.alloc_outputs(desc, bl[l], with_intermediates=False) for l in range(n_layers)]
-    kvc.kvc_compress_layers(desc, layers, bl, outs, kvc.alloc_sweep_workspace(desc))
+    kvc.kvc_compress_layers(desc, layers, bl, outs, kvc.alloc_sweep_workspace(desc), aux_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     from gpu_util import from_dev_bits
     for l in range(n_layers):

@@ -230,7 +230,7 @@ def test_sweep_in_a_raw_inner_product_mode_equals_layer_by_layer():
     want = [run_fused(desc, *layers[i], budgets[i], intermediates=False) for i in range(3)]
     outs = [kvc.alloc_outputs(desc, budgets[i], with_intermediates=False) for i in range(3)]
     ws = kvc.alloc_sweep_workspace(desc)
-    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws)
+    kvc.kvc_compress_layers(desc, layers, budgets, outs, ws, aux_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     for i in range(3):
         np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"])
