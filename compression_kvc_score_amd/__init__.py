@@ -3,7 +3,7 @@ top-k selection and retained-cache gather) as a C-ABI HIP library, with a thin
 Python binding whose functions carry the C entry points' names."""
 from ._lib import (  # noqa: F401
     KVC_ERR_ALIGN, KVC_ERR_HIP, KVC_ERR_INVALID_ARG, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE,
-    KVC_SCORE_LOGIT, KVC_SCORE_LOGIT_INT8, KVC_SCORE_SOFTMAX, kvc_overlap_coefficient,
+    KVC_SCORE_LOGIT, KVC_SCORE_LOGIT_INT8, KVC_SCORE_SOFTMAX, KVC_FLAG_FUSED_SELECT, kvc_overlap_coefficient,
     KVC_MAX_KV_HEADS, KVC_MAX_POOL, KVC_MAX_ROWS, KVC_OK, LIB_PATH, KvcError, LayerDesc,
     LayerOutputs, PreparedLayer, PreparedSweep, SWEEP_STREAMS, alloc_outputs, alloc_sweep_workspace,
     alloc_workspace, compress_layer, desc_for, kvc_budgets_inverse_stability,

@@ -30,6 +30,7 @@ KVC_NOALLOC_SCRATCH_BYTES = 16 << 20
 KVC_SCORE_SOFTMAX = 0
 KVC_SCORE_LOGIT = 1
 KVC_SCORE_LOGIT_INT8 = 2
+KVC_FLAG_FUSED_SELECT = 1  # select and gather inside the fused scan launch, scores on chip
 KVC_SCAN_STREAM = 1
 KVC_SCAN_PER_HEAD = 2
 KVC_SCAN_LOGIT = 3
@@ -62,6 +63,8 @@ class LayerDesc(ctypes.Structure):
         ("k_head_stride", ctypes.c_int64),
         ("v_tok_stride", ctypes.c_int64),
         ("v_head_stride", ctypes.c_int64),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -73,6 +76,7 @@ class LayerPlan(ctypes.Structure):
         ("splits", ctypes.c_int32),
         ("hist_in_scan", ctypes.c_int32),
         ("fused_scans", ctypes.c_int32),
+        ("fused_select", ctypes.c_int32),
         ("keys_per_wg", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -92,12 +96,12 @@ class PrefillDesc(ctypes.Structure):
 
 def make_desc(s, w, hq, hkv, d, block=256, scale=0.0, n_sink=0, n_recent=0, pool=1,
               pos_offset=0, q_strides=(0, 0), k_strides=(0, 0), v_strides=(0, 0),
-              score_mode=0) -> LayerDesc:
+              score_mode=0, flags=0) -> LayerDesc:
     return LayerDesc(s=s, w=w, hq=hq, hkv=hkv, d=d, block=block, scale=scale, n_sink=n_sink,
                      n_recent=n_recent, pool=pool, score_mode=score_mode, pos_offset=pos_offset,
                      q_tok_stride=q_strides[0], q_head_stride=q_strides[1],
                      k_tok_stride=k_strides[0], k_head_stride=k_strides[1],
-                     v_tok_stride=v_strides[0], v_head_stride=v_strides[1])
+                     v_tok_stride=v_strides[0], v_head_stride=v_strides[1], flags=flags, reserved=0)
 
 
 _lib = None
@@ -202,7 +206,7 @@ def _host_i32(arr, n, name):
 
 
 def desc_for(q_win, k, v=None, *, block=256, scale=0.0, n_sink=0, n_recent=0, pool=1,
-             pos_offset=0, score_mode=0) -> LayerDesc:
+             pos_offset=0, score_mode=0, flags=0) -> LayerDesc:
     """Descriptor for tensors Q_win [W, hq, D] and K (V) [S, hkv, D] with their
     strides (the head dimension must be contiguous)."""
     w, hq, d = q_win.shape
@@ -211,7 +215,7 @@ def desc_for(q_win, k, v=None, *, block=256, scale=0.0, n_sink=0, n_recent=0, po
         raise ValueError("Q_win and K head dimensions differ")
     vs = (v.stride(0), v.stride(1)) if v is not None else (0, 0)
     return make_desc(s, w, hq, hkv, d, block=block, scale=scale, n_sink=n_sink,
-                     n_recent=n_recent, pool=pool, pos_offset=pos_offset, score_mode=score_mode,
+                     n_recent=n_recent, pool=pool, pos_offset=pos_offset, score_mode=score_mode, flags=flags,
                      q_strides=(q_win.stride(0), q_win.stride(1)),
                      k_strides=(k.stride(0), k.stride(1)), v_strides=vs)
 

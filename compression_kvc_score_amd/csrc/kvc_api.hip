@@ -155,6 +155,8 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
     return fail(KVC_ERR_UNSUPPORTED, "s=%lld > 2^22 with signed (raw inner-product) scores", (long long)d->s);
   if (d->pos_offset < 0 || d->pos_offset + d->s > kInt32Max)
     return fail(KVC_ERR_INVALID_ARG, "pos_offset=%lld: positions must fit in int32", (long long)d->pos_offset);
+  if ((d->flags & ~KVC_FLAG_FUSED_SELECT) != 0)
+    return fail(KVC_ERR_INVALID_ARG, "flags=0x%x has unknown bits", (unsigned)d->flags);
 
   const int64_t strides[6] = {d->q_tok_stride, d->q_head_stride, d->k_tok_stride,
                               d->k_head_stride, d->v_tok_stride, d->v_head_stride};
@@ -186,9 +188,25 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   L.v_head = d->v_head_stride ? d->v_head_stride : d->d;
 
   // Streaming scans for up to four query-row tiles per KV head; head pairs
-  // when the KV heads pair up and a slot's copy offsets stay in 32 bits.
+  // when the KV heads pair up and a slot's copy offsets stay in 32 bits. The
+  // selection inside the scan launch takes one head per workgroup.
+  L.fsel = (d->flags & KVC_FLAG_FUSED_SELECT) != 0;
   L.stream_hg = 0;
-  if (L.row_tiles <= 4 && stream_scans_enabled()) {
+  if (L.fsel) {
+    if (L.score_mode != KVC_SCORE_SOFTMAX || L.pool != 1)
+      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT needs softmax scores and pool 1");
+    if (L.row_tiles > 4 || !stream_offsets_fit(L, 1))
+      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT needs G*W <= 128 and the streaming scans");
+    // the fused kernel's wavefronts split a head's row tiles into row groups
+    // of equal size, at most two tiles each: pad to that (padding rows are
+    // masked like the ones past G*W in the last tile)
+    const int rs = stream_row_groups(L.d, 1);
+    L.row_tiles = (L.row_tiles + rs - 1) / rs * rs;
+    if (L.row_tiles / rs > 2)
+      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: %d query rows per KV head > %d with d=%d",
+                  L.rows, 64 * rs, L.d);
+    L.stream_hg = 1;
+  } else if (L.row_tiles <= 4 && stream_scans_enabled()) {
     if (L.hkv % 2 == 0 && stream_offsets_fit(L, 2)) L.stream_hg = 2;
     else if (stream_offsets_fit(L, 1)) L.stream_hg = 1;
   }
@@ -203,6 +221,9 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   const int64_t want_bpw = ((int64_t)L.n_blocks * groups + target - 1) / target;
   L.blocks_per_wg = (int)std::max<int64_t>(1, std::max(min_bpw, want_bpw));
   L.n_split = (L.n_blocks + L.blocks_per_wg - 1) / L.blocks_per_wg;
+  if (L.fsel && (int64_t)L.blocks_per_wg * unit > kFselMaxSegKeys)
+    return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: %lld keys per workgroup > %d (s too long for the grid)",
+                (long long)L.blocks_per_wg * unit, kFselMaxSegKeys);
   return KVC_OK;
 }
 
@@ -246,6 +267,7 @@ int n_subs(const Layer& L) { return (int)((L.s + kSub - 1) / kSub); }
 struct WsLayout {
   size_t sync, part, m, z, scores, pooled;
   size_t hist, slots;
+  size_t ghist, segcnt;  // the selection inside the scan launch
   size_t total;
 };
 
@@ -257,20 +279,38 @@ WsLayout ws_layout(const Layer& L) {
   off += align_up(kSyncBytes, 256);
   w.hist = off;
   off += align_up((size_t)L.hkv * kHistBins * 4, 256);
-  w.slots = off;
-  off += align_up((size_t)L.hkv * nc * kSlotStride * 4, 256);
   w.part = off;
   off += align_up((size_t)L.hkv * kMaxSplit * L.row_tiles * kRowTile * sizeof(float2), 256);
   w.m = off;
   off += align_up((size_t)L.hq * L.w * sizeof(float), 256);
   w.z = off;
   off += align_up((size_t)L.hq * L.w * sizeof(float), 256);
+  if (L.fsel) {
+    // scores stay on chip: only the radix round histograms and the segments'
+    // counts, none of it growing with s
+    w.ghist = off;
+    off += align_up((size_t)L.hkv * (kFselR1Bins + kFselR2Bins) * 4, 256);
+    w.segcnt = off;
+    off += align_up((size_t)L.hkv * kMaxSplit * 2 * 4, 256);
+    w.slots = w.scores = w.pooled = off;  // (none)
+    w.total = off;
+    return w;
+  }
+  w.slots = off;
+  off += align_up((size_t)L.hkv * nc * kSlotStride * 4, 256);
   w.scores = off;
   off += align_up((size_t)L.hkv * L.s * sizeof(float), 256);
   w.pooled = off;
   if (L.pool > 1) off += align_up((size_t)L.hkv * L.s * sizeof(float), 256);
   w.total = off;
   return w;
+}
+
+// Entry points whose contract involves the s-length score vector or the
+// staged selection's bookkeeping reject KVC_FLAG_FUSED_SELECT.
+int reject_fsel(const Layer& L, const char* what) {
+  if (!L.fsel) return KVC_OK;
+  return fail(KVC_ERR_INVALID_ARG, "%s does not take KVC_FLAG_FUSED_SELECT (kvc_compress_layer does)", what);
 }
 
 int check_ws(const Layer& L, const void* ws, size_t ws_bytes) {
@@ -305,7 +345,7 @@ int check_lds(const Layer& L) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], lim, __ATOMIC_RELAXED);
   }
-  const size_t scan = L.stream_hg ? std::max(pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L))
+  const size_t scan = L.stream_hg ? std::max({pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L), fused_lds_bytes(L)})
                                   : std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
   const size_t need = std::max(scan, select_lds_bytes(n_chunks(L), n_subs(L)) + 16384);
   if (need > (size_t)lim)
@@ -367,13 +407,11 @@ int run_pass2(const Layer& L, const void* q, const void* k, const float* m, cons
   return KVC_OK;
 }
 
-// need_hist: the selection clears and builds its own histogram (and pooled
-// values); otherwise pass 1 cleared it and pass 2 built it. k != nullptr: the
-// compaction also copies the retained K/V rows and writes their positions.
-int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
-               void* ws, bool need_hist, hipStream_t st, const void* k = nullptr,
-               const void* v = nullptr, void* k_out = nullptr, void* v_out = nullptr,
-               int32_t* pos_out = nullptr, const int32_t* pos_in = nullptr, int64_t pos_in_head = 0) {
+// Arguments of the selection; k != nullptr: the retained K/V rows are copied
+// and their positions written too.
+SelectArgs select_args(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out, void* ws,
+                       const void* k, const void* v, void* k_out, void* v_out, int32_t* pos_out,
+                       const int32_t* pos_in, int64_t pos_in_head) {
   const WsLayout lay = ws_layout(L);
   char* wsb = static_cast<char*>(ws);
   SelectArgs a{};
@@ -406,6 +444,17 @@ int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t
     a.pos_in_head = pos_in_head;
     a.d = L.d;
   }
+  return a;
+}
+
+// need_hist: the selection clears and builds its own histogram (and pooled
+// values); otherwise pass 1 cleared it and pass 2 built it. k != nullptr: the
+// compaction also copies the retained K/V rows and writes their positions.
+int run_select(const Layer& L, const float* scores, const HeadTable& ht, int32_t* idx_out,
+               void* ws, bool need_hist, hipStream_t st, const void* k = nullptr,
+               const void* v = nullptr, void* k_out = nullptr, void* v_out = nullptr,
+               int32_t* pos_out = nullptr, const int32_t* pos_in = nullptr, int64_t pos_in_head = 0) {
+  const SelectArgs a = select_args(L, scores, ht, idx_out, ws, k, v, k_out, v_out, pos_out, pos_in, pos_in_head);
   const hipError_t e = launch_select(L, a, need_hist || L.pool > 1, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return KVC_OK;
@@ -516,7 +565,7 @@ int enqueue_scans(const Layer& L, const void* q_win, const void* k, float* m, fl
     a.scores = sc;
     a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
     a.epoch = next_epoch();
-    const hipError_t e = launch_stream_fused(L, a, st);
+    const hipError_t e = launch_stream_fused(L, a, SelectArgs{}, st);
     if (e != hipSuccess) return hip_fail(e, "fused scan launch");
     return KVC_OK;
   }
@@ -535,6 +584,31 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
   char* wsb = static_cast<char*>(ws);
   float* m = m_out ? m_out : reinterpret_cast<float*>(wsb + lay.m);
   float* z = z_out ? z_out : reinterpret_cast<float*>(wsb + lay.z);
+  if (L.fsel) {
+    // one launch: both scans, the selection and the gather; the scores stay
+    // on chip (written out only when the caller asks for them)
+    if (!use_fused_scans(L))
+      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: the %d workgroups of the fused launch do not fit "
+                  "the device at once", L.hkv * L.n_split);
+    ScoreArgs a = score_args(L, q_win, k);
+    a.part = reinterpret_cast<float*>(wsb + lay.part);
+    a.hist = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+    a.m_out = m;
+    a.m_in = m;
+    a.z_out = z;
+    a.z_in = z;
+    a.scores = scores_out;
+    a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
+    a.epoch = next_epoch();
+    a.fsel_kpt = (int)((stream_keys_per_wg(L) + kFselThreadsHost - 1) / kFselThreadsHost);
+    a.ghist = reinterpret_cast<uint32_t*>(wsb + lay.ghist);
+    a.segcnt = reinterpret_cast<uint32_t*>(wsb + lay.segcnt);
+    const SelectArgs sa =
+        select_args(L, scores_out, ht, idx_out, ws, k, v, k_out, v_out, pos_out, pos_in, pos_in_head);
+    const hipError_t e = launch_stream_fused(L, a, sa, st);
+    if (e != hipSuccess) return hip_fail(e, "fused scan and selection launch");
+    return KVC_OK;
+  }
   float* sc = scores_out ? scores_out : reinterpret_cast<float*>(wsb + lay.scores);
   bool hist_built = false;
   KVC_TRY(enqueue_scans(L, q_win, k, m, z, sc, ws, st, &hist_built, allow_fused));
@@ -720,6 +794,7 @@ int kvc_plan_layer(const kvc_layer_desc* desc, kvc_layer_plan* plan) {
     p.keys_per_wg = L.stream_hg ? stream_keys_per_wg(L) : (int64_t)L.blocks_per_wg * L.block;
     p.hist_in_scan = L.pool == 1 && hist_fits_scan(L);
     p.fused_scans = use_fused_scans(L);
+    p.fused_select = L.fsel && p.fused_scans;
   }
   p.workspace_bytes = ws_layout(L).total;
   *plan = p;
@@ -780,6 +855,7 @@ int kvc_score_pass1(const kvc_layer_desc* desc, const void* q_win, const void* k
                     float* z_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
+  KVC_TRY(reject_fsel(L, "kvc_score_pass1"));
   KVC_TRY(check_ptr(q_win, 16, "q_win"));
   KVC_TRY(check_ptr(k, 16, "k"));
   KVC_TRY(check_ptr(m_out, 4, "m_out"));
@@ -795,6 +871,7 @@ int kvc_score_pass2(const kvc_layer_desc* desc, const void* q_win, const void* k
                     const float* z, float* scores, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
+  KVC_TRY(reject_fsel(L, "kvc_score_pass2"));
   KVC_TRY(check_ptr(q_win, 16, "q_win"));
   KVC_TRY(check_ptr(k, 16, "k"));
   KVC_TRY(check_ptr(scores, 4, "scores"));
@@ -810,6 +887,7 @@ int kvc_select_topk(const kvc_layer_desc* desc, const float* scores, const int32
                     int32_t* idx_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
+  KVC_TRY(reject_fsel(L, "kvc_select_topk"));
   KVC_TRY(check_ptr(scores, 4, "scores"));
   KVC_TRY(check_ptr(idx_out, 4, "idx_out"));
   HeadTable ht;
@@ -857,6 +935,7 @@ int kvc_score_layer(const kvc_layer_desc* desc, const void* q_win, const void* k
                     float* scores_out, void* ws, size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
+  KVC_TRY(reject_fsel(L, "kvc_score_layer"));
   KVC_TRY(check_ptr(q_win, 16, "q_win"));
   KVC_TRY(check_ptr(k, 16, "k"));
   if (m_out) KVC_TRY(check_ptr(m_out, 4, "m_out"));
@@ -926,7 +1005,8 @@ int kvc_compress_layers(const kvc_layer_desc* desc, int32_t n_layers, const void
   if (n_layers == 0) return KVC_OK;
   if (!q_win || !k || !v || !budgets || !idx_out || !k_out || !v_out || !pos_out)
     return fail(KVC_ERR_INVALID_ARG, "a per-layer pointer array is NULL");
-  const int n_lanes = aux_stream != nullptr && aux_stream != stream ? kSweepStreams : 1;
+  // the selection in the scan launch needs the whole device: one lane then
+  const int n_lanes = aux_stream != nullptr && aux_stream != stream && !L.fsel ? kSweepStreams : 1;
   const size_t one = ws_layout(L).total;  // a multiple of 256
   if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", n_lanes * one);
   if (ws_bytes < n_lanes * one)
@@ -991,6 +1071,7 @@ int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k
                     kvc_stream_t stream) {
   Layer Lc;
   KVC_TRY(normalize(desc, Lc));
+  KVC_TRY(reject_fsel(Lc, "kvc_evict_chunk"));
   if (budget < 0) return fail(KVC_ERR_INVALID_ARG, "budget=%d < 0", budget);
   if (n_kept < 0) return fail(KVC_ERR_INVALID_ARG, "n_kept=%lld < 0", (long long)n_kept);
   if (cap < n_kept + Lc.s || cap > kMaxPrompt)
@@ -1060,6 +1141,7 @@ int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* 
                          size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
+  KVC_TRY(reject_fsel(L, "kvc_compress_chunked"));
   ChunkedPlan p;
   KVC_TRY(chunked_plan(desc, chunk, budget, p));
   KVC_TRY(check_ptr(q_windows, 16, "q_windows"));

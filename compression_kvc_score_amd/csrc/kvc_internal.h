@@ -40,6 +40,7 @@ struct Layer {
   int n_split;        // workgroups per KV head (per head group when streaming)
   int stream_hg;      // 0: per-head scans; 1 or 2: streaming scans with this many heads per workgroup
   int score_mode;     // KVC_SCORE_*
+  bool fsel;          // KVC_FLAG_FUSED_SELECT: select inside the fused scan launch, scores on chip
 };
 
 // Arguments of the two scans and the split combine (passed by value).
@@ -64,10 +65,21 @@ struct ScoreArgs {
   // epoch (a value no earlier launch used), so they need no clearing
   uint64_t* sync;
   uint64_t epoch;
+  // selection inside the fused launch (0: none): segment keys per thread;
+  // the heads' radix round histograms [hkv][kFselR1Bins + kFselR2Bins] and
+  // per-segment counts [hkv][kMaxSplit][2]
+  int fsel_kpt;
+  uint32_t* ghist;
+  uint32_t* segcnt;
 };
 
 constexpr int kMaxFusedWgs = 1024;  // workgroups of one fused scan launch (one per compute unit)
-constexpr size_t kSyncBytes = (size_t)2 * kMaxFusedWgs * sizeof(uint64_t);
+constexpr int kFusedFlagSets = 6;   // partials, normalisers, scores + histogram, two radix rounds, counts
+constexpr size_t kSyncBytes = (size_t)kFusedFlagSets * kMaxFusedWgs * sizeof(uint64_t);
+constexpr int kFselMaxSegKeys = 4096;  // selection in the fused launch: keys of a segment, at most
+constexpr int kFselThreadsHost = 512;  // its threads per workgroup
+constexpr int kFselR1Bins = 1024;      // its radix rounds: 10 bits, then 9
+constexpr int kFselR2Bins = 512;
 
 // Arguments of the raw inner-product scan (score modes other than softmax).
 struct LogitArgs {
@@ -189,6 +201,7 @@ inline int scan_waves(const Layer& L) {
 
 // Streaming scans (G*W <= 128): head-group workgroups with K staged in LDS.
 int stream_tokens(int d, int hg);                  // tokens per ring slot of the streaming scans
+int stream_row_groups(int d, int hg);              // row groups sharing a key tile (RS)
 bool stream_offsets_fit(const Layer& L, int hg);  // a slot's copy offsets fit in 32 bits
 size_t pass1_stream_lds_bytes(const Layer& L);
 size_t pass2_stream_lds_bytes(const Layer& L);
@@ -197,7 +210,10 @@ hipError_t launch_stream(bool pass1, const Layer& L, const ScoreArgs& a, hipStre
 // set): true when the layer's shape has a fused kernel and its workgroups
 // can all be resident at once on a device of `cus` compute units.
 bool stream_fused_ok(const Layer& L, int cus);
-hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, hipStream_t st);
+// sel: the selection's arguments when a.fsel_kpt != 0 (else unused).
+hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, const SelectArgs& sel, hipStream_t st);
+// Dynamic LDS of the fused launch (with the segment's scores when the layer selects in it).
+size_t fused_lds_bytes(const Layer& L);
 
 // Dynamic LDS bytes of the scans.
 size_t pass1_lds_bytes(const Layer& L);

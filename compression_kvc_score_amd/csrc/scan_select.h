@@ -1,0 +1,256 @@
+// Selection and gather inside the fused scan launch, with each workgroup's
+// scores kept on chip (TideKV, Fig. 3 caption: per KV head the mandatory sink
+// and recent keys plus the top K_h - |R_mand| other keys by (score
+// descending, index ascending), in ascending key order, with a scoring
+// footprint that does not grow with S; Fig. 2 caption: their K and V rows and
+// absolute positions).
+//
+// A workgroup owns one KV head's key segment (its token range). Pass 2 leaves
+// the segment's scores in LDS and adds the segment's top-bit histogram to the
+// head's. Then, with a rendezvous of the head's workgroups before each step
+// that needs all of them:
+//
+//  1. b* = the histogram bin holding the head's k-th best candidate (every
+//     workgroup reads the head's histogram);
+//  2. two radix rounds over the LOW pattern bits of the candidates inside b*
+//     (the top 10 bits, then the other 9): each workgroup adds its segment's
+//     LDS histogram of the round's digit to the head's round histogram in
+//     device memory, and after the rendezvous every workgroup picks the same
+//     digit from it. This gives the exact pattern T of the k-th best
+//     candidate and how many candidates equal to T are taken (the lowest
+//     indices), whatever the ties;
+//  3. each workgroup publishes its segment's counts above and equal to T and
+//     reads those of the earlier segments;
+//  4. it writes its kept indices and positions in ascending order from there
+//     and copies the kept K and V rows.
+//
+// Device memory holds only the histograms and the per-segment counts, none of
+// which grows with S. Every decision a barrier depends on is the same for all
+// threads of the workgroup, and the same for every workgroup of a head.
+
+#pragma once
+
+#include "select_common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kFselThreads = 8 * kWave;  // the scan workgroup
+constexpr int kFselWaves = kFselThreads / kWave;
+constexpr int kFselMaxKpt = kFselMaxSegKeys / kFselThreads;  // segment keys per thread
+constexpr int kFselCopyUnroll = 4;       // row pieces in flight per thread
+static_assert(kFselThreads == kFselThreadsHost && kFselMaxKpt * kFselThreads == kFselMaxSegKeys, "host sizes");
+static_assert(kFselR1Bins == 1024 && kFselR2Bins == (int)KeyFmt<false>::R2_BINS, "radix round widths");
+
+__device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS of the selection (inside the scan's ring, idle by then).
+struct FselLds {
+  uint32_t hist[kFselR1Bins];      // this segment's radix round histogram
+  uint32_t ghist[kFselR1Bins];     // the head's, as read back
+  int32_t kept[kFselMaxSegKeys];   // kept keys of the segment, in order
+  uint32_t scratch[4 * kFselWaves];
+  uint32_t pick[2];
+  uint32_t bstar;
+};
+
+// This segment's histogram of `digit(u)` over its candidates u with
+// (u & mask) == prefix into the head's round histogram `g` (nb bins), then
+// publish and wait; returns with m.ghist holding the head's bins.
+template <int NB, typename Digit, typename Meet>
+__device__ __forceinline__ void fsel_round(const uint32_t (&bits)[kFselMaxKpt], const bool (&cand)[kFselMaxKpt],
+                                           uint32_t mask, uint32_t prefix, Digit digit, uint32_t* g, FselLds& m,
+                                           Meet meet) {
+  for (int i = threadIdx.x; i < NB; i += kFselThreads) m.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e)
+    if (cand[e] && (bits[e] & mask) == prefix) atomicAdd(&m.hist[digit(bits[e])], 1u);
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB; i += kFselThreads) {
+    const uint32_t c = m.hist[i];
+    if (c != 0u) atomicAdd(g + i, c);  // device scope: performed where every XCD sees it
+  }
+  meet();
+  for (int i = threadIdx.x; i < NB; i += kFselThreads) m.ghist[i] = ld_coh(g + i);
+  __syncthreads();
+}
+
+// Steps 1-4 for KV head `head`, segment [seg0, seg1) of split `split`; the
+// segment's scores are in LDS at `sc` (key seg0 + i at sc[i]). meet(n):
+// publish this workgroup's n-th selection flag and wait for the head's.
+template <typename Meet>
+__device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs& sa, int head, int split,
+                                            int64_t seg0, int64_t seg1, const float* sc, unsigned char* smem,
+                                            Meet meet) {
+  using KF = KeyFmt<false>;
+  FselLds& m = *reinterpret_cast<FselLds*>(smem);
+  const int t = threadIdx.x;
+  const int kpt = a.fsel_kpt;
+  const HeadGeom h = head_geom(sa, head);
+  const bool ranked = !h.keep_all && h.k_sel > 0;  // the same in every workgroup of the head
+  const int64_t k0 = seg0 + (int64_t)t * kpt;
+
+  // this thread's keys: contiguous, kpt of them
+  uint32_t bits[kFselMaxKpt];
+  bool cand[kFselMaxKpt];
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e) {
+    const int64_t j = k0 + e;
+    cand[e] = e < kpt && j < seg1 && is_candidate(h, j);
+    bits[e] = cand[e] ? KF::key(sc[j - seg0]) : 0u;
+  }
+  uint32_t* g1 = a.ghist + (int64_t)head * (kFselR1Bins + kFselR2Bins);
+  uint32_t* g2 = g1 + kFselR1Bins;
+  uint32_t* cnt = a.segcnt + (int64_t)head * kMaxSplit * 2;
+
+  uint32_t thr = 0xFFFFFFFFu, need_eq = 0u, gt_before = 0u, eq_before = 0u;
+  if (ranked) {
+    // ---- 1. b*: thread t owns bins 4095-8t .. 4088-8t (descending)
+    const uint32_t* hist = a.hist + (int64_t)head * kHistBins;
+    uint32_t c[8], loc = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      c[q] = ld_coh(hist + kHistBins - 1 - 8 * t - q);
+      loc += c[q];
+    }
+    if (t == 0) m.bstar = 0u;
+    uint32_t total;
+    uint32_t before = block_exclusive_scan<kFselWaves>(loc, m.scratch, total);
+    if (before < h.k_sel && h.k_sel <= before + loc) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (before < h.k_sel && h.k_sel <= before + c[q]) {
+          m.bstar = (uint32_t)(kHistBins - 1 - 8 * t - q);
+          m.pick[1] = h.k_sel - before;  // rank inside b*
+        }
+        before += c[q];
+      }
+    }
+    __syncthreads();
+    // (a histogram that missed keys cannot hold the k-th: b* would stay 0 and
+    // the rounds below pick from what is there; pass 2 counts every candidate)
+    const uint32_t bstar = m.bstar;
+    uint32_t rem = m.pick[1];
+    __syncthreads();
+    // ---- 2. radix rounds over the LOW bits inside b*
+    const uint32_t top = bstar << KF::LOW;
+    fsel_round<kFselR1Bins>(bits, cand, ~KF::LOW_MASK, top, [](uint32_t u) { return (u >> KF::R2) & 1023u; },
+                            g1, m, [&]() { meet(1); });
+    if (t < kWave) pick_digit_wave<kFselR1Bins>(m.ghist, rem, m.pick);
+    __syncthreads();
+    const uint32_t d1 = m.pick[0];
+    rem = m.pick[1];
+    __syncthreads();
+    const uint32_t pre2 = top | (d1 << KF::R2);
+    fsel_round<kFselR2Bins>(bits, cand, ~(KF::R2_BINS - 1u), pre2, [](uint32_t u) { return u & (KF::R2_BINS - 1u); },
+                            g2, m, [&]() { meet(2); });
+    if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
+    __syncthreads();
+    thr = pre2 | m.pick[0];
+    need_eq = m.pick[1];
+    __syncthreads();
+    // ---- 3. this segment's counts above and equal to T; the earlier ones'
+    uint32_t q2[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < kFselMaxKpt; ++e) {
+      q2[0] += cand[e] && bits[e] > thr;
+      q2[1] += cand[e] && bits[e] == thr;
+    }
+    block_sums<kFselWaves, 2>(q2, m.scratch);
+    if (t == 0) {
+      st_coh(cnt + 2 * split, q2[0]);
+      st_coh(cnt + 2 * split + 1, q2[1]);
+    }
+    meet(3);
+    uint32_t b2[2] = {0u, 0u};
+    for (int s = t; s < split; s += kFselThreads) {
+      b2[0] += ld_coh(cnt + 2 * s);
+      b2[1] += ld_coh(cnt + 2 * s + 1);
+    }
+    block_sums<kFselWaves, 2>(b2, m.scratch);
+    gt_before = b2[0];
+    eq_before = b2[1];
+  }
+
+  // ---- 4. kept indices and positions of this segment, then the row copy
+  uint32_t first, quota = 0u;
+  if (ranked) {
+    quota = need_eq > eq_before ? need_eq - eq_before : 0u;
+    first = mandatory_in(h, 0, seg0) + gt_before + (need_eq < eq_before ? need_eq : eq_before);
+  } else {
+    first = h.keep_all ? (uint32_t)seg0 : mandatory_in(h, 0, seg0);
+  }
+  // 1: kept; 2: equal to T (taken in key order while the quota lasts)
+  uint32_t flag[kFselMaxKpt], n_kept = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e) {
+    const int64_t j = k0 + e;
+    flag[e] = 0u;
+    if (e >= kpt || j >= seg1) continue;
+    if (h.keep_all || !is_candidate(h, j)) flag[e] = 1u;
+    else if (ranked) flag[e] = bits[e] > thr ? 1u : (bits[e] == thr ? 2u : 0u);
+    n_kept += flag[e] == 1u;
+    n_eq += flag[e] == 2u;
+  }
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<kFselWaves>((n_kept << 16) | n_eq, m.scratch, total);
+  uint32_t eq_seen = before & 0xFFFFu;
+  uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
+  const int64_t row0 = sa.heads.offset[head];
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e) {
+    bool keep = flag[e] == 1u;
+    if (flag[e] == 2u) {
+      keep = eq_seen < quota;
+      ++eq_seen;
+    }
+    if (keep) {
+      const int64_t o = (int64_t)first + p;
+      const int32_t j = (int32_t)(k0 + e);
+      if (o < h.budget) {
+        sa.idx_out[row0 + o] = j;
+        sa.pos_out[row0 + o] = sa.pos_in ? sa.pos_in[head * sa.pos_in_head + j] : (int32_t)(sa.pos_offset + j);
+      }
+      m.kept[p] = j;
+      ++p;
+    }
+  }
+  const uint32_t eq_all = total & 0xFFFFu;
+  int64_t n = (int64_t)(total >> 16) + (eq_all < quota ? eq_all : quota);
+  if (n > h.budget - (int64_t)first) n = h.budget - (int64_t)first;  // never past this head's rows
+  __syncthreads();
+  // a row is d/8 16-byte pieces of K then d/8 of V; consecutive threads take
+  // consecutive pieces, so each row is one contiguous read and write
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int cpr = sa.d >> 3;
+  const int units = 2 * cpr;
+  const int rpp = kFselThreads / units;  // rows per pass
+  const int u = t % units, r0 = t / units;
+  const bool is_k = u < cpr;
+  const int cu = is_k ? u : u - cpr;
+  const uint16_t* src = (is_k ? sa.k + (int64_t)head * sa.k_head : sa.v + (int64_t)head * sa.v_head) + cu * 8;
+  const int64_t tok = is_k ? sa.k_tok : sa.v_tok;
+  uint16_t* dst = (is_k ? sa.k_out : sa.v_out) + (row0 + first) * sa.d + cu * 8;
+  for (int64_t rb = r0; rb < n; rb += (int64_t)kFselCopyUnroll * rpp) {
+    u32x4 buf[kFselCopyUnroll];
+#pragma unroll
+    for (int i = 0; i < kFselCopyUnroll; ++i) {
+      const int64_t rr = rb + (int64_t)i * rpp;
+      if (rr < n) buf[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)m.kept[rr] * tok);
+    }
+#pragma unroll
+    for (int i = 0; i < kFselCopyUnroll; ++i) {
+      const int64_t rr = rb + (int64_t)i * rpp;
+      if (rr < n) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4*>(dst + rr * sa.d));
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kvc

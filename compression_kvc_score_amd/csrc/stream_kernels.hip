@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "kvc_internal.h"
+#include "scan_select.h"
 
 // 0 selects the job-at-a-time loops everywhere (for comparisons).
 #ifndef KVC_SLOT_PIPE
@@ -1025,14 +1026,28 @@ __device__ __forceinline__ float pass2_tile(const ScoreArgs& a, const uint4 (&qr
   return s + __shfl_xor(s, 32);
 }
 
-// Store a key's score and count it in the head's LDS histogram.
+// Store a key's score (to device memory unless the caller asked for none,
+// and to the segment's LDS copy when the launch selects) and count it in the
+// head's LDS histogram.
 __device__ __forceinline__ void emit_score(const ScoreArgs& a, float* out, uint32_t* lh, bool with_hist, int key,
-                                           float sum) {
-  out[key] = sum;
+                                           float sum, float* seg_sc = nullptr, int seg0 = 0) {
+  if (a.scores != nullptr) out[key] = sum;
+  if (seg_sc != nullptr) seg_sc[key - seg0] = sum;
   if (with_hist && key >= a.sink_end && key < a.rec_begin) {
     const uint32_t b = (__float_as_uint(sum) >> 19) & (kHistBins - 1);
     lds_add_u32(&lh[b >> 1], 1u << ((b & 1) * 16));
   }
+}
+
+// Where pass 2 leaves the segment's scores in LDS when the launch selects:
+// past the ring, the row biases and prompt positions, the histogram halves
+// and the row-group partial sums.
+template <int NRT, int HG>
+__device__ __forceinline__ float* pass2_seg_scores(unsigned char* smem) {
+  constexpr int ROWS_PAD = NRT * kRowTile;
+  return reinterpret_cast<float*>(smem + kRingBytes + HG * ROWS_PAD * (sizeof(float) + sizeof(int)) +
+                                  HG * (kHistBins / 2) * sizeof(uint32_t)) +
+         2 * 8 * kKeyTile;
 }
 
 // Pass 2 after its prologue: the ring's first slots are requested, qr holds
@@ -1050,6 +1065,10 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
   int* qpos_all = reinterpret_cast<int*>(bias_all + HG * ROWS_PAD);         // [HG][ROWS_PAD]
   uint32_t* hist2 = reinterpret_cast<uint32_t*>(qpos_all + HG * ROWS_PAD);  // [HG][kHistBins/2], u16 pairs
   float* psum = reinterpret_cast<float*>(hist2 + HG * (kHistBins / 2));     // [2][HG][KT][RS][32]
+  // the segment's scores when the launch selects (one head per workgroup)
+  float* seg_sc = a.fsel_kpt ? pass2_seg_scores<NRT, HG>(smem) : nullptr;
+  static_assert(R::WAVES == 8, "row-group partial sums: [2][8 wavefronts][32]");
+  const int seg0 = rg.t0;
   const int h0 = c.h0, lane = c.lane, wave = c.wave, half = c.half, l32 = c.l32, ntile = c.ntile;
   const int head = c.head, first_hidden = c.first_hidden;
   const Role ro = c.ro;
@@ -1068,7 +1087,7 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
   const float* bias = bias_all + ro.hl * ROWS_PAD;
   const int* qpos = qpos_all + ro.hl * ROWS_PAD;
   uint32_t* lh = hist2 + ro.hl * (kHistBins / 2);
-  float* out = a.scores + (int64_t)head * a.s;
+  float* out = a.scores != nullptr ? a.scores + (int64_t)head * a.s : nullptr;
   // row-group partial sums of slot n: psum[n & 1][hl][kt][rg][key]
   auto psum_at = [&](int n, int g) {
     return psum + ((((n & 1) * HG + ro.hl) * R::KT + ro.kt) * R::RS + g) * kKeyTile + l32;
@@ -1084,7 +1103,7 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
       float sum = v[0];
 #pragma unroll
       for (int g = 1; g < R::RS; ++g) sum += v[g];
-      emit_score(a, out, lh, with_hist, key, sum);
+      emit_score(a, out, lh, with_hist, key, sum, seg_sc, seg0);
     }
   };
 
@@ -1136,7 +1155,7 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
         if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
         if (n > 0) finish(n - 1);
       } else {
-        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum);
+        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum, seg_sc, seg0);
       }
     };
     for (int n = 0; n < rg.nst; n += 2) {
@@ -1161,7 +1180,7 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
       if constexpr (R::RS > 1) {
         if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
       } else {
-        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum);
+        if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum, seg_sc, seg0);
       }
     }
   }
@@ -1305,7 +1324,7 @@ __device__ __forceinline__ void group_merge(const ScoreArgs& a, int h0, int spli
 }
 
 template <int D, int NRT, int HG>
-__global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a) {
+__global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a, SelectArgs sa) {
   using R = Ring<D, HG>;
   constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
   constexpr int ROWS_PAD = NRT * kRowTile;
@@ -1323,6 +1342,11 @@ __global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a) {
   if (a.hist != nullptr && c.split == 0)
     for (int i = threadIdx.x; i < HG * kHistBins; i += blockDim.x)
       __hip_atomic_store(a.hist + (int64_t)c.h0 * kHistBins + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the selection's round histograms likewise (written after the first rendezvous)
+  if (HG == 1 && a.fsel_kpt && c.split == 0)
+    for (int i = threadIdx.x; i < kFselR1Bins + kFselR2Bins; i += blockDim.x)
+      __hip_atomic_store(a.ghist + (int64_t)c.h0 * (kFselR1Bins + kFselR2Bins) + i, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
 
   uint32_t off[R::NI];
   copy_offsets<D, HG>(a, c.wave, c.lane, off);
@@ -1364,6 +1388,23 @@ __global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a) {
     }
   }
   pass2_main<D, NRT, HG>(a, c, rg2, off, smem, qr, mv, zv, real_row);
+
+  if constexpr (HG == 1) {
+    if (a.fsel_kpt == 0) return;
+    // selection and gather, once the head's scores and histogram are complete
+    static_assert(sizeof(FselLds) <= kRingBytes, "the selection's LDS lives in the idle ring");
+    const float* seg_sc = pass2_seg_scores<NRT, HG>(smem);
+    uint64_t* pub3 = a.sync + 2 * kMaxFusedWgs + wg;
+    group_arrive(a, pub3 + c.split);
+    group_wait(a, pub3);
+    const int64_t seg0 = rg1.t0;
+    const int64_t seg1 = min((int64_t)a.s, seg0 + (int64_t)a.blocks_per_wg * R::TOKS);
+    scan_select(a, sa, c.h0, c.split, seg0, seg1, seg_sc, smem, [&](int n) {
+      uint64_t* pub = a.sync + (2 + n) * kMaxFusedWgs + wg;
+      group_arrive(a, pub + c.split);
+      group_wait(a, pub);
+    });
+  }
 }
 
 template <int D, int HG>
@@ -1428,6 +1469,11 @@ bool stream_offsets_fit(const Layer& L, int hg) {
   return span < (1LL << 32);
 }
 
+int stream_row_groups(int d, int hg) {
+  if (d == 128) return hg == 2 ? Ring<128, 2>::RS : Ring<128, 1>::RS;
+  return hg == 2 ? Ring<64, 2>::RS : Ring<64, 1>::RS;
+}
+
 size_t pass1_stream_lds_bytes(const Layer& L) {
   const size_t red = (size_t)L.stream_hg * slot_key_tiles(L) * L.row_tiles * kRowTile * sizeof(float2);
   return red > (size_t)kRingBytes ? red : (size_t)kRingBytes;
@@ -1446,16 +1492,24 @@ bool stream_fused_ok(const Layer& L, int cus) {
   return wgs <= cus && wgs <= kMaxFusedWgs;
 }
 
-hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, hipStream_t st) {
+size_t fused_lds_bytes(const Layer& L) {
+  // pass 1's reduction, the merge's (kWave rows x 8 partials past the ring),
+  // pass 2's, and the segment's scores after pass 2's when the launch selects
+  const size_t merge = (size_t)kRingBytes + (size_t)8 * kWave * sizeof(float2);
+  size_t p2 = pass2_stream_lds_bytes(L);
+  if (L.fsel) p2 += (size_t)L.blocks_per_wg * stream_tokens(L.d, L.stream_hg) * sizeof(float);
+  return std::max({pass1_stream_lds_bytes(L), p2, merge});
+}
+
+hipError_t launch_stream_fused(const Layer& L, const ScoreArgs& a, const SelectArgs& sel, hipStream_t st) {
   const void* fn = stream_fused_fn(L);
   if (fn == nullptr) return hipErrorInvalidValue;
-  // pass 1's reduction, the merge's (kWave rows x 8 partials past the ring) and pass 2's
-  const size_t merge = (size_t)kRingBytes + (size_t)8 * kWave * sizeof(float2);
-  const size_t lds = std::max({pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L), merge});
+  const size_t lds = fused_lds_bytes(L);
   const hipError_t e = ensure_lds(fn, lds);
   if (e != hipSuccess) return e;
   ScoreArgs args = a;
-  void* kargs[] = {&args};
+  SelectArgs sargs = sel;
+  void* kargs[] = {&args, &sargs};
   const dim3 grid((unsigned)(L.hkv / L.stream_hg * L.n_split));
   return hipLaunchKernel(fn, grid, dim3(8 * kWave), kargs, lds, st);
 }

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 #define KVC_MAX_KV_HEADS 64    /* hkv limit */
 #define KVC_MAX_ROWS 256       /* limit on G * W (query rows per KV head) */
 #define KVC_MAX_POOL 31        /* largest max-pool width */
@@ -136,7 +136,24 @@ typedef struct kvc_layer_desc {
   int64_t q_tok_stride, q_head_stride;
   int64_t k_tok_stride, k_head_stride;
   int64_t v_tok_stride, v_head_stride;
+  int32_t flags;     /* KVC_FLAG_* bits, 0 for none */
+  int32_t reserved;  /* 0 */
 } kvc_layer_desc;
+
+/*
+ * KVC_FLAG_FUSED_SELECT: kvc_compress_layer (and its _noalloc variant and
+ * kvc_compress_layers) run both scans, the selection and the gather as ONE
+ * launch in which every workgroup keeps its key segment's scores on chip, so
+ * the workspace does not grow with s at all and no fp32 score vector goes to
+ * device memory unless scores_out asks for it (TideKV, Fig. 3 caption:
+ * scoring temporaries O(W * b_s + K_l), independent of S). Outputs equal the
+ * unflagged call's bit for bit. Needs softmax scores, pool 1, G * W <= 128,
+ * at most 4096 keys of a head per workgroup (s up to about 128K with 8 KV
+ * heads on a 256-CU device) and a device whose compute units hold the whole
+ * launch at once; else KVC_ERR_UNSUPPORTED. The staged entry points and the
+ * chunk-boundary calls reject the flag (KVC_ERR_INVALID_ARG).
+ */
+#define KVC_FLAG_FUSED_SELECT 1
 
 /* KVC_ABI_VERSION of the built library. */
 int kvc_version(void);
@@ -154,7 +171,8 @@ const char* kvc_last_error(void);
  * NULL). Pure host function. Apart from the fp32 score and pooled-score
  * vectors (4 * hkv * s bytes each) and about 1 byte per key and KV head of
  * selection bookkeeping (4104 bytes per 4096 keys), it does not grow with s, following the
- * S-independent temporary bound of TideKV's Fig. 3 caption.
+ * S-independent temporary bound of TideKV's Fig. 3 caption; with
+ * KVC_FLAG_FUSED_SELECT none of it grows with s.
  * Returns 0 if the descriptor is invalid.
  */
 size_t kvc_workspace_size(const kvc_layer_desc* desc);
@@ -175,6 +193,8 @@ typedef struct kvc_layer_plan {
                               the last scan; 0: a separate histogram kernel does */
   int32_t fused_scans;     /* 1: kvc_compress_layer runs pass 1, the split merge and
                               pass 2 as one launch on the current device */
+  int32_t fused_select;    /* 1: that launch also selects and gathers, scores on chip
+                              (KVC_FLAG_FUSED_SELECT) */
   int64_t keys_per_wg;     /* keys of one KV head that one scan workgroup covers (at most) */
   size_t workspace_bytes;  /* kvc_workspace_size(desc) */
 } kvc_layer_plan;

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
         for n in names:
             assert hasattr(lib, n), f"{n} declared in {os.path.basename(header)} but not exported"
     assert len(declared_functions()) >= 10
-    assert kvc.kvc_version() == 1
+    assert kvc.kvc_version() == 2
 
 
 def test_strerror_names():
@@ -433,3 +433,62 @@ def test_boundary_deviations_are_as_declared():
     assert sweep[-2].endswith(" stream") and sweep[-1].endswith("aux_stream"), sweep[-2:]
     sl = params("kvc_score_layer")
     assert any(p.endswith("ws") for p in sl) and any(p.endswith("ws_bytes") for p in sl)
+
+
+FSEL = kvc.KVC_FLAG_FUSED_SELECT
+
+
+def test_fused_select_workspace_does_not_grow_with_s():
+    """With the selection inside the scan launch the scores stay on chip: the
+    workspace of the 8B-shaped layer is the same at 16K, 64K and 128K keys
+    (TideKV, Fig. 3 caption: temporaries independent of S), and far below the
+    unflagged one, which holds the fp32 score vector."""
+    sizes = {s: kvc.kvc_workspace_size(base_desc(s=s, flags=FSEL)) for s in (16384, 65536, 131072)}
+    assert len(set(sizes.values())) == 1, sizes
+    plain = {s: kvc.kvc_workspace_size(base_desc(s=s)) for s in (16384, 65536, 131072)}
+    assert plain[131072] > plain[16384]  # the unflagged one grows by 4 * hkv * s + bookkeeping
+    assert sizes[65536] < plain[65536] - 4 * 8 * 65536
+    # it also holds no per-key bookkeeping: the same for a shorter or longer prompt at 4K
+    assert kvc.kvc_workspace_size(base_desc(s=4096, flags=FSEL)) == sizes[16384]
+
+
+def test_fused_select_flag_is_validated():
+    lib = kvc.lib()
+    for bad in (2, 4, 1 << 30):
+        d = base_desc(s=65536, flags=bad)
+        assert lib.kvc_workspace_size(ctypes.byref(d)) == 0
+        with pytest.raises(kvc.KvcError):
+            kvc.kvc_plan_layer(d)
+    for kw in (dict(pool=7), dict(score_mode=kvc.KVC_SCORE_LOGIT), dict(w=64),  # 256 rows per KV head
+               dict(s=1 << 20)):  # 32768 keys of a head per workgroup
+        d = base_desc(**dict(dict(s=65536, flags=FSEL), **kw))
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kvc_plan_layer(d)
+        assert e.value.status == kvc.KVC_ERR_UNSUPPORTED, kw
+        assert "FUSED_SELECT" in str(e.value)
+    p = kvc.kvc_plan_layer(base_desc(s=131072, flags=FSEL))
+    assert p.scan == kvc.KVC_SCAN_STREAM and p.heads_per_wg == 1 and p.keys_per_wg <= 4096
+    assert p.hist_in_scan == 1
+    import os
+    if not os.path.exists("/dev/kfd"):
+        assert p.fused_select == 0 and p.fused_scans == 0  # no device to hold the launch
+
+
+def test_staged_entry_points_reject_the_fused_select_flag():
+    """The staged calls and the chunk-boundary calls keep the s-length score
+    vector or the staged selection's bookkeeping in their contract: they
+    reject the flag before anything else touches the arguments."""
+    lib = kvc.lib()
+    d = base_desc(s=65536, flags=FSEL)
+    dd = ctypes.byref(d)
+    P = _fake(0x10000)
+    n = kvc.kvc_workspace_size(d)
+    calls = {
+        "kvc_score_pass1": lambda: lib.kvc_score_pass1(dd, P, P, P, P, P, n, None),
+        "kvc_score_pass2": lambda: lib.kvc_score_pass2(dd, P, P, P, P, P, None),
+        "kvc_score_layer": lambda: lib.kvc_score_layer(dd, P, P, P, P, P, P, n, None),
+        "kvc_select_topk": lambda: lib.kvc_select_topk(dd, P, P, P, P, n, None),
+    }
+    for name, call in calls.items():
+        assert call() == kvc.KVC_ERR_INVALID_ARG, name
+        assert name in lib.kvc_last_error().decode() and "FUSED_SELECT" in lib.kvc_last_error().decode()

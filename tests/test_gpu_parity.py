@@ -562,3 +562,134 @@ def test_maximum_prompt_length():
     np.testing.assert_allclose(got["scores"].sum(axis=1, dtype=np.float64), cfg.w * cfg.group, rtol=1e-4)
     say("max prompt: oracle")
     check_layer(x, got, b)
+
+
+# --------------------------------------------------------------------------- selection inside the scan launch
+
+FSEL_CASES = [
+    ("tiny", {}, None),
+    ("llama8b_16k", {"s": 8192}, None),
+    ("llama8b_16k", {"s": 5000}, None),
+    ("llama8b_16k", {"s": 3333, "w": 7}, None),
+    ("llama8b_16k", {"s": 2049, "hq": 16, "w": 16}, None),
+    ("llama8b_16k", {"s": 2000}, "keep_all"),
+    ("llama8b_16k", {"s": 6000}, "mandatory_only"),
+    ("llama8b_16k", {"s": 9000}, "mixed"),
+    ("llama8b_64k", {}, None),
+    ("llama8b_64k", {"s": 131072}, None),
+]
+
+
+def _fsel_budgets(cfg, x, kind):
+    b = budgets_for(cfg, x)
+    if kind == "keep_all":
+        return np.full(cfg.hkv, cfg.s + 5, dtype=np.int64)
+    if kind == "mandatory_only":
+        return np.full(cfg.hkv, cfg.n_sink + cfg.n_recent, dtype=np.int64)
+    if kind == "mixed":
+        rng = np.random.default_rng(7)
+        m = cfg.n_sink + cfg.n_recent
+        return np.array([rng.choice([m, m + 1, 700, 3000, cfg.s, cfg.s + 9]) for _ in range(cfg.hkv)], dtype=np.int64)
+    return b
+
+
+def _staged_select(desc, q, k, v, scores, b):
+    """The staged selection and gather on given scores (a device tensor)."""
+    ws = kvc.alloc_workspace(desc)
+    out = kvc.alloc_outputs(desc, b)
+    kvc.kvc_select_topk(desc, scores, b, out.idx, ws)
+    kvc.kvc_gather_retained(desc, k, v, out.idx, b, out.k_hat, out.v_hat, out.pos)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def _fused_select_run(fdesc, q, k, v, b, intermediates=True):
+    ws = kvc.alloc_workspace(fdesc)
+    ws.fill_(255)  # no initialisation needed
+    out = kvc.alloc_outputs(fdesc, b, with_intermediates=intermediates)
+    kvc.compress_layer(fdesc, q, k, v, b, out, ws)
+    torch.cuda.synchronize()
+    return host(out), out
+
+
+@pytest.mark.parametrize("name,over,kind", FSEL_CASES)
+def test_fused_select_equals_staged_selection(name, over, kind):
+    """KVC_FLAG_FUSED_SELECT (scans, selection and gather in one launch, the
+    scores kept on chip): its retained set and rows equal, bit for bit, what
+    the staged selection and gather make of the same call's scores; its
+    scores, m and Z match the unflagged call's to float rounding (one KV head
+    per workgroup merges pass 1's partials in another order; with one KV head
+    per layer the order is the same and so are the bits), and the oracle's
+    within the parity tolerance."""
+    cfg = get_config(name).with_(**over) if over else get_config(name)
+    x = layer_inputs(cfg, 8)
+    q, k, v = dev_inputs(x)
+    b = _fsel_budgets(cfg, x, kind)
+    desc = desc_from(cfg, q, k, v)
+    fdesc = desc_from(cfg, q, k, v, flags=kvc.KVC_FLAG_FUSED_SELECT)
+    plan = kvc.kvc_plan_layer(fdesc)
+    say(f"fused select {name} {over} {kind}: splits {plan.splits}, keys per workgroup {plan.keys_per_wg}, "
+        f"workspace {plan.workspace_bytes} B (unflagged {kvc.kvc_workspace_size(desc)} B)")
+    assert plan.fused_select == 1
+    got, out = _fused_select_run(fdesc, q, k, v, b)
+    sel = _staged_select(desc, q, k, v, out.scores, b)
+    for key in ["idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(got[key], sel[key], err_msg=key)
+    want = run_fused(desc, q, k, v, b)
+    for key in ["m", "z", "scores"]:
+        if cfg.hkv == 1:
+            np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+        else:
+            np.testing.assert_allclose(got[key], want[key], rtol=2e-6, atol=1e-30, err_msg=key)
+    if cfg.s <= 16384:
+        check_layer(x, got, b, heads=[0, cfg.hkv - 1])
+    got2, _ = _fused_select_run(fdesc, q, k, v, b, intermediates=False)
+    for key in ["idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(got2[key], got[key], err_msg=f"no intermediates: {key}")
+
+
+def test_fused_select_identical_keys_tie_break():
+    """All keys equal: every candidate ties, and the lowest indices are kept
+    (the radix rounds count ties exactly; there is no list to overflow)."""
+    cfg = get_config("llama8b_16k").with_(s=12000)
+    x = layer_inputs(cfg, 1)
+    kk = np.repeat(x.k[:1], cfg.s, axis=0)
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(kk), to_dev_bf16(x.v)
+    b = np.full(cfg.hkv, 1000, dtype=np.int64)
+    fdesc = desc_from(cfg, q, k, v, flags=kvc.KVC_FLAG_FUSED_SELECT)
+    got, out = _fused_select_run(fdesc, q, k, v, b)
+    sel = _staged_select(desc_from(cfg, q, k, v), q, k, v, out.scores, b)
+    for key in ["idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(got[key], sel[key], err_msg=key)
+    n_free = 1000 - cfg.n_sink - cfg.n_recent
+    expect = np.concatenate([np.arange(cfg.n_sink), np.arange(cfg.n_sink, cfg.n_sink + n_free),
+                             np.arange(cfg.s - cfg.n_recent, cfg.s)])
+    for g, first in enumerate(split_heads(got["idx"], got["offsets"])):
+        np.testing.assert_array_equal(first, expect, err_msg=f"head {g}")
+
+
+def test_fused_select_offset_noalloc_and_sweep():
+    """The flag with a position offset, through the no-allocation call, and
+    through the sweep (which then runs its layers on one stream): the same
+    bits as one flagged kvc_compress_layer call per layer."""
+    cfg = get_config("llama8b_16k").with_(s=8192)
+    xs = [layer_inputs(cfg, l) for l in range(3)]
+    layers = [dev_inputs(x) for x in xs]
+    budgets = np.stack([budgets_for(cfg, x) for x in xs])
+    fdesc = desc_from(cfg, *layers[0], pos_offset=12345, flags=kvc.KVC_FLAG_FUSED_SELECT)
+    want = [_fused_select_run(fdesc, *layers[i], budgets[i], intermediates=False)[0] for i in range(3)]
+    assert want[0]["pos"].min() >= 12345
+    out = kvc.alloc_outputs(fdesc, budgets[0], with_intermediates=False)
+    kvc.kvc_compress_layer_noalloc(fdesc, *layers[0], budgets[0], out.idx, out.k_hat, out.v_hat, out.pos)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.idx.cpu().numpy(), want[0]["idx"])
+    np.testing.assert_array_equal(out.pos.cpu().numpy(), want[0]["pos"])
+    np.testing.assert_array_equal(from_dev_bits(out.k_hat), want[0]["k_hat"])
+    outs = [kvc.alloc_outputs(fdesc, budgets[i], with_intermediates=False) for i in range(3)]
+    kvc.kvc_compress_layers(fdesc, layers, budgets, outs, kvc.alloc_sweep_workspace(fdesc),
+                            aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for i in range(3):
+        np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"], err_msg=f"sweep idx {i}")
+        np.testing.assert_array_equal(from_dev_bits(outs[i].v_hat), want[i]["v_hat"], err_msg=f"sweep v_hat {i}")
+        np.testing.assert_array_equal(outs[i].pos.cpu().numpy(), want[i]["pos"], err_msg=f"sweep pos {i}")
