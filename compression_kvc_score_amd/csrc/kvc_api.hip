@@ -267,7 +267,7 @@ int n_subs(const Layer& L) { return (int)((L.s + kSub - 1) / kSub); }
 struct WsLayout {
   size_t sync, part, m, z, scores, pooled;
   size_t hist, slots;
-  size_t ghist, segcnt;  // the selection inside the scan launch
+  size_t ghist, segcnt, fslots;  // the selection inside the scan launch
   size_t total;
 };
 
@@ -286,12 +286,14 @@ WsLayout ws_layout(const Layer& L) {
   w.z = off;
   off += align_up((size_t)L.hq * L.w * sizeof(float), 256);
   if (L.fsel) {
-    // scores stay on chip: only the radix round histograms and the segments'
-    // counts, none of it growing with s
+    // scores stay on chip: only the radix round histograms, the segments'
+    // counts and lists, none of it growing with s
     w.ghist = off;
     off += align_up((size_t)L.hkv * (kFselR1Bins + kFselR2Bins) * 4, 256);
     w.segcnt = off;
     off += align_up((size_t)L.hkv * kMaxSplit * 2 * 4, 256);
+    w.fslots = off;
+    off += align_up((size_t)L.hkv * kMaxSplit * kFSlotWords * 4, 256);
     w.slots = w.scores = w.pooled = off;  // (none)
     w.total = off;
     return w;
@@ -603,6 +605,7 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
     a.fsel_kpt = (int)((stream_keys_per_wg(L) + kFselThreadsHost - 1) / kFselThreadsHost);
     a.ghist = reinterpret_cast<uint32_t*>(wsb + lay.ghist);
     a.segcnt = reinterpret_cast<uint32_t*>(wsb + lay.segcnt);
+    a.fslots = reinterpret_cast<uint32_t*>(wsb + lay.fslots);
     const SelectArgs sa =
         select_args(L, scores_out, ht, idx_out, ws, k, v, k_out, v_out, pos_out, pos_in, pos_in_head);
     const hipError_t e = launch_stream_fused(L, a, sa, st);

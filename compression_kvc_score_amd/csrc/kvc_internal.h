@@ -71,15 +71,17 @@ struct ScoreArgs {
   int fsel_kpt;
   uint32_t* ghist;
   uint32_t* segcnt;
+  uint32_t* fslots;  // per (head, segment) a list of the candidates inside b*: [hkv][kMaxSplit][kFSlotWords]
 };
 
 constexpr int kMaxFusedWgs = 1024;  // workgroups of one fused scan launch (one per compute unit)
-constexpr int kFusedFlagSets = 6;   // partials, normalisers, scores + histogram, two radix rounds, counts
+constexpr int kFusedFlagSets = 7;   // partials, normalisers, scores + histogram, lists, two radix rounds, counts
 constexpr size_t kSyncBytes = (size_t)kFusedFlagSets * kMaxFusedWgs * sizeof(uint64_t);
 constexpr int kFselMaxSegKeys = 4096;  // selection in the fused launch: keys of a segment, at most
 constexpr int kFselThreadsHost = 512;  // its threads per workgroup
 constexpr int kFselR1Bins = 1024;      // its radix rounds: 10 bits, then 9
 constexpr int kFselR2Bins = 512;
+constexpr int kFSlotWords = 256;       // a segment's list: 4 header words, then up to 252 entries
 
 // Arguments of the raw inner-product scan (score modes other than softmax).
 struct LogitArgs {

@@ -12,21 +12,29 @@
 //
 //  1. b* = the histogram bin holding the head's k-th best candidate (every
 //     workgroup reads the head's histogram);
-//  2. two radix rounds over the LOW pattern bits of the candidates inside b*
-//     (the top 10 bits, then the other 9): each workgroup adds its segment's
-//     LDS histogram of the round's digit to the head's round histogram in
-//     device memory, and after the rendezvous every workgroup picks the same
-//     digit from it. This gives the exact pattern T of the k-th best
-//     candidate and how many candidates equal to T are taken (the lowest
-//     indices), whatever the ties;
-//  3. each workgroup publishes its segment's counts above and equal to T and
-//     reads those of the earlier segments;
-//  4. it writes its kept indices and positions in ascending order from there
-//     and copies the kept K and V rows.
+//  2. each workgroup lists, in key order, the LOW pattern bits of its
+//     segment's candidates inside b* (tagged with the segment) in the
+//     segment's slot, with its count above b*; after the rendezvous every
+//     workgroup reads all of the head's slots (the headers and the first
+//     entries in one round trip) and radix-selects in LDS the exact pattern T
+//     of the k-th best candidate, how many candidates equal to T are taken
+//     (the lowest indices), and how many kept candidates the earlier
+//     segments hold;
+//  3. where a list does not fit its slot (heavy ties), the workgroups instead
+//     run two radix rounds over the candidates inside b* (the top 10 LOW
+//     bits, then the other 9): each adds its segment's LDS histogram of the
+//     round's digit to the head's round histogram in device memory and,
+//     after a rendezvous, picks the same digit from it; then each publishes
+//     its segment's counts above and equal to T and reads the earlier ones.
+//     Exact whatever the ties;
+//  4. each workgroup writes its kept indices and positions in ascending order
+//     from there (the rows it keeps were requested into the caches while it
+//     resolved) and copies the kept K and V rows.
 //
-// Device memory holds only the histograms and the per-segment counts, none of
-// which grows with S. Every decision a barrier depends on is the same for all
-// threads of the workgroup, and the same for every workgroup of a head.
+// Device memory holds only the histograms, the per-segment lists (bounded
+// by the number of segments, not by S) and counts. Every decision a barrier
+// depends on is the same for all threads of the workgroup, and the same for
+// every workgroup of a head.
 
 #pragma once
 
@@ -39,6 +47,12 @@ constexpr int kFselThreads = 8 * kWave;  // the scan workgroup
 constexpr int kFselWaves = kFselThreads / kWave;
 constexpr int kFselMaxKpt = kFselMaxSegKeys / kFselThreads;  // segment keys per thread
 constexpr int kFselCopyUnroll = 4;       // row pieces in flight per thread
+constexpr int kFSlotHdr = 4;             // a list's header words: entries, count above b*, -, -
+constexpr int kFSlotCap = kFSlotWords - kFSlotHdr;
+constexpr int kFSpecWords = 64;          // words of each list read in the first round trip
+constexpr int kFSpecEntries = kFSpecWords - kFSlotHdr;
+constexpr int kFselCand = 8192;          // listed entries of a head gathered in LDS
+constexpr int kFselSpecPerThread = kMaxSplit * kFSpecWords / kFselThreads;  // 16
 static_assert(kFselThreads == kFselThreadsHost && kFselMaxKpt * kFselThreads == kFselMaxSegKeys, "host sizes");
 static_assert(kFselR1Bins == 1024 && kFselR2Bins == (int)KeyFmt<false>::R2_BINS, "radix round widths");
 
@@ -51,9 +65,12 @@ __device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
 
 // LDS of the selection (inside the scan's ring, idle by then).
 struct FselLds {
-  uint32_t hist[kFselR1Bins];      // this segment's radix round histogram
-  uint32_t ghist[kFselR1Bins];     // the head's, as read back
+  uint32_t hist[kFselR1Bins];      // a radix round's histogram (this segment's, or of the lists)
+  uint32_t ghist[kFselR1Bins];     // the head's, as read back (or the lists' second round)
   int32_t kept[kFselMaxSegKeys];   // kept keys of the segment, in order
+  uint32_t cand[kFselCand];        // the head's listed entries
+  uint32_t n_in[kMaxSplit];        // listed entries per segment
+  uint32_t off[kMaxSplit];         // their exclusive prefix
   uint32_t scratch[4 * kFselWaves];
   uint32_t pick[2];
   uint32_t bstar;
@@ -110,6 +127,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
   uint32_t* cnt = a.segcnt + (int64_t)head * kMaxSplit * 2;
 
   uint32_t thr = 0xFFFFFFFFu, need_eq = 0u, gt_before = 0u, eq_before = 0u;
+  uint32_t touched[kFselMaxKpt][4] = {};  // words of prefetched rows (consumed at the end)
   if (ranked) {
     // ---- 1. b*: thread t owns bins 4095-8t .. 4088-8t (descending)
     const uint32_t* hist = a.hist + (int64_t)head * kHistBins;
@@ -138,44 +156,181 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
     const uint32_t bstar = m.bstar;
     uint32_t rem = m.pick[1];
     __syncthreads();
-    // ---- 2. radix rounds over the LOW bits inside b*
-    const uint32_t top = bstar << KF::LOW;
-    fsel_round<kFselR1Bins>(bits, cand, ~KF::LOW_MASK, top, [](uint32_t u) { return (u >> KF::R2) & 1023u; },
-                            g1, m, [&]() { meet(1); });
-    if (t < kWave) pick_digit_wave<kFselR1Bins>(m.ghist, rem, m.pick);
-    __syncthreads();
-    const uint32_t d1 = m.pick[0];
-    rem = m.pick[1];
-    __syncthreads();
-    const uint32_t pre2 = top | (d1 << KF::R2);
-    fsel_round<kFselR2Bins>(bits, cand, ~(KF::R2_BINS - 1u), pre2, [](uint32_t u) { return u & (KF::R2_BINS - 1u); },
-                            g2, m, [&]() { meet(2); });
-    if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
-    __syncthreads();
-    thr = pre2 | m.pick[0];
-    need_eq = m.pick[1];
-    __syncthreads();
-    // ---- 3. this segment's counts above and equal to T; the earlier ones'
-    uint32_t q2[2] = {0u, 0u};
+    // ---- 2. this segment's list of its candidates inside b*
+    uint32_t above = 0, nin = 0;
 #pragma unroll
     for (int e = 0; e < kFselMaxKpt; ++e) {
-      q2[0] += cand[e] && bits[e] > thr;
-      q2[1] += cand[e] && bits[e] == thr;
+      if (cand[e]) {
+        const uint32_t bin = bits[e] >> KF::LOW;
+        above += bin > bstar;
+        nin += bin == bstar;
+      }
     }
-    block_sums<kFselWaves, 2>(q2, m.scratch);
+    uint32_t tot_in;
+    uint32_t pos = block_exclusive_scan<kFselWaves>(nin, m.scratch, tot_in);
+    uint32_t ab[1] = {above};
+    block_sums<kFselWaves, 1>(ab, m.scratch);
+    uint32_t* slot = a.fslots + ((int64_t)head * kMaxSplit + split) * kFSlotWords;
+    const uint32_t tag = (uint32_t)split << KF::LOW;
+#pragma unroll
+    for (int e = 0; e < kFselMaxKpt; ++e) {
+      if (cand[e] && (bits[e] >> KF::LOW) == bstar) {
+        if (pos < (uint32_t)kFSlotCap) st_coh(slot + kFSlotHdr + pos, tag | (bits[e] & KF::LOW_MASK));
+        ++pos;
+      }
+    }
     if (t == 0) {
-      st_coh(cnt + 2 * split, q2[0]);
-      st_coh(cnt + 2 * split + 1, q2[1]);
+      st_coh(slot, tot_in);
+      st_coh(slot + 1, ab[0]);
     }
-    meet(3);
-    uint32_t b2[2] = {0u, 0u};
-    for (int s = t; s < split; s += kFselThreads) {
-      b2[0] += ld_coh(cnt + 2 * s);
-      b2[1] += ld_coh(cnt + 2 * s + 1);
+    meet(1);
+    // every list of the head: thread t holds words 8*(t%8)..+7 of lists
+    // t/8, t/8 + 64 (the headers and the first entries in one round trip)
+    const int n_split = a.n_split;
+    const uint32_t* slots = a.fslots + (int64_t)head * kMaxSplit * kFSlotWords;
+    uint32_t w[kFselSpecPerThread];
+    const int sw = (t & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < kFselSpecPerThread; ++i) {
+      const int sl = (t >> 3) + (i >> 3) * (kFselThreads / 8);
+      w[i] = sl < n_split ? ld_coh(slots + (int64_t)sl * kFSlotWords + sw + (i & 7)) : 0u;
     }
-    block_sums<kFselWaves, 2>(b2, m.scratch);
-    gt_before = b2[0];
-    eq_before = b2[1];
+    uint32_t sums[3] = {0u, 0u, 0u};  // above b* in all lists, in the earlier ones; lists that overflow
+    if (sw == 0) {
+#pragma unroll
+      for (int g = 0; g < kFselSpecPerThread / 8; ++g) {
+        const int sl = (t >> 3) + g * (kFselThreads / 8);
+        if (sl < n_split) {
+          m.n_in[sl] = w[8 * g];
+          sums[0] += w[8 * g + 1];
+          sums[1] += sl < split ? w[8 * g + 1] : 0u;
+          sums[2] += w[8 * g] > (uint32_t)kFSlotCap;
+        }
+      }
+    }
+    block_sums<kFselWaves, 3>(sums, m.scratch);  // (its barrier also publishes n_in)
+    uint32_t listed;
+    const uint32_t o = block_exclusive_scan<kFselWaves>(t < n_split ? m.n_in[t] : 0u, m.scratch, listed);
+    if (t < n_split) m.off[t] = o;
+    if (sums[2] == 0u && listed <= (uint32_t)kFselCand) {
+      __syncthreads();
+      // gather the entries: the speculative words, then the rest of the long
+      // lists (the eight threads of a list read eight entries at a time)
+#pragma unroll
+      for (int i = 0; i < kFselSpecPerThread; ++i) {
+        const int sl = (t >> 3) + (i >> 3) * (kFselThreads / 8);
+        const int e = sw + (i & 7) - kFSlotHdr;
+        if (sl < n_split && e >= 0 && (uint32_t)e < m.n_in[sl]) m.cand[m.off[sl] + e] = w[i];
+      }
+#pragma unroll
+      for (int g = 0; g < kFselSpecPerThread / 8; ++g) {
+        const int sl = (t >> 3) + g * (kFselThreads / 8);
+        const uint32_t nl = sl < n_split ? m.n_in[sl] : 0u;
+        for (uint32_t e0 = kFSpecEntries + (t & 7); e0 < nl; e0 += 64) {
+          uint32_t tmp[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t e = e0 + 8 * q;
+            tmp[q] = e < nl ? ld_coh(slots + (int64_t)sl * kFSlotWords + kFSlotHdr + e) : 0u;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t e = e0 + 8 * q;
+            if (e < nl) m.cand[m.off[sl] + e] = tmp[q];
+          }
+        }
+      }
+      for (int i = t; i < kFselR1Bins; i += kFselThreads) {
+        m.hist[i] = 0u;
+        m.ghist[i] = 0u;
+      }
+      // the rows this segment keeps for sure or may keep, into the caches
+      // while the threshold is resolved (consumed at the end)
+#pragma unroll
+      for (int e = 0; e < kFselMaxKpt; ++e) {
+        const int64_t j = k0 + e;
+        const bool want = e < kpt && j < seg1 && (!cand[e] || (bits[e] >> KF::LOW) >= bstar);
+        if (want) {
+          const uint16_t* kr = sa.k + j * sa.k_tok + (int64_t)head * sa.k_head;
+          const uint16_t* vr = sa.v + j * sa.v_tok + (int64_t)head * sa.v_head;
+          touched[e][0] = *reinterpret_cast<const uint32_t*>(kr);
+          touched[e][1] = *reinterpret_cast<const uint32_t*>(vr);
+          if (sa.d > 64) {
+            touched[e][2] = *reinterpret_cast<const uint32_t*>(kr + 64);
+            touched[e][3] = *reinterpret_cast<const uint32_t*>(vr + 64);
+          }
+        }
+      }
+      __syncthreads();
+      // radix over the LOW bits: the top 10, then the other 9
+      for (uint32_t x = t; x < listed; x += kFselThreads) atomicAdd(&m.hist[(m.cand[x] >> KF::R2) & 1023u], 1u);
+      __syncthreads();
+      if (t < kWave) pick_digit_wave<kFselR1Bins>(m.hist, rem, m.pick);
+      __syncthreads();
+      const uint32_t d1 = m.pick[0];
+      rem = m.pick[1];
+      for (uint32_t x = t; x < listed; x += kFselThreads) {
+        const uint32_t u = m.cand[x];
+        if (((u >> KF::R2) & 1023u) == d1) atomicAdd(&m.ghist[u & (KF::R2_BINS - 1u)], 1u);
+      }
+      __syncthreads();
+      if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
+      __syncthreads();
+      const uint32_t low = (d1 << KF::R2) | m.pick[0];
+      need_eq = m.pick[1];
+      thr = (bstar << KF::LOW) | low;
+      // listed candidates of the earlier segments
+      uint32_t gq[2] = {0u, 0u};
+      for (uint32_t x = t; x < listed; x += kFselThreads) {
+        const uint32_t u = m.cand[x];
+        if ((int)(u >> KF::LOW) < split) {
+          gq[0] += (u & KF::LOW_MASK) > low;
+          gq[1] += (u & KF::LOW_MASK) == low;
+        }
+      }
+      block_sums<kFselWaves, 2>(gq, m.scratch);
+      gt_before = sums[1] + gq[0];
+      eq_before = gq[1];
+    } else {
+      // ---- 3. a list overflowed: radix rounds over the device-memory histograms
+      __syncthreads();
+      const uint32_t top = bstar << KF::LOW;
+      fsel_round<kFselR1Bins>(bits, cand, ~KF::LOW_MASK, top, [](uint32_t u) { return (u >> KF::R2) & 1023u; },
+                              g1, m, [&]() { meet(2); });
+      if (t < kWave) pick_digit_wave<kFselR1Bins>(m.ghist, rem, m.pick);
+      __syncthreads();
+      const uint32_t d1 = m.pick[0];
+      rem = m.pick[1];
+      __syncthreads();
+      const uint32_t pre2 = top | (d1 << KF::R2);
+      fsel_round<kFselR2Bins>(bits, cand, ~(KF::R2_BINS - 1u), pre2,
+                              [](uint32_t u) { return u & (KF::R2_BINS - 1u); }, g2, m, [&]() { meet(3); });
+      if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
+      __syncthreads();
+      thr = pre2 | m.pick[0];
+      need_eq = m.pick[1];
+      __syncthreads();
+      uint32_t q2[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < kFselMaxKpt; ++e) {
+        q2[0] += cand[e] && bits[e] > thr;
+        q2[1] += cand[e] && bits[e] == thr;
+      }
+      block_sums<kFselWaves, 2>(q2, m.scratch);
+      if (t == 0) {
+        st_coh(cnt + 2 * split, q2[0]);
+        st_coh(cnt + 2 * split + 1, q2[1]);
+      }
+      meet(4);
+      uint32_t b2[2] = {0u, 0u};
+      for (int s = t; s < split; s += kFselThreads) {
+        b2[0] += ld_coh(cnt + 2 * s);
+        b2[1] += ld_coh(cnt + 2 * s + 1);
+      }
+      block_sums<kFselWaves, 2>(b2, m.scratch);
+      gt_before = b2[0];
+      eq_before = b2[1];
+    }
   }
 
   // ---- 4. kept indices and positions of this segment, then the row copy
@@ -250,6 +405,10 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       if (rr < n) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4*>(dst + rr * sa.d));
     }
   }
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" : : "v"(touched[e][q]));
 }
 
 }  // namespace

@@ -446,9 +446,10 @@ def test_fused_select_workspace_does_not_grow_with_s():
     sizes = {s: kvc.kvc_workspace_size(base_desc(s=s, flags=FSEL)) for s in (16384, 65536, 131072)}
     assert len(set(sizes.values())) == 1, sizes
     plain = {s: kvc.kvc_workspace_size(base_desc(s=s)) for s in (16384, 65536, 131072)}
-    assert plain[131072] > plain[16384]  # the unflagged one grows by 4 * hkv * s + bookkeeping
-    assert sizes[65536] < plain[65536] - 4 * 8 * 65536
-    # it also holds no per-key bookkeeping: the same for a shorter or longer prompt at 4K
+    # the unflagged one grows by the score vector and about a byte per key and head
+    assert plain[131072] - plain[65536] >= (4 + 1) * 8 * 65536
+    assert sizes[65536] < plain[65536] and sizes[131072] < plain[131072] // 2
+    # no per-key state at all: the same for a 4K prompt
     assert kvc.kvc_workspace_size(base_desc(s=4096, flags=FSEL)) == sizes[16384]
 
 
