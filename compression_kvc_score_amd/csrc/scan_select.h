@@ -49,10 +49,10 @@ constexpr int kFselMaxKpt = kFselMaxSegKeys / kFselThreads;  // segment keys per
 constexpr int kFselCopyUnroll = 4;       // row pieces in flight per thread
 constexpr int kFSlotHdr = 4;             // a list's header words: entries, count above b*, -, -
 constexpr int kFSlotCap = kFSlotWords - kFSlotHdr;
-constexpr int kFSpecWords = 64;          // words of each list read in the first round trip
-constexpr int kFSpecEntries = kFSpecWords - kFSlotHdr;
 constexpr int kFselCand = 8192;          // listed entries of a head gathered in LDS
-constexpr int kFselSpecPerThread = kMaxSplit * kFSpecWords / kFselThreads;  // 16
+constexpr int kFselSpecPerThread = 16;   // list words per thread read in the first round trip
+static_assert(kFselSpecPerThread * kFselThreads == kMaxSplit * 64 && kFselSpecPerThread * kFselThreads == 32 * kFSlotWords,
+              "the first round trip covers 64 words of 128 lists, or 32 whole lists");
 static_assert(kFselThreads == kFselThreadsHost && kFselMaxKpt * kFselThreads == kFselMaxSegKeys, "host sizes");
 static_assert(kFselR1Bins == 1024 && kFselR2Bins == (int)KeyFmt<false>::R2_BINS, "radix round widths");
 
@@ -184,28 +184,32 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       st_coh(slot + 1, ab[0]);
     }
     meet(1);
-    // every list of the head: thread t holds words 8*(t%8)..+7 of lists
-    // t/8, t/8 + 64 (the headers and the first entries in one round trip)
+    // every list of the head, the first spw words of each in one round trip
+    // (whole lists for up to 32 segments): word i*512 + t of the lists laid
+    // end to end is this thread's w[i]
     const int n_split = a.n_split;
     const uint32_t* slots = a.fslots + (int64_t)head * kMaxSplit * kFSlotWords;
+    const int lg = n_split <= 32 ? 8 : (n_split <= 64 ? 7 : 6);
+    const int spw = 1 << lg;
     uint32_t w[kFselSpecPerThread];
-    const int sw = (t & 7) * 8;
 #pragma unroll
     for (int i = 0; i < kFselSpecPerThread; ++i) {
-      const int sl = (t >> 3) + (i >> 3) * (kFselThreads / 8);
-      w[i] = sl < n_split ? ld_coh(slots + (int64_t)sl * kFSlotWords + sw + (i & 7)) : 0u;
+      const int L = i * kFselThreads + t;
+      const int sl = L >> lg;
+      w[i] = sl < n_split ? ld_coh(slots + (int64_t)sl * kFSlotWords + (L & (spw - 1))) : 0u;
     }
     uint32_t sums[3] = {0u, 0u, 0u};  // above b* in all lists, in the earlier ones; lists that overflow
-    if (sw == 0) {
 #pragma unroll
-      for (int g = 0; g < kFselSpecPerThread / 8; ++g) {
-        const int sl = (t >> 3) + g * (kFselThreads / 8);
-        if (sl < n_split) {
-          m.n_in[sl] = w[8 * g];
-          sums[0] += w[8 * g + 1];
-          sums[1] += sl < split ? w[8 * g + 1] : 0u;
-          sums[2] += w[8 * g] > (uint32_t)kFSlotCap;
-        }
+    for (int i = 0; i < kFselSpecPerThread; ++i) {
+      const int L = i * kFselThreads + t;
+      const int sl = L >> lg, wd = L & (spw - 1);
+      if (sl < n_split && wd == 0) {
+        m.n_in[sl] = w[i];
+        sums[2] += w[i] > (uint32_t)kFSlotCap;
+      }
+      if (sl < n_split && wd == 1) {
+        sums[0] += w[i];
+        sums[1] += sl < split ? w[i] : 0u;
       }
     }
     block_sums<kFselWaves, 3>(sums, m.scratch);  // (its barrier also publishes n_in)
@@ -218,15 +222,18 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       // lists (the eight threads of a list read eight entries at a time)
 #pragma unroll
       for (int i = 0; i < kFselSpecPerThread; ++i) {
-        const int sl = (t >> 3) + (i >> 3) * (kFselThreads / 8);
-        const int e = sw + (i & 7) - kFSlotHdr;
+        const int L = i * kFselThreads + t;
+        const int sl = L >> lg;
+        const int e = (L & (spw - 1)) - kFSlotHdr;
         if (sl < n_split && e >= 0 && (uint32_t)e < m.n_in[sl]) m.cand[m.off[sl] + e] = w[i];
       }
+      // (more than 64 lists: the eight threads t/8 of a list read the rest of
+      // it eight entries at a time)
 #pragma unroll
-      for (int g = 0; g < kFselSpecPerThread / 8; ++g) {
+      for (int g = 0; g < kMaxSplit / (kFselThreads / 8); ++g) {
         const int sl = (t >> 3) + g * (kFselThreads / 8);
         const uint32_t nl = sl < n_split ? m.n_in[sl] : 0u;
-        for (uint32_t e0 = kFSpecEntries + (t & 7); e0 < nl; e0 += 64) {
+        for (uint32_t e0 = (uint32_t)(spw - kFSlotHdr) + (t & 7); e0 < nl; e0 += 64) {
           uint32_t tmp[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {

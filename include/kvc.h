@@ -146,8 +146,12 @@ typedef struct kvc_layer_desc {
  * launch in which every workgroup keeps its key segment's scores on chip, so
  * the workspace does not grow with s at all and no fp32 score vector goes to
  * device memory unless scores_out asks for it (TideKV, Fig. 3 caption:
- * scoring temporaries O(W * b_s + K_l), independent of S). Outputs equal the
- * unflagged call's bit for bit. Needs softmax scores, pool 1, G * W <= 128,
+ * scoring temporaries O(W * b_s + K_l), independent of S). The retained
+ * indices, rows and positions equal, bit for bit, what kvc_select_topk and
+ * kvc_gather_retained make of the same call's scores; a workgroup scans one
+ * KV head, so pass 1's partials merge in another order than the unflagged
+ * path's when hkv is even and m, Z and the scores then differ from its in the
+ * last bits. Needs softmax scores, pool 1, G * W <= 128,
  * at most 4096 keys of a head per workgroup (s up to about 128K with 8 KV
  * heads on a 256-CU device) and a device whose compute units hold the whole
  * launch at once; else KVC_ERR_UNSUPPORTED. The staged entry points and the
