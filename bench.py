@@ -363,6 +363,57 @@ def layer_sweep(kvc, torch, dev, name, sp, stream):
     return out
 
 
+def fused_select_detail(kvc, torch, dev, sp, stream, reps=6, calls=32):
+    """KVC_FLAG_FUSED_SELECT (scans, selection and gather in one launch, the
+    scores kept on chip, a workspace that does not grow with S) against the
+    default whole-layer call on the same resident layers: four layers per
+    shape, `reps` interleaved rounds of `calls` calls each way, HIP events
+    around each round; medians."""
+    from synth import get_config, layer_inputs
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    out = {}
+    for name, over in (("llama8b_16k", {}), ("llama8b_64k", {}), ("llama8b_64k", {"s": 131072})):
+        cfg = get_config(name).with_(**over) if over else get_config(name)
+        layers = []
+        for l in range(4):
+            x = layer_inputs(cfg, l)
+            layers.append((dev_bf16(x.q), dev_bf16(x.k), dev_bf16(x.v), np.full(cfg.hkv, cfg.budget, dtype=np.int32)))
+            del x
+        runs = {}
+        for flag in (0, kvc.KVC_FLAG_FUSED_SELECT):
+            q0, k0, v0, _ = layers[0]
+            desc = kvc.desc_for(q0, k0, v0, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, flags=flag)
+            ws = kvc.alloc_workspace(desc, dev)
+            runs[flag] = ([kvc.PreparedLayer(desc, q, k, v, b, kvc.alloc_outputs(desc, b, dev, with_intermediates=False), ws)
+                           for q, k, v, b in layers], [], int(ws.numel()))
+        for r in range(reps):
+            for flag in ((0, kvc.KVC_FLAG_FUSED_SELECT) if r % 2 == 0 else (kvc.KVC_FLAG_FUSED_SELECT, 0)):
+                preps, ts, _ = runs[flag]
+                for i in range(4):
+                    preps[i].kvc_compress_layer(sp)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(calls):
+                    preps[i % 4].kvc_compress_layer(sp)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+        key = f"{name}_s{cfg.s}"
+        out[key] = {"s": cfg.s, "w": cfg.w, "default_us": round(float(np.median(runs[0][1])), 2),
+                    "fused_select_us": round(float(np.median(runs[kvc.KVC_FLAG_FUSED_SELECT][1])), 2),
+                    "default_workspace_bytes": runs[0][2],
+                    "fused_select_workspace_bytes": runs[kvc.KVC_FLAG_FUSED_SELECT][2]}
+        log(f"fused select {key}: {out[key]['fused_select_us']:.1f} us per layer (workspace "
+            f"{out[key]['fused_select_workspace_bytes']} B) against {out[key]['default_us']:.1f} us "
+            f"(workspace {out[key]['default_workspace_bytes']} B)")
+        del runs, layers
+        torch.cuda.empty_cache()
+    return out
+
+
 def layer_major_prefill(kvc, torch, dev, s=65536, chunk=2048, w=32, budget=4096):
     """The compressor inside the schedule it serves: a random-weight
     Llama-3.1-8B-shaped stack (32 layers) prefilled layer-major in chunks with
@@ -765,6 +816,7 @@ def main(argv=None):
     # keys, each against the one-shot layer-end compressor on the same tensors
     imm_detail = {name: immediate_eviction(kvc, torch, dev, name, max(4, K // 4), sp, stream)
                   for name in ("llama8b_16k_imm", "llama8b_64k_imm")}
+    fsel_detail = fused_select_detail(kvc, torch, dev, sp, stream) if args.configs else None
     configs_detail = other_configs(kvc, torch, dev, OTHER_CONFIGS, 20, sp, stream) if args.configs else None
     if args.configs:
         configs_detail[SWEEP_CONFIG] = layer_sweep(kvc, torch, dev, SWEEP_CONFIG, sp, stream)
@@ -803,6 +855,7 @@ def main(argv=None):
         "score_modes": mode_detail,
         "other_configs": configs_detail,
         "immediate_eviction": imm_detail,
+        "fused_select": fsel_detail,
         "layer_major_prefill": prefill_detail,
         "sweep": {
             "entry_point": "kvc_compress_layers", "layers_in_flight": kvc.SWEEP_STREAMS,
