@@ -157,6 +157,7 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
     return fail(KVC_ERR_INVALID_ARG, "pos_offset=%lld: positions must fit in int32", (long long)d->pos_offset);
   if ((d->flags & ~KVC_FLAG_FUSED_SELECT) != 0)
     return fail(KVC_ERR_INVALID_ARG, "flags=0x%x has unknown bits", (unsigned)d->flags);
+  if (d->reserved != 0) return fail(KVC_ERR_INVALID_ARG, "reserved=%d must be 0", d->reserved);
 
   const int64_t strides[6] = {d->q_tok_stride, d->q_head_stride, d->k_tok_stride,
                               d->k_head_stride, d->v_tok_stride, d->v_head_stride};

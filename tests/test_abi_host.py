@@ -460,6 +460,11 @@ def test_fused_select_flag_is_validated():
         assert lib.kvc_workspace_size(ctypes.byref(d)) == 0
         with pytest.raises(kvc.KvcError):
             kvc.kvc_plan_layer(d)
+    d = base_desc(s=65536)
+    d.reserved = 1  # kept for later use: must be 0
+    assert lib.kvc_workspace_size(ctypes.byref(d)) == 0
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_plan_layer(d)
     for kw in (dict(pool=7), dict(score_mode=kvc.KVC_SCORE_LOGIT), dict(w=64),  # 256 rows per KV head
                dict(s=1 << 20)):  # 32768 keys of a head per workgroup
         d = base_desc(**dict(dict(s=65536, flags=FSEL), **kw))
