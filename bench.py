@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA peak
 METRIC = "prefix tokens evicted/sec per layer (all KV heads) + % HBM roofline, S=64K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-KERNEL_SOURCES = ["score_kernels.hip", "stream_kernels.hip", "select_kernels.hip", "gather_kernel.hip", "kvc_internal.h"]
+KERNEL_SOURCES = ["score_kernels.hip", "stream_kernels.hip", "select_kernels.hip", "gather_kernel.hip", "kvc_internal.h",
+                  "scan_select.h", "select_common.h", "wave_ops.h"]
 
 
 def log(msg):
