@@ -611,10 +611,13 @@ def main(argv=None):
                 "mfma_frac": round(2 * mfma_flops(cfg) / (scan_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     if args.roofline_only:
-        scan_ms = roofline_loop(args.steps, args.warmup)
+        # at least ~14 ms of warm calls, so that the device has left its idle
+        # clocks before the timed calls (the full run's loop follows the
+        # whole-layer calls)
+        scan_ms = roofline_loop(args.steps, max(args.warmup, 200))
         roof = roofline_object(scan_ms)
         log(f"roofline loop: {scan_ms * 1e3:.2f} us per kvc_score_layer call, {roof['frac'] * 100:.1f}% of the HBM peak")
-        print(json.dumps({"metric": METRIC, "mode": "roofline-only", "steps": args.steps, "warmup": args.warmup,
+        print(json.dumps({"metric": METRIC, "mode": "roofline-only", "steps": args.steps, "warmup": max(args.warmup, 200),
                           "config": {"workload": cfg.name, "s": cfg.s, "fused_scans": int(plan.fused_scans)},
                           "roofline": roof, "kernel_hash": kernel_source_hash()}), flush=True)
         return 0
