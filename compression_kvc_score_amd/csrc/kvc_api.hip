@@ -93,6 +93,16 @@ bool fused_scans_enabled() {
   return v;
 }
 
+// Head groups that run on one XCD meet through its L2 after their first
+// rendezvous (KVC_XCD_LOCAL=0: always through device-coherent memory).
+bool xcd_local_enabled() {
+  static const bool v = [] {
+    const char* e = std::getenv("KVC_XCD_LOCAL");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+
 // Compute units of the current device (0 if it cannot be read), cached per device.
 int device_cus() {
   static int cache[64] = {0};
@@ -350,7 +360,7 @@ int check_lds(const Layer& L) {
   }
   const size_t scan = L.stream_hg ? std::max({pass1_stream_lds_bytes(L), pass2_stream_lds_bytes(L), fused_lds_bytes(L)})
                                   : std::max(pass1_lds_bytes(L), pass2_lds_bytes(L));
-  const size_t need = std::max(scan, select_lds_bytes(n_chunks(L), n_subs(L)) + 16384);
+  const size_t need = std::max(scan + kFusedStaticLds, select_lds_bytes(n_chunks(L), n_subs(L)) + 16384);
   if (need > (size_t)lim)
     return fail(KVC_ERR_UNSUPPORTED, "kernels need %zu bytes of LDS, device allows %d", need, lim);
   return KVC_OK;
@@ -568,6 +578,7 @@ int enqueue_scans(const Layer& L, const void* q_win, const void* k, float* m, fl
     a.scores = sc;
     a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
     a.epoch = next_epoch();
+    a.xcd_local = xcd_local_enabled() ? 1 : 0;
     const hipError_t e = launch_stream_fused(L, a, SelectArgs{}, st);
     if (e != hipSuccess) return hip_fail(e, "fused scan launch");
     return KVC_OK;
@@ -603,6 +614,7 @@ int enqueue_layer(const Layer& L, const void* q_win, const void* k, const void* 
     a.scores = scores_out;
     a.sync = reinterpret_cast<uint64_t*>(wsb + lay.sync);
     a.epoch = next_epoch();
+    a.xcd_local = xcd_local_enabled() ? 1 : 0;
     a.fsel_kpt = (int)((stream_keys_per_wg(L) + kFselThreadsHost - 1) / kFselThreadsHost);
     a.ghist = reinterpret_cast<uint32_t*>(wsb + lay.ghist);
     a.segcnt = reinterpret_cast<uint32_t*>(wsb + lay.segcnt);

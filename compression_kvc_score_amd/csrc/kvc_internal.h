@@ -72,8 +72,14 @@ struct ScoreArgs {
   uint32_t* ghist;
   uint32_t* segcnt;
   uint32_t* fslots;  // per (head, segment) a list of the candidates inside b*: [hkv][kMaxSplit][kFSlotWords]
+  // 1: head groups whose workgroups all run on one XCD may meet through that
+  // XCD's L2 after their first (device-coherent) rendezvous
+  int xcd_local;
 };
 
+// static LDS the scan kernels declare beside their dynamic LDS (a rendezvous
+// result word), rounded up
+constexpr size_t kFusedStaticLds = 16;
 constexpr int kMaxFusedWgs = 1024;  // workgroups of one fused scan launch (one per compute unit)
 constexpr int kFusedFlagSets = 7;   // partials, normalisers, scores + histogram, lists, two radix rounds, counts
 constexpr size_t kSyncBytes = (size_t)kFusedFlagSets * kMaxFusedWgs * sizeof(uint64_t);

@@ -56,11 +56,16 @@ static_assert(kFselSpecPerThread * kFselThreads == kMaxSplit * 64 && kFselSpecPe
 static_assert(kFselThreads == kFselThreadsHost && kFselMaxKpt * kFselThreads == kFselMaxSegKeys, "host sizes");
 static_assert(kFselR1Bins == 1024 && kFselR2Bins == (int)KeyFmt<false>::R2_BINS, "radix round widths");
 
+typedef uint32_t fsel_u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t ld_coh(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A store the head's other workgroups read with ld_coh: device coherent, or
+// kept in the XCD's L2 when all of them run on that XCD (`local`).
+__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v, bool local) {
+  if (local) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS of the selection (inside the scan's ring, idle by then).
@@ -84,18 +89,18 @@ __device__ __forceinline__ void fsel_round(const uint32_t (&bits)[kFselMaxKpt], 
                                            uint32_t mask, uint32_t prefix, Digit digit, uint32_t* g, FselLds& m,
                                            Meet meet) {
   for (int i = threadIdx.x; i < NB; i += kFselThreads) m.hist[i] = 0u;
-  __syncthreads();
+  wg_sync<true>();
 #pragma unroll
   for (int e = 0; e < kFselMaxKpt; ++e)
     if (cand[e] && (bits[e] & mask) == prefix) atomicAdd(&m.hist[digit(bits[e])], 1u);
-  __syncthreads();
+  wg_sync<true>();
   for (int i = threadIdx.x; i < NB; i += kFselThreads) {
     const uint32_t c = m.hist[i];
     if (c != 0u) atomicAdd(g + i, c);  // device scope: performed where every XCD sees it
   }
   meet();
   for (int i = threadIdx.x; i < NB; i += kFselThreads) m.ghist[i] = ld_coh(g + i);
-  __syncthreads();
+  wg_sync<true>();
 }
 
 // Steps 1-4 for KV head `head`, segment [seg0, seg1) of split `split`; the
@@ -104,7 +109,7 @@ __device__ __forceinline__ void fsel_round(const uint32_t (&bits)[kFselMaxKpt], 
 template <typename Meet>
 __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs& sa, int head, int split,
                                             int64_t seg0, int64_t seg1, const float* sc, unsigned char* smem,
-                                            Meet meet) {
+                                            bool local, Meet meet) {
   using KF = KeyFmt<false>;
   FselLds& m = *reinterpret_cast<FselLds*>(smem);
   const int t = threadIdx.x;
@@ -132,14 +137,26 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
     // ---- 1. b*: thread t owns bins 4095-8t .. 4088-8t (descending)
     const uint32_t* hist = a.hist + (int64_t)head * kHistBins;
     uint32_t c[8], loc = 0;
+    {
+      // bins 4088-8t .. 4095-8t as two 16-byte device-coherent loads
+      fsel_u32x4 lo, hi;
+      const uint32_t* b0 = hist + kHistBins - 8 - 8 * t;
+      asm volatile(
+          "global_load_dwordx4 %0, %2, off sc1\n\tglobal_load_dwordx4 %1, %3, off sc1\n\ts_waitcnt vmcnt(0)"
+          : "=&v"(lo), "=&v"(hi)
+          : "v"(b0), "v"(b0 + 4)
+          : "memory");
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      c[q] = ld_coh(hist + kHistBins - 1 - 8 * t - q);
-      loc += c[q];
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hi[3 - q];  // bin 4095-8t-q
+        c[4 + q] = lo[3 - q];
+      }
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) loc += c[q];
     if (t == 0) m.bstar = 0u;
     uint32_t total;
-    uint32_t before = block_exclusive_scan<kFselWaves>(loc, m.scratch, total);
+    uint32_t before = block_exclusive_scan<kFselWaves, true>(loc, m.scratch, total);
     if (before < h.k_sel && h.k_sel <= before + loc) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -150,12 +167,12 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
         before += c[q];
       }
     }
-    __syncthreads();
+    wg_sync<true>();
     // (a histogram that missed keys cannot hold the k-th: b* would stay 0 and
     // the rounds below pick from what is there; pass 2 counts every candidate)
     const uint32_t bstar = m.bstar;
     uint32_t rem = m.pick[1];
-    __syncthreads();
+    wg_sync<true>();
     // ---- 2. this segment's list of its candidates inside b*
     uint32_t above = 0, nin = 0;
 #pragma unroll
@@ -167,21 +184,21 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       }
     }
     uint32_t tot_in;
-    uint32_t pos = block_exclusive_scan<kFselWaves>(nin, m.scratch, tot_in);
+    uint32_t pos = block_exclusive_scan<kFselWaves, true>(nin, m.scratch, tot_in);
     uint32_t ab[1] = {above};
-    block_sums<kFselWaves, 1>(ab, m.scratch);
+    block_sums<kFselWaves, 1, true>(ab, m.scratch);
     uint32_t* slot = a.fslots + ((int64_t)head * kMaxSplit + split) * kFSlotWords;
     const uint32_t tag = (uint32_t)split << KF::LOW;
 #pragma unroll
     for (int e = 0; e < kFselMaxKpt; ++e) {
       if (cand[e] && (bits[e] >> KF::LOW) == bstar) {
-        if (pos < (uint32_t)kFSlotCap) st_coh(slot + kFSlotHdr + pos, tag | (bits[e] & KF::LOW_MASK));
+        if (pos < (uint32_t)kFSlotCap) st_coh(slot + kFSlotHdr + pos, tag | (bits[e] & KF::LOW_MASK), local);
         ++pos;
       }
     }
     if (t == 0) {
-      st_coh(slot, tot_in);
-      st_coh(slot + 1, ab[0]);
+      st_coh(slot, tot_in, local);
+      st_coh(slot + 1, ab[0], local);
     }
     meet(1);
     // every list of the head, the first spw words of each in one round trip
@@ -212,12 +229,12 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
         sums[1] += sl < split ? w[i] : 0u;
       }
     }
-    block_sums<kFselWaves, 3>(sums, m.scratch);  // (its barrier also publishes n_in)
+    block_sums<kFselWaves, 3, true>(sums, m.scratch);  // (its barrier also publishes n_in)
     uint32_t listed;
-    const uint32_t o = block_exclusive_scan<kFselWaves>(t < n_split ? m.n_in[t] : 0u, m.scratch, listed);
+    const uint32_t o = block_exclusive_scan<kFselWaves, true>(t < n_split ? m.n_in[t] : 0u, m.scratch, listed);
     if (t < n_split) m.off[t] = o;
     if (sums[2] == 0u && listed <= (uint32_t)kFselCand) {
-      __syncthreads();
+      wg_sync<true>();
       // gather the entries: the speculative words, then the rest of the long
       // lists (the eight threads of a list read eight entries at a time)
 #pragma unroll
@@ -268,21 +285,21 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
           }
         }
       }
-      __syncthreads();
+      wg_sync<true>();
       // radix over the LOW bits: the top 10, then the other 9
       for (uint32_t x = t; x < listed; x += kFselThreads) atomicAdd(&m.hist[(m.cand[x] >> KF::R2) & 1023u], 1u);
-      __syncthreads();
+      wg_sync<true>();
       if (t < kWave) pick_digit_wave<kFselR1Bins>(m.hist, rem, m.pick);
-      __syncthreads();
+      wg_sync<true>();
       const uint32_t d1 = m.pick[0];
       rem = m.pick[1];
       for (uint32_t x = t; x < listed; x += kFselThreads) {
         const uint32_t u = m.cand[x];
         if (((u >> KF::R2) & 1023u) == d1) atomicAdd(&m.ghist[u & (KF::R2_BINS - 1u)], 1u);
       }
-      __syncthreads();
+      wg_sync<true>();
       if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
-      __syncthreads();
+      wg_sync<true>();
       const uint32_t low = (d1 << KF::R2) | m.pick[0];
       need_eq = m.pick[1];
       thr = (bstar << KF::LOW) | low;
@@ -295,38 +312,38 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
           gq[1] += (u & KF::LOW_MASK) == low;
         }
       }
-      block_sums<kFselWaves, 2>(gq, m.scratch);
+      block_sums<kFselWaves, 2, true>(gq, m.scratch);
       gt_before = sums[1] + gq[0];
       eq_before = gq[1];
     } else {
       // ---- 3. a list overflowed: radix rounds over the device-memory histograms
-      __syncthreads();
+      wg_sync<true>();
       const uint32_t top = bstar << KF::LOW;
       fsel_round<kFselR1Bins>(bits, cand, ~KF::LOW_MASK, top, [](uint32_t u) { return (u >> KF::R2) & 1023u; },
                               g1, m, [&]() { meet(2); });
       if (t < kWave) pick_digit_wave<kFselR1Bins>(m.ghist, rem, m.pick);
-      __syncthreads();
+      wg_sync<true>();
       const uint32_t d1 = m.pick[0];
       rem = m.pick[1];
-      __syncthreads();
+      wg_sync<true>();
       const uint32_t pre2 = top | (d1 << KF::R2);
       fsel_round<kFselR2Bins>(bits, cand, ~(KF::R2_BINS - 1u), pre2,
                               [](uint32_t u) { return u & (KF::R2_BINS - 1u); }, g2, m, [&]() { meet(3); });
       if (t < kWave) pick_digit_wave<kFselR2Bins>(m.ghist, rem, m.pick);
-      __syncthreads();
+      wg_sync<true>();
       thr = pre2 | m.pick[0];
       need_eq = m.pick[1];
-      __syncthreads();
+      wg_sync<true>();
       uint32_t q2[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < kFselMaxKpt; ++e) {
         q2[0] += cand[e] && bits[e] > thr;
         q2[1] += cand[e] && bits[e] == thr;
       }
-      block_sums<kFselWaves, 2>(q2, m.scratch);
+      block_sums<kFselWaves, 2, true>(q2, m.scratch);
       if (t == 0) {
-        st_coh(cnt + 2 * split, q2[0]);
-        st_coh(cnt + 2 * split + 1, q2[1]);
+        st_coh(cnt + 2 * split, q2[0], local);
+        st_coh(cnt + 2 * split + 1, q2[1], local);
       }
       meet(4);
       uint32_t b2[2] = {0u, 0u};
@@ -334,7 +351,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
         b2[0] += ld_coh(cnt + 2 * s);
         b2[1] += ld_coh(cnt + 2 * s + 1);
       }
-      block_sums<kFselWaves, 2>(b2, m.scratch);
+      block_sums<kFselWaves, 2, true>(b2, m.scratch);
       gt_before = b2[0];
       eq_before = b2[1];
     }
@@ -361,7 +378,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
     n_eq += flag[e] == 2u;
   }
   uint32_t total;
-  const uint32_t before = block_exclusive_scan<kFselWaves>((n_kept << 16) | n_eq, m.scratch, total);
+  const uint32_t before = block_exclusive_scan<kFselWaves, true>((n_kept << 16) | n_eq, m.scratch, total);
   uint32_t eq_seen = before & 0xFFFFu;
   uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
   const int64_t row0 = sa.heads.offset[head];
@@ -386,7 +403,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
   const uint32_t eq_all = total & 0xFFFFu;
   int64_t n = (int64_t)(total >> 16) + (eq_all < quota ? eq_all : quota);
   if (n > h.budget - (int64_t)first) n = h.budget - (int64_t)first;  // never past this head's rows
-  __syncthreads();
+  wg_sync<true>();
   // a row is d/8 16-byte pieces of K then d/8 of V; consecutive threads take
   // consecutive pieces, so each row is one contiguous read and write
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

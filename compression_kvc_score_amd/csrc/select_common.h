@@ -35,14 +35,22 @@ struct KeyFmt {
   __device__ static __forceinline__ uint32_t bin(uint32_t key) { return (key >> LOW) & (kHistBins - 1); }
 };
 
+// Workgroup barrier. LDS_ONLY: it orders LDS accesses alone and leaves this
+// thread's global loads and stores in flight (__syncthreads waits for them).
+template <bool LDS_ONLY>
+__device__ __forceinline__ void wg_sync() {
+  if constexpr (LDS_ONLY) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __syncthreads();
+}
+
 // Exclusive prefix sum over a workgroup of NW wavefronts, one value per
 // thread; also returns the total. Uses `scratch` (NW entries) in LDS.
-template <int NW>
+template <int NW, bool LDS_ONLY = false>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_inclusive_sum(v);
   if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
   uint32_t before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -51,13 +59,13 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t
     all += t;
   }
   total = all;
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
   return before + incl - v;
 }
 
 // Sums over a workgroup of NW wavefronts of two values per thread (every
 // thread gets both). Uses `scratch` (2 * NW entries) in LDS.
-template <int NW>
+template <int NW, bool LDS_ONLY = false>
 __device__ void block_sum2(uint32_t& x, uint32_t& y, uint32_t* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t ix = wave_inclusive_sum(x), iy = wave_inclusive_sum(y);
@@ -65,7 +73,7 @@ __device__ void block_sum2(uint32_t& x, uint32_t& y, uint32_t* scratch) {
     scratch[wave] = ix;
     scratch[NW + wave] = iy;
   }
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
   x = 0u;
   y = 0u;
 #pragma unroll
@@ -73,12 +81,12 @@ __device__ void block_sum2(uint32_t& x, uint32_t& y, uint32_t* scratch) {
     x += scratch[w];
     y += scratch[NW + w];
   }
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
 }
 
 // Sums over a workgroup of NW wavefronts of N values per thread (every
 // thread gets all N). Uses `scratch` (N * NW entries) in LDS.
-template <int NW, int N>
+template <int NW, int N, bool LDS_ONLY = false>
 __device__ void block_sums(uint32_t (&x)[N], uint32_t* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -86,14 +94,14 @@ __device__ void block_sums(uint32_t (&x)[N], uint32_t* scratch) {
     const uint32_t inc = wave_inclusive_sum(x[i]);
     if (lane == 63) scratch[i * NW + wave] = inc;
   }
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     x[i] = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) x[i] += scratch[i * NW + w];
   }
-  __syncthreads();
+  wg_sync<LDS_ONLY>();
 }
 
 struct HeadGeom {

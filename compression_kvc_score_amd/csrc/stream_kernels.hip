@@ -312,6 +312,30 @@ __device__ __forceinline__ void key_read(const unsigned char* slot, int hl, int 
   }
 }
 
+// As key_read, and one float read from `extra` in the same round trip (its
+// value, like the fragments, is defined only after the wait).
+template <int D, int HG>
+__device__ __forceinline__ void key_read_x(const unsigned char* slot, int hl, int kt, int half, int l32,
+                                           u32x4_t (&kf)[D / 16], const float* extra, float& xv) {
+  using R = Ring<D, HG>;
+  static_assert(D == 128, "the two-row-group pass 2 runs with D = 128");
+  const int r = kt * kKeyTile + l32;
+  uint32_t ad[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    ad[st] = lds_addr(slot + (r * R::R16 + ((hl * R::CPH + 2 * st + half) ^ (r & (R::XS - 1)))) * 16);
+  asm volatile(
+      "ds_read_b32 %8, %17\n\t"
+      "ds_read_b128 %0, %9\n\tds_read_b128 %1, %10\n\tds_read_b128 %2, %11\n\tds_read_b128 %3, %12\n\t"
+      "ds_read_b128 %4, %13\n\tds_read_b128 %5, %14\n\tds_read_b128 %6, %15\n\tds_read_b128 %7, %16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]), "=&v"(kf[6]),
+        "=&v"(kf[7]), "=&v"(xv)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(lds_addr(extra))
+      : "memory");
+}
+
 template <int D>
 __device__ __forceinline__ void key_settle(u32x4_t (&raw)[D / 16], uint4 (&kf)[D / 16]) {
   lds_settle(raw);
@@ -1139,6 +1163,19 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
       key_read<D, HG>(smem, ro.hl, ro.kt, half, l32, kf);
       slot_contract<D, NRTW, false>(accA, qr, kf, Ms{});
     }
+    // With two row groups each wavefront finishes half of its key tile's
+    // keys: it keeps its own partial of the previous slot in a register and
+    // reads the other group's with this slot's key fragments, so the sum
+    // costs no LDS round trip of its own and both groups share the stores.
+    float own_prev = 0.f;
+    auto other_at = [&](int m) {
+      return psum + ((((m & 1) * HG + ro.hl) * R::KT + ro.kt) * R::RS + (R::RS - 1 - ro.rg)) * kKeyTile + l32;
+    };
+    auto finalize = [&](int m, float own, float other) {
+      const int key = rg.tok(m) + ro.kt * kKeyTile + l32;
+      // own + other is v[0] + v[1] for either group (addition commutes)
+      if (half == 0 && (l32 >> 4) == ro.rg && key < a.s) emit_score(a, out, lh, with_hist, key, own + other, seg_sc, seg0);
+    };
     auto step = [&](int n, f32x16_t (&cur)[NRTW], f32x16_t (&nxt)[NRTW]) {
       const int kbase = rg.tok(n) + ro.kt * kKeyTile;
       const int key = kbase + l32;
@@ -1147,13 +1184,20 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
       const bool more = n + 1 < rg.nst;
       if (more) ring_advance<D, HG>(a, h0, rg, n + 1, wave, lane, off, smem);
       else if constexpr (R::RS > 1) lds_barrier();  // the other row groups' partial sums of slot n-1
-      key_read<D, HG>(smem + ((more ? n + 1 : n) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, kf);
+      float other = 0.f;
+      if constexpr (R::RS > 1)  // (for n = 0 the read lands in the idle half of psum and is unused)
+        key_read_x<D, HG>(smem + ((more ? n + 1 : n) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, kf,
+                          other_at(n - 1), other);
+      else
+        key_read<D, HG>(smem + ((more ? n + 1 : n) % kRingSlots) * kSlotBytes, ro.hl, ro.kt, half, l32, kf);
       const float sum = kbase + kKeyTile > first_hidden
                             ? pass2_slot<D, NRTW, R::RS, true>(a, cur, nxt, qr, kf, breg, qpos, ro.rg, key, half, Ms{})
                             : pass2_slot<D, NRTW, R::RS, false>(a, cur, nxt, qr, kf, breg, qpos, ro.rg, key, half, Ms{});
       if constexpr (R::RS > 1) {
+        static_assert(R::RS == 2, "two row groups");
         if (half == 0) lds_write_f32(psum_at(n, ro.rg), sum);
-        if (n > 0) finish(n - 1);
+        if (n > 0) finalize(n - 1, own_prev, other);
+        own_prev = sum;
       } else {
         if (half == 0 && key < a.s) emit_score(a, out, lh, with_hist, key, sum, seg_sc, seg0);
       }
@@ -1161,6 +1205,14 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
     for (int n = 0; n < rg.nst; n += 2) {
       step(n, accA, accB);
       if (n + 1 < rg.nst) step(n + 1, accB, accA);
+    }
+    if constexpr (R::RS > 1) {
+      if (rg.nst > 0) {
+        lds_barrier();
+        float other[1] = {lds_read_f32(other_at(rg.nst - 1))};
+        lds_settle(other);
+        finalize(rg.nst - 1, own_prev, other[0]);
+      }
     }
   } else {
   for (int n = 0; n < rg.nst; ++n) {
@@ -1185,7 +1237,7 @@ __device__ __forceinline__ void pass2_main(const ScoreArgs& a, const WgCtx<D, HG
     }
   }
   }
-  if constexpr (R::RS > 1) {
+  if constexpr (R::RS > 1 && !SLOT_PIPE) {
     lds_barrier();
     if (rg.nst > 0) finish(rg.nst - 1);
   }
@@ -1256,35 +1308,73 @@ __global__ void __launch_bounds__(8 * kWave) pass2_stream_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// Publish flag `flag` once this workgroup's device-coherent stores are
-// acknowledged (vmcnt) and every thread has issued its own (barrier).
-__device__ __forceinline__ void group_arrive(const ScoreArgs& a, uint64_t* flag) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The XCD (accelerator die, with its own L2) this wavefront runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xFu;
 }
 
-// Wait until the n_split flags from `flags` hold the epoch: wavefront 0 polls
+// Whether this workgroup runs on the XCD its head group is meant for: the
+// hardware deals workgroups to the eight XCDs in turn (workgroup b to XCD
+// b % 8), xcd_remap gives every XCD a contiguous range of the work, and when
+// that range holds whole head groups, a group placed as dealt lies on one
+// XCD and shares its L2.
+__device__ __forceinline__ bool on_group_xcd(const ScoreArgs& a) {
+  return a.xcd_local && (gridDim.x & 7u) == 0 && (int)((gridDim.x >> 3) % (unsigned)a.n_split) == 0 &&
+         xcc_id() == (blockIdx.x & 7u);
+}
+
+// A store that the group's later device-coherent loads observe: device
+// coherent (through to memory) in general, or kept in the XCD's L2 when the
+// whole group runs on that XCD (a workgroup-scope store is written through
+// the CU's cache to the L2, where the other CUs' coherent loads find it).
+template <typename T>
+__device__ __forceinline__ void group_store(T* p, T v, bool local) {
+  if (local) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish `value` in flag `flag` once this workgroup's stores are
+// acknowledged (vmcnt) and every thread has issued its own (barrier).
+__device__ __forceinline__ void group_arrive(uint64_t* flag, uint64_t value, bool local) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (threadIdx.x == 0) group_store(flag, value, local);
+}
+
+// Wait until the n_split flags from `flags` hold the epoch (or, with
+// `either`, the epoch with its lowest bit flipped too): wavefront 0 polls
 // them (a lane per flag), the others wait at an LDS-only barrier, so ring
-// copies in flight stay in flight.
-__device__ __forceinline__ void group_wait(const ScoreArgs& a, const uint64_t* flags) {
+// copies in flight stay in flight. Returns whether every flag holds exactly
+// the epoch (the same answer in every workgroup that reads the same flags).
+__device__ __forceinline__ bool group_wait(const ScoreArgs& a, const uint64_t* flags, bool either = false) {
+  __shared__ uint32_t s_exact;
   if (threadIdx.x < kWave) {
+    bool exact = true;
     for (uint32_t spins = 0; spins < kSpinLimit; ++spins) {
       bool ok = true;
-      for (int i = threadIdx.x; i < a.n_split; i += kWave)
-        ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+      exact = true;
+      for (int i = threadIdx.x; i < a.n_split; i += kWave) {
+        const uint64_t f = __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = ok && (f == a.epoch || (either && f == (a.epoch ^ 1u)));
+        exact = exact && f == a.epoch;
+      }
       if (__all(ok)) break;
       __builtin_amdgcn_s_sleep(2);
     }
+    if (threadIdx.x == 0) s_exact = 1u;
+    if (!exact) s_exact = 0u;  // (any lane; the value written is the same)
   }
   lds_barrier();
+  return s_exact != 0u;
 }
 
 // This workgroup's share of its head group's rows: the partials of every
 // split merged as the split combine merges them (eight strided runs, then
 // runs 1..7 into run 0), written as the normalisers (m in natural-log units).
 template <int NRT, int HG>
-__device__ __forceinline__ void group_merge(const ScoreArgs& a, int h0, int split, float2* red) {
+__device__ __forceinline__ void group_merge(const ScoreArgs& a, int h0, int split, float2* red, bool local) {
   constexpr int ROWS_PAD = NRT * kRowTile;
   constexpr int RPR = kWave;  // rows per round: eight threads per row
   const int total = HG * a.rows;
@@ -1316,8 +1406,8 @@ __device__ __forceinline__ void group_merge(const ScoreArgs& a, int h0, int spli
       for (int k = 1; k < 8; ++k) lse_merge(m, z, red[k * RPR + rl].x, red[k * RPR + rl].y, a.c);
       const int hh = r / a.w, i = r % a.w;
       const int64_t o = (int64_t)((h0 + h) * a.g + hh) * a.w + i;
-      __hip_atomic_store(a.m_out + o, m * a.scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.z_out + o, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      group_store(a.m_out + o, m * a.scale, local);
+      group_store(a.z_out + o, z, local);
     }
     __syncthreads();
   }
@@ -1367,11 +1457,14 @@ __global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a, Sele
   pass1_loops<D, NRT, HG>(a, c, rg1, off, smem, qr, qpos, mrun, zrun);
   pass1_finish<D, NRT, HG, true>(a, c, smem, mrun, zrun);
 
-  group_arrive(a, pub1 + c.split);
+  // The first rendezvous is device coherent; its flags also say whether each
+  // workgroup runs on its group's XCD. If all do, the group's later stores
+  // and flags stay in that XCD's L2.
+  group_arrive(pub1 + c.split, on_group_xcd(a) ? a.epoch : a.epoch ^ 1u, false);
   ring_fill<D, HG>(a, c.h0, rg2, c.wave, c.lane, off, smem);  // (the reduction above is done with the ring)
-  group_wait(a, pub1);
-  group_merge<NRT, HG>(a, c.h0, c.split, reinterpret_cast<float2*>(smem + kRingBytes));
-  group_arrive(a, pub2 + c.split);
+  const bool local = group_wait(a, pub1, true);
+  group_merge<NRT, HG>(a, c.h0, c.split, reinterpret_cast<float2*>(smem + kRingBytes), local);
+  group_arrive(pub2 + c.split, a.epoch, local);
   group_wait(a, pub2);
 
   // this thread's normaliser (one bias entry per thread), as pass 2 reads it
@@ -1395,13 +1488,13 @@ __global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a, Sele
     static_assert(sizeof(FselLds) <= kRingBytes, "the selection's LDS lives in the idle ring");
     const float* seg_sc = pass2_seg_scores<NRT, HG>(smem);
     uint64_t* pub3 = a.sync + 2 * kMaxFusedWgs + wg;
-    group_arrive(a, pub3 + c.split);
+    group_arrive(pub3 + c.split, a.epoch, local);
     group_wait(a, pub3);
     const int64_t seg0 = rg1.t0;
     const int64_t seg1 = min((int64_t)a.s, seg0 + (int64_t)a.blocks_per_wg * R::TOKS);
-    scan_select(a, sa, c.h0, c.split, seg0, seg1, seg_sc, smem, [&](int n) {
+    scan_select(a, sa, c.h0, c.split, seg0, seg1, seg_sc, smem, local, [&](int n) {
       uint64_t* pub = a.sync + (2 + n) * kMaxFusedWgs + wg;
-      group_arrive(a, pub + c.split);
+      group_arrive(pub + c.split, a.epoch, local);
       group_wait(a, pub);
     });
   }

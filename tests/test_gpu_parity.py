@@ -692,3 +692,54 @@ def test_fused_select_offset_noalloc_and_sweep():
         np.testing.assert_array_equal(outs[i].idx.cpu().numpy(), want[i]["idx"], err_msg=f"sweep idx {i}")
         np.testing.assert_array_equal(from_dev_bits(outs[i].v_hat), want[i]["v_hat"], err_msg=f"sweep v_hat {i}")
         np.testing.assert_array_equal(outs[i].pos.cpu().numpy(), want[i]["pos"], err_msg=f"sweep pos {i}")
+
+
+_RENDEZVOUS_SCRIPT = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[1] + "/tests")
+import compression_kvc_score_amd as kvc
+from synth import get_config, layer_inputs
+from gpu_util import desc_from, host
+out_path = sys.argv[2]
+res = {}
+for name, s in (("llama8b_16k", None), ("llama8b_64k", None), ("llama8b_16k", 3000)):
+    cfg = get_config(name).with_(s=s) if s else get_config(name)
+    x = layer_inputs(cfg, 3)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+               for a in (x.q, x.k, x.v))
+    b = np.full(cfg.hkv, min(cfg.budget, cfg.s), dtype=np.int64)
+    for flags in (kvc.KVC_FLAG_FUSED_SELECT, 0):
+        d = desc_from(cfg, q, k, v, flags=flags)
+        ws = kvc.alloc_workspace(d)
+        out = kvc.alloc_outputs(d, b)
+        kvc.compress_layer(d, q, k, v, b, out, ws)
+        torch.cuda.synchronize()
+        for key, val in host(out).items():
+            res[f"{name}_{cfg.s}_{flags}_{key}"] = val
+np.savez(out_path, **res)
+"""
+
+
+def test_rendezvous_through_l2_or_memory_same_bits(tmp_path):
+    """Head groups whose workgroups all run on one XCD meet through its L2
+    after their first rendezvous; KVC_XCD_LOCAL=0 makes every rendezvous go
+    through device-coherent memory. The outputs (fused selection and the
+    default call, m, Z, scores, indices, rows, positions) are the same bits
+    either way. (The switch is read once per process: two child processes.)"""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    paths = {}
+    for local in ("1", "0"):
+        paths[local] = str(tmp_path / f"out_{local}.npz")
+        env = dict(os.environ, KVC_XCD_LOCAL=local)
+        say(f"rendezvous run with KVC_XCD_LOCAL={local}")
+        subprocess.run([sys.executable, "-c", _RENDEZVOUS_SCRIPT, root, paths[local]], env=env, check=True,
+                       timeout=240)
+    a, b = np.load(paths["1"]), np.load(paths["0"])
+    assert sorted(a.files) == sorted(b.files) and len(a.files) > 0
+    for key in a.files:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
