@@ -382,6 +382,17 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
   uint32_t eq_seen = before & 0xFFFFu;
   uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
   const int64_t row0 = sa.heads.offset[head];
+  // Positions looked up (pos_in) are all loaded before any store: with a
+  // load feeding each store the compiler waits for every outstanding memory
+  // operation (the prefetched rows included) once per kept key.
+  int32_t pos[kFselMaxKpt];
+#pragma unroll
+  for (int e = 0; e < kFselMaxKpt; ++e) pos[e] = (int32_t)(sa.pos_offset + k0 + e);
+  if (sa.pos_in != nullptr) {
+#pragma unroll
+    for (int e = 0; e < kFselMaxKpt; ++e)
+      if (flag[e] != 0u) pos[e] = sa.pos_in[head * sa.pos_in_head + (int32_t)(k0 + e)];
+  }
 #pragma unroll
   for (int e = 0; e < kFselMaxKpt; ++e) {
     bool keep = flag[e] == 1u;
@@ -394,7 +405,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       const int32_t j = (int32_t)(k0 + e);
       if (o < h.budget) {
         sa.idx_out[row0 + o] = j;
-        sa.pos_out[row0 + o] = sa.pos_in ? sa.pos_in[head * sa.pos_in_head + j] : (int32_t)(sa.pos_offset + j);
+        sa.pos_out[row0 + o] = pos[e];
       }
       m.kept[p] = j;
       ++p;

@@ -256,7 +256,7 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) sums[i] = 0u;
   }
-  block_sums<NW, 4>(sums, m.scratch);
+  block_sums<NW, 4, true>(sums, m.scratch);
   if (sums[2] >= 0x10000u) return kNeedRow;
   if (sums[2] != 0u) return kNeedLists;
   const uint32_t bstar = sums[3];
@@ -274,9 +274,9 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
         const int e = r * kWave + lane - kSlotHdr;
         if (e >= 0 && (uint32_t)e < n[g][i]) atomicAdd(&m.hist1[(v[g][i][r] >> KF::R2) & 1023u], 1u);
       }
-  __syncthreads();
+  wg_sync<true>();
   if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
-  __syncthreads();
+  wg_sync<true>();
   const uint32_t d1 = m.pick[0];
   rem = m.pick[1];
 #pragma unroll
@@ -289,9 +289,9 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
         if (e >= 0 && (uint32_t)e < n[g][i] && ((v[g][i][r] >> KF::R2) & 1023u) == d1)
           atomicAdd(&m.hist2[v[g][i][r] & (KF::R2_BINS - 1u)], 1u);
       }
-  __syncthreads();
+  wg_sync<true>();
   if (threadIdx.x < kWave) pick_digit_wave<KF::R2_BINS>(m.hist2, rem, m.pick);
-  __syncthreads();
+  wg_sync<true>();
   const uint32_t low = (d1 << KF::R2) | m.pick[0];
   need_eq = m.pick[1];
   thr = (bstar << KF::LOW) | low;
@@ -310,7 +310,7 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
           gq[1] += (x & KF::LOW_MASK) == low;
         }
       }
-  block_sums<NW, 2>(gq, m.scratch);
+  block_sums<NW, 2, true>(gq, m.scratch);
   gt_before = sums[1] + gq[0];
   eq_before = gq[1];
   return kResolved;
@@ -349,7 +349,7 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
       for (int r = 0; r < kSpecRounds; ++r)
         v[i][r] = c < nc ? slots[(int64_t)c * kSlotStride + r * kWave + lane] : 0u;
     }
-    if (c0 == 0) __syncthreads();  // s_count and the radix bins are cleared
+    if (c0 == 0) wg_sync<true>();  // s_count and the radix bins are cleared
     uint32_t n[kGroupChunks], tot = 0;
 #pragma unroll
     for (int i = 0; i < kGroupChunks; ++i) {
@@ -391,7 +391,7 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
     ab_all = 0u;
     ab_before = 0u;
   }
-  block_sum2<NW>(ab_all, ab_before, m.scratch);
+  block_sum2<NW, true>(ab_all, ab_before, m.scratch);
   if (s_flag != 0u) return false;
   on_bstar(s_bstar);
 
@@ -400,18 +400,18 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
   uint32_t rem = h.k_sel - ab_all;  // rank of the threshold inside the list
   for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads)
     atomicAdd(&m.hist1[(m.cbits[i] >> KF::R2) & 1023u], 1u);
-  __syncthreads();
+  wg_sync<true>();
   if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
-  __syncthreads();
+  wg_sync<true>();
   const uint32_t d1 = m.pick[0];
   rem = m.pick[1];
   for (uint32_t i = threadIdx.x; i < n_total; i += kCompactThreads) {
     const uint32_t e = m.cbits[i];
     if (((e >> KF::R2) & 1023u) == d1) atomicAdd(&m.hist2[e & (KF::R2_BINS - 1u)], 1u);
   }
-  __syncthreads();
+  wg_sync<true>();
   if (threadIdx.x < kWave) pick_digit_wave<KF::R2_BINS>(m.hist2, rem, m.pick);
-  __syncthreads();
+  wg_sync<true>();
   const uint32_t low = (d1 << KF::R2) | m.pick[0];
   need_eq = m.pick[1];
   thr = (s_bstar << KF::LOW) | low;
@@ -424,7 +424,7 @@ __device__ bool resolve_from_lists(const SelectArgs& a, const HeadGeom& h, int h
       q += (e & KF::LOW_MASK) == low;
     }
   }
-  block_sum2<NW>(g, q, m.scratch);
+  block_sum2<NW, true>(g, q, m.scratch);
   gt_before = ab_before + g;
   eq_before = q;
   return true;
@@ -442,18 +442,18 @@ __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int hea
   uint32_t prefix = 0u, mask = 0u, rem = h.k_sel;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += NT) m.hist1[i] = 0u;
-    __syncthreads();
+    wg_sync<true>();
     for (int64_t j = h.sink_end + threadIdx.x; j < h.rec_begin; j += NT) {
       const uint32_t u = KF::key(row[j]);
       if ((u & mask) == prefix) atomicAdd(&m.hist1[(u >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    wg_sync<true>();
     if (threadIdx.x < kWave) pick_digit_wave<256>(m.hist1, rem, m.pick);
-    __syncthreads();
+    wg_sync<true>();
     prefix |= m.pick[0] << shift;
     rem = m.pick[1];
     mask |= 255u << shift;
-    __syncthreads();
+    wg_sync<true>();
   }
   thr = prefix;
   need_eq = rem;
@@ -465,7 +465,7 @@ __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int hea
     g += u > thr;
     q += u == thr;
   }
-  block_sum2<NW>(g, q, m.scratch);
+  block_sum2<NW, true>(g, q, m.scratch);
   gt_before = g;
   eq_before = q;
 }
@@ -574,7 +574,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
   const uint32_t packed = (n_kept << 16) | n_eq;
   const uint32_t incl = wave_inclusive_sum(packed);
   if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
+  wg_sync<true>();  // (LDS only: the prefetched rows stay in flight)
   uint32_t before = incl - packed, total = 0;
 #pragma unroll
   for (int w = 0; w < kCWaves; ++w) {
@@ -586,6 +586,20 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
   uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
   const int64_t row0 = a.heads.offset[head];
   int32_t* out = a.idx_out + row0;
+  // Positions looked up (pos_in) are all loaded before any store: with a
+  // load feeding each store the compiler waits for every outstanding memory
+  // operation (the prefetched rows included) once per kept key.
+  int32_t pos[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int32_t j = (int32_t)(j0 + e);
+    pos[e] = (int32_t)(a.pos_offset + j);
+  }
+  if (GATHER && a.pos_in != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (flag[e] != 0u) pos[e] = a.pos_in[head * a.pos_in_head + (int32_t)(j0 + e)];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     bool keep = flag[e] == 1u;
@@ -598,8 +612,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
       const int32_t j = (int32_t)(j0 + e);
       if (o < h.budget && rep == 0) {
         out[o] = j;
-        if (GATHER)
-          a.pos_out[row0 + o] = a.pos_in ? a.pos_in[head * a.pos_in_head + j] : (int32_t)(a.pos_offset + j);
+        if (GATHER) a.pos_out[row0 + o] = pos[e];
       }
       if (GATHER) kept_keys[p] = j;
       ++p;
@@ -609,7 +622,8 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     const uint32_t eq_all = total & 0xFFFFu;
     int64_t n = (int64_t)(total >> 16) + (eq_all < quota ? eq_all : quota);
     if (n > h.budget - (int64_t)first) n = h.budget - (int64_t)first;  // never past this head's rows
-    __syncthreads();
+    // (LDS only: the index stores and the prefetched rows stay in flight)
+    wg_sync<true>();
     // a row is d/8 16-byte units of K then d/8 of V; consecutive threads take
     // consecutive units, so each row is one contiguous read and write
     const int cpr = a.d >> 3;
