@@ -382,17 +382,11 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
   uint32_t eq_seen = before & 0xFFFFu;
   uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
   const int64_t row0 = sa.heads.offset[head];
-  // Positions looked up (pos_in) are all loaded before any store: with a
-  // load feeding each store the compiler waits for every outstanding memory
-  // operation (the prefetched rows included) once per kept key.
-  int32_t pos[kFselMaxKpt];
-#pragma unroll
-  for (int e = 0; e < kFselMaxKpt; ++e) pos[e] = (int32_t)(sa.pos_offset + k0 + e);
-  if (sa.pos_in != nullptr) {
-#pragma unroll
-    for (int e = 0; e < kFselMaxKpt; ++e)
-      if (flag[e] != 0u) pos[e] = sa.pos_in[head * sa.pos_in_head + (int32_t)(k0 + e)];
-  }
+  // Index stores, and the positions when they follow from the index; looked
+  // up positions are written after the copy from the kept keys in LDS. (A
+  // load feeding these stores would make each of them wait for every earlier
+  // memory operation, the rows prefetched above among them.)
+  const bool lookup = sa.pos_in != nullptr;
 #pragma unroll
   for (int e = 0; e < kFselMaxKpt; ++e) {
     bool keep = flag[e] == 1u;
@@ -405,7 +399,7 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       const int32_t j = (int32_t)(k0 + e);
       if (o < h.budget) {
         sa.idx_out[row0 + o] = j;
-        sa.pos_out[row0 + o] = pos[e];
+        if (!lookup) sa.pos_out[row0 + o] = (int32_t)(sa.pos_offset + j);
       }
       m.kept[p] = j;
       ++p;
@@ -440,6 +434,9 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       if (rr < n) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4*>(dst + rr * sa.d));
     }
   }
+  if (lookup)
+    for (int64_t r = t; r < n; r += kFselThreads)
+      sa.pos_out[row0 + first + r] = sa.pos_in[head * sa.pos_in_head + m.kept[r]];
 #pragma unroll
   for (int e = 0; e < kFselMaxKpt; ++e)
 #pragma unroll

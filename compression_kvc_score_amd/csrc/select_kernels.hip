@@ -29,6 +29,8 @@
 // All counts are integers, so the output does not depend on the order in
 // which workgroups run.
 
+#include <type_traits>
+
 #include "kvc_internal.h"
 #include "select_common.h"
 #include "wave_ops.h"
@@ -590,20 +592,11 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
   uint32_t p = (before >> 16) + (eq_seen < quota ? eq_seen : quota);
   const int64_t row0 = a.heads.offset[head];
   int32_t* out = a.idx_out + row0;
-  // Positions looked up (pos_in) are all loaded before any store: with a
-  // load feeding each store the compiler waits for every outstanding memory
-  // operation (the prefetched rows included) once per kept key.
-  int32_t pos[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int32_t j = (int32_t)(j0 + e);
-    pos[e] = (int32_t)(a.pos_offset + j);
-  }
-  if (GATHER && a.pos_in != nullptr) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (flag[e] != 0u) pos[e] = a.pos_in[head * a.pos_in_head + (int32_t)(j0 + e)];
-  }
+  // Index stores, and the positions when they follow from the index; looked
+  // up positions are written after the copy from the kept keys in LDS. (A
+  // load feeding these stores would make each of them wait for every earlier
+  // memory operation, the rows prefetched during the resolve among them.)
+  const bool lookup = GATHER && a.pos_in != nullptr;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     bool keep = flag[e] == 1u;
@@ -616,7 +609,7 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
       const int32_t j = (int32_t)(j0 + e);
       if (o < h.budget && rep == 0) {
         out[o] = j;
-        if (GATHER) a.pos_out[row0 + o] = pos[e];
+        if (GATHER && !lookup) a.pos_out[row0 + o] = (int32_t)(a.pos_offset + j);
       }
       if (GATHER) kept_keys[p] = j;
       ++p;
@@ -654,6 +647,9 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
         if (rr < nr) __builtin_nontemporal_store(buf[i], reinterpret_cast<u32x4*>(dst + (int64_t)rr * a.d));
       }
     }
+    if (lookup && rep == 0)
+      for (int r = threadIdx.x; r < nr; r += kCompactThreads)
+        a.pos_out[row0 + first + r] = a.pos_in[head * a.pos_in_head + kept_keys[r]];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
