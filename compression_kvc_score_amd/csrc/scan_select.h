@@ -270,16 +270,22 @@ __device__ __forceinline__ void scan_select(const ScoreArgs& a, const SelectArgs
       }
       // the rows this segment keeps for sure or may keep, into the caches
       // while the threshold is resolved (consumed at the end)
+      // (every address first, outside the conditional loads, so that the
+      // layout fields are read once rather than inside each branch)
+      const uint16_t* kr0 = sa.k + k0 * sa.k_tok + (int64_t)head * sa.k_head;
+      const uint16_t* vr0 = sa.v + k0 * sa.v_tok + (int64_t)head * sa.v_head;
+      const int64_t ktk = sa.k_tok, vtk = sa.v_tok;
+      const bool wide = sa.d > 64;
 #pragma unroll
       for (int e = 0; e < kFselMaxKpt; ++e) {
         const int64_t j = k0 + e;
         const bool want = e < kpt && j < seg1 && (!cand[e] || (bits[e] >> KF::LOW) >= bstar);
         if (want) {
-          const uint16_t* kr = sa.k + j * sa.k_tok + (int64_t)head * sa.k_head;
-          const uint16_t* vr = sa.v + j * sa.v_tok + (int64_t)head * sa.v_head;
+          const uint16_t* kr = kr0 + e * ktk;
+          const uint16_t* vr = vr0 + e * vtk;
           touched[e][0] = *reinterpret_cast<const uint32_t*>(kr);
           touched[e][1] = *reinterpret_cast<const uint32_t*>(vr);
-          if (sa.d > 64) {
+          if (wide) {
             touched[e][2] = *reinterpret_cast<const uint32_t*>(kr + 64);
             touched[e][3] = *reinterpret_cast<const uint32_t*>(vr + 64);
           }

@@ -529,17 +529,22 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
           const int64_t j = j0 + e;
           want[e] = j < h.s && (!is_candidate(h, j) || KF::bin(vb[e]) >= bstar);
         }
+        // every address first, outside the conditional loads, so that the
+        // layout fields are read once rather than inside each branch
+        const uint16_t* kr0 = a.k + j0 * a.k_tok + (int64_t)head * a.k_head;
+        const uint16_t* vr0 = a.v + j0 * a.v_tok + (int64_t)head * a.v_head;
+        const int64_t kt = a.k_tok, vt = a.v_tok;
+        const bool wide = a.d > 64;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (want[e]) {
             // one word per 128-byte line; the words are only consumed at the
             // end of the kernel, so nothing waits for them before then
-            const int64_t j = j0 + e;
-            const uint16_t* kr = a.k + j * a.k_tok + (int64_t)head * a.k_head;
-            const uint16_t* vr = a.v + j * a.v_tok + (int64_t)head * a.v_head;
+            const uint16_t* kr = kr0 + e * kt;
+            const uint16_t* vr = vr0 + e * vt;
             touched[e][0] = *reinterpret_cast<const uint32_t*>(kr);
             touched[e][1] = *reinterpret_cast<const uint32_t*>(vr);
-            if (a.d > 64) {
+            if (wide) {
               touched[e][2] = *reinterpret_cast<const uint32_t*>(kr + 64);
               touched[e][3] = *reinterpret_cast<const uint32_t*>(vr + 64);
             }
