@@ -293,14 +293,13 @@ def other_configs(kvc, torch, dev, names, reps, sp, stream):
         us = [a.elapsed_time(b) * 1e3 for a, b in evs]
         med = float(np.median(us))
         alg = sum(algorithmic_bytes(cfg, rows).values())
-        rows_per_head = cfg.group * cfg.w
         plan = kvc.kvc_plan_layer(preps[0].desc)
         out[name] = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "pool": cfg.pool,
                      "us_per_layer": _pct(us), "reps": reps, "flushed": True,
                      "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
                      "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "scans": ("streaming (K staged in LDS)" + (", fused into one launch" if plan.fused_scans else "")
-                               if rows_per_head <= 128 else "per-head (K in VGPRs)")}
+                               if plan.scan == kvc.KVC_SCAN_STREAM else "per-head (K in VGPRs)")}
         log(f"{name}: median {med:.1f} us per layer (p10 {out[name]['us_per_layer']['p10']:.1f}, "
             f"p90 {out[name]['us_per_layer']['p90']:.1f}; {reps} calls after a cache flush), "
             f"{out[name]['hbm_frac'] * 100:.1f}% of the HBM peak, {out[name]['scans']} scans")

@@ -217,7 +217,7 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
       return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: %d query rows per KV head > %d with d=%d",
                   L.rows, 64 * rs, L.d);
     L.stream_hg = 1;
-  } else if (L.row_tiles <= 4 && stream_scans_enabled()) {
+  } else if ((L.row_tiles <= 4 || (L.d == 128 && L.row_tiles <= kStreamMaxRowTiles)) && stream_scans_enabled()) {
     if (L.hkv % 2 == 0 && stream_offsets_fit(L, 2)) L.stream_hg = 2;
     else if (stream_offsets_fit(L, 1)) L.stream_hg = 1;
   }

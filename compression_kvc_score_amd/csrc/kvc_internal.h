@@ -80,6 +80,12 @@ struct ScoreArgs {
 // static LDS the scan kernels declare beside their dynamic LDS (a rendezvous
 // result word), rounded up
 constexpr size_t kFusedStaticLds = 16;
+// Query-row tiles of a KV head the streaming scans take with D = 128: past
+// four, a wavefront keeps three tiles of queries in registers with one
+// accumulator (the Qwen-shaped 160 rows: 99 against 111 us per 64K layer for
+// the per-head scans); with four tiles per wavefront (seven or eight row
+// tiles) pass 1 spills and the per-head scans are faster.
+constexpr int kStreamMaxRowTiles = 6;
 constexpr int kMaxFusedWgs = 1024;  // workgroups of one fused scan launch (one per compute unit)
 constexpr int kFusedFlagSets = 7;   // partials, normalisers, scores + histogram, lists, two radix rounds, counts
 constexpr size_t kSyncBytes = (size_t)kFusedFlagSets * kMaxFusedWgs * sizeof(uint64_t);

@@ -1523,6 +1523,9 @@ const void* pass1_stream_fn(int nrt) {
     case 2: return reinterpret_cast<const void*>(&pass1_stream_kernel<D, 2, HG>);
     case 3: return reinterpret_cast<const void*>(&pass1_stream_kernel<D, 3, HG>);
     case 4: return reinterpret_cast<const void*>(&pass1_stream_kernel<D, 4, HG>);
+    // (five and six row tiles: D = 128 only, as the host takes them)
+    case 5: if constexpr (D == 128) return reinterpret_cast<const void*>(&pass1_stream_kernel<D, 5, HG>); else return nullptr;
+    case 6: if constexpr (D == 128) return reinterpret_cast<const void*>(&pass1_stream_kernel<D, 6, HG>); else return nullptr;
     default: return nullptr;
   }
 }
@@ -1534,6 +1537,9 @@ const void* pass2_stream_fn(int nrt) {
     case 2: return reinterpret_cast<const void*>(&pass2_stream_kernel<D, 2, HG>);
     case 3: return reinterpret_cast<const void*>(&pass2_stream_kernel<D, 3, HG>);
     case 4: return reinterpret_cast<const void*>(&pass2_stream_kernel<D, 4, HG>);
+    // (five and six row tiles: D = 128 only, as the host takes them)
+    case 5: if constexpr (D == 128) return reinterpret_cast<const void*>(&pass2_stream_kernel<D, 5, HG>); else return nullptr;
+    case 6: if constexpr (D == 128) return reinterpret_cast<const void*>(&pass2_stream_kernel<D, 6, HG>); else return nullptr;
     default: return nullptr;
   }
 }

@@ -392,8 +392,15 @@ def test_plan_histogram_counter_bound():
             if p.scan == kvc.KVC_SCAN_STREAM:
                 assert (p.hist_in_scan == 1) == (p.keys_per_wg < 65536), (s, hkv, hq, d, w)
             assert p.splits >= 1 and p.keys_per_wg >= 1
-    # per-head scans (G * W > 128) count in 32 bits; pooling ranks pooled
-    # values, which the selection's own histogram kernel counts
+    # up to 192 query rows per KV head (D 128) stream as well (the
+    # Qwen-shaped 160 rows: five row tiles); per-head scans (more rows)
+    # count in 32 bits; pooling ranks pooled values, which the selection's
+    # own histogram kernel counts
+    qwen = kvc.kvc_plan_layer(base_desc(s=65536, hq=40))
+    assert qwen.scan == kvc.KVC_SCAN_STREAM and qwen.fused_scans == 0
+    assert kvc.kvc_plan_layer(base_desc(s=65536, hq=48)).scan == kvc.KVC_SCAN_STREAM  # 192 rows
+    assert kvc.kvc_plan_layer(base_desc(s=65536, hq=56)).scan == kvc.KVC_SCAN_PER_HEAD  # 224 rows
+    assert kvc.kvc_plan_layer(base_desc(s=65536, hq=40, hkv=8, d=64)).scan == kvc.KVC_SCAN_PER_HEAD
     assert kvc.kvc_plan_layer(base_desc(s=1 << 20, w=64)).scan == kvc.KVC_SCAN_PER_HEAD
     assert kvc.kvc_plan_layer(base_desc(s=1 << 20, w=64)).hist_in_scan == 1
     assert kvc.kvc_plan_layer(base_desc(s=65536, pool=7)).hist_in_scan == 0

@@ -171,6 +171,12 @@ EDGE_CASES = {
                        None, dict(scale=0.05)),
     "hetero_budgets": (dict(s=6000, w=32, hq=40, hkv=8, d=128, n_sink=4, n_recent=32, n_heavy=60, budget=0,
                             hetero=True, total_budget=8 * 300), None, {}),
+    # streaming scans with three query tiles per wavefront: 176 rows (a
+    # ragged sixth row tile) and 192 rows
+    "stream_176_rows": (dict(s=3001, w=44, hq=8, hkv=2, d=128, n_sink=4, n_recent=44, n_heavy=15, budget=300),
+                        [300, 52], {}),
+    "stream_192_rows": (dict(s=2500, w=48, hq=4, hkv=1, d=128, n_sink=4, n_recent=48, n_heavy=12, budget=256),
+                        None, {}),
 }
 
 
@@ -183,6 +189,8 @@ def test_edge_shapes(name):
     desc = desc_from(cfg, q, k, v, **extra)
     b = np.asarray(budgets) if budgets is not None else budgets_for(cfg, x)
     say(f"edge {name} s={cfg.s} w={cfg.w} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} budgets={list(b)[:4]}")
+    if name.startswith("stream_") or name == "hetero_budgets":
+        assert kvc.kvc_plan_layer(desc).scan == kvc.KVC_SCAN_STREAM
     st = run_staged(desc, q, k, v, b)
     check_layer(x, st, b, scale=extra.get("scale"))
     fu = run_fused(desc, q, k, v, b)
