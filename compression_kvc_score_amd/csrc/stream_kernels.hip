@@ -1418,7 +1418,7 @@ __global__ void __launch_bounds__(8 * kWave) scan_fused_kernel(ScoreArgs a, Sele
   using R = Ring<D, HG>;
   constexpr int NRTW = (NRT + R::RS - 1) / R::RS;
   constexpr int ROWS_PAD = NRT * kRowTile;
-  static_assert(NRT % R::RS == 0 && NRTW <= 2, "fused scans use the slot pipeline");
+  static_assert(NRTW <= 3, "at most three query-row tiles per wavefront");
   extern __shared__ __align__(16) unsigned char smem[];
   const WgCtx<D, HG> c = wg_ctx<D, NRT, HG>(a);
   const Range rg1 = wg_range(a, c.split, R::TOKS, false);
@@ -1507,6 +1507,9 @@ const void* fused_fn(int nrt) {
     case 1: if constexpr (1 % RS == 0) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 1, HG>); else return nullptr;
     case 2: return reinterpret_cast<const void*>(&scan_fused_kernel<D, 2, HG>);
     case 4: if constexpr ((4 + RS - 1) / RS <= 2) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 4, HG>); else return nullptr;
+    // (five and six row tiles: D = 128 with two row groups, as the host takes them)
+    case 5: if constexpr (D == 128 && RS == 2) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 5, HG>); else return nullptr;
+    case 6: if constexpr (D == 128 && RS == 2) return reinterpret_cast<const void*>(&scan_fused_kernel<D, 6, HG>); else return nullptr;
     default: return nullptr;
   }
 }

@@ -396,8 +396,7 @@ def test_plan_histogram_counter_bound():
     # Qwen-shaped 160 rows: five row tiles); per-head scans (more rows)
     # count in 32 bits; pooling ranks pooled values, which the selection's
     # own histogram kernel counts
-    qwen = kvc.kvc_plan_layer(base_desc(s=65536, hq=40))
-    assert qwen.scan == kvc.KVC_SCAN_STREAM and qwen.fused_scans == 0
+    assert kvc.kvc_plan_layer(base_desc(s=65536, hq=40)).scan == kvc.KVC_SCAN_STREAM
     assert kvc.kvc_plan_layer(base_desc(s=65536, hq=48)).scan == kvc.KVC_SCAN_STREAM  # 192 rows
     assert kvc.kvc_plan_layer(base_desc(s=65536, hq=56)).scan == kvc.KVC_SCAN_PER_HEAD  # 224 rows
     assert kvc.kvc_plan_layer(base_desc(s=65536, hq=40, hkv=8, d=64)).scan == kvc.KVC_SCAN_PER_HEAD

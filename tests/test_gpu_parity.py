@@ -190,7 +190,10 @@ def test_edge_shapes(name):
     b = np.asarray(budgets) if budgets is not None else budgets_for(cfg, x)
     say(f"edge {name} s={cfg.s} w={cfg.w} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} budgets={list(b)[:4]}")
     if name.startswith("stream_") or name == "hetero_budgets":
-        assert kvc.kvc_plan_layer(desc).scan == kvc.KVC_SCAN_STREAM
+        plan = kvc.kvc_plan_layer(desc)
+        assert plan.scan == kvc.KVC_SCAN_STREAM
+        if name.startswith("stream_"):
+            assert plan.fused_scans == 1  # the whole-layer call below runs both scans in one launch
     st = run_staged(desc, q, k, v, b)
     check_layer(x, st, b, scale=extra.get("scale"))
     fu = run_fused(desc, q, k, v, b)
@@ -402,7 +405,8 @@ def test_deterministic_repeat():
         np.testing.assert_array_equal(a1[key], a2[key], err_msg=key)
 
 
-@pytest.mark.parametrize("name,s", [("tiny", None), ("llama8b_16k", 8192), ("llama8b_64k", None)])
+@pytest.mark.parametrize("name,s", [("tiny", None), ("llama8b_16k", 8192), ("llama8b_64k", None),
+                                    ("qwen14b_hetero_64k", 8192)])
 def test_fused_scans_need_no_workspace_init(name, s):
     """Where the scans run as one launch (pass 1, split merge, pass 2 with
     waits between workgroups), the outputs equal the staged calls' bit for
