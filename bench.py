@@ -293,13 +293,11 @@ def other_configs(kvc, torch, dev, names, reps, sp, stream):
         us = [a.elapsed_time(b) * 1e3 for a, b in evs]
         med = float(np.median(us))
         alg = sum(algorithmic_bytes(cfg, rows).values())
-        plan = kvc.kvc_plan_layer(preps[0].desc)
         out[name] = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "pool": cfg.pool,
                      "us_per_layer": _pct(us), "reps": reps, "flushed": True,
                      "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
                      "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "scans": ("streaming (K staged in LDS)" + (", fused into one launch" if plan.fused_scans else "")
-                               if plan.scan == kvc.KVC_SCAN_STREAM else "per-head (K in VGPRs)")}
+                     "scans": _scan_label(kvc, preps[0].desc)}
         log(f"{name}: median {med:.1f} us per layer (p10 {out[name]['us_per_layer']['p10']:.1f}, "
             f"p90 {out[name]['us_per_layer']['p90']:.1f}; {reps} calls after a cache flush), "
             f"{out[name]['hbm_frac'] * 100:.1f}% of the HBM peak, {out[name]['scans']} scans")
@@ -307,6 +305,14 @@ def other_configs(kvc, torch, dev, names, reps, sp, stream):
         torch.cuda.empty_cache()
     del flush
     return out
+
+
+def _scan_label(kvc, desc):
+    """How the library runs a layer's scans, from its plan."""
+    plan = kvc.kvc_plan_layer(desc)
+    if plan.scan != kvc.KVC_SCAN_STREAM:
+        return "per-head (K in VGPRs)"
+    return "streaming (K staged in LDS)" + (", fused into one launch" if plan.fused_scans else "")
 
 
 def layer_sweep(kvc, torch, dev, name, sp, stream):
@@ -354,7 +360,7 @@ def layer_sweep(kvc, torch, dev, name, sp, stream):
            "retained_arena_bytes": arena, "us_per_layer": _pct(us),
            "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
            "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "scans": "per-head (K in VGPRs)" if cfg.group * cfg.w > 128 else "streaming (K staged in LDS)"}
+           "scans": _scan_label(kvc, preps[0].desc)}
     log(f"{name} sweep over {cfg.layers} layers: median {med:.1f} us per layer (p10 {out['us_per_layer']['p10']:.1f}, "
         f"p90 {out['us_per_layer']['p90']:.1f}), retained arena {arena / 2**20:.0f} MiB, "
         f"{out['hbm_frac'] * 100:.1f}% of the HBM peak")
