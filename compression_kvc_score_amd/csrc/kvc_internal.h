@@ -213,7 +213,8 @@ inline int scan_waves(const Layer& L) {
   return 1;
 }
 
-// Streaming scans (G*W <= 128): head-group workgroups with K staged in LDS.
+// Streaming scans (G*W <= 128, or 192 at D = 128): head-group workgroups
+// with K staged in LDS.
 int stream_tokens(int d, int hg);                  // tokens per ring slot of the streaming scans
 int stream_row_groups(int d, int hg);              // row groups sharing a key tile (RS)
 bool stream_offsets_fit(const Layer& L, int hg);  // a slot's copy offsets fit in 32 bits

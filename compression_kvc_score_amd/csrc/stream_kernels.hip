@@ -1,5 +1,6 @@
 // Streaming form of the two scans (TideKV, Fig. 3 caption) for query-row
-// counts G*W <= 128: used whenever its register budget allows.
+// counts G*W <= 128, and up to 192 at D = 128 (three row tiles per
+// wavefront): used whenever its register budget allows.
 //
 // A workgroup of 8 wavefronts owns HG KV heads (a head pair when Hkv is even)
 // and a contiguous token range. K flows through a ring of kRingSlots LDS

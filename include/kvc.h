@@ -183,7 +183,7 @@ size_t kvc_workspace_size(const kvc_layer_desc* desc);
 
 /* Scan designs reported by kvc_plan_layer. */
 typedef enum kvc_scan_kind {
-  KVC_SCAN_STREAM = 1,    /* head-group workgroups, K streamed through LDS rings (G * W <= 128) */
+  KVC_SCAN_STREAM = 1,    /* head-group workgroups, K streamed through LDS rings (G * W <= 128; 192 at D = 128) */
   KVC_SCAN_PER_HEAD = 2,  /* one KV head per workgroup, K tiles in registers (G * W <= 256) */
   KVC_SCAN_LOGIT = 3      /* the one-pass raw inner-product scan of the non-softmax score modes */
 } kvc_scan_kind;
