@@ -212,6 +212,18 @@ def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
 
     imm_us, imm_wall = timed(lambda: imm.kvc_compress_chunked(sp))
     del_us, _ = timed(lambda: delayed.kvc_compress_layer(sp))
+    # the same boundaries with the fused-selection flag: each evicting
+    # boundary is one launch (scans, selection and gather)
+    fdesc = kvc.desc_for(q, k, v, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool,
+                         flags=kvc.KVC_FLAG_FUSED_SELECT)
+    try:
+        fws = torch.empty(kvc.kvc_chunked_workspace_size(fdesc, cfg.chunk, cfg.budget), dtype=torch.uint8, device=dev)
+        fimm = kvc.PreparedChunked(fdesc, cfg.chunk, qwd, k, v, cfg.budget, torch.empty_like(k_out),
+                                   torch.empty_like(v_out), torch.empty_like(pos), fws)
+        fsel_us, _ = timed(lambda: fimm.kvc_compress_chunked(sp))
+    except kvc.KvcError as e:
+        log(f"immediate eviction {name} with the fused-selection flag: {e}")
+        fsel_us = None
     ov = torch.empty(cfg.hkv, dtype=torch.float32, device=dev)
     kvc.kvc_overlap_coefficient(desc, pos.view(-1), lout.idx, budgets, ov)
     torch.cuda.synchronize()
@@ -235,10 +247,13 @@ def immediate_eviction(kvc, torch, dev, name, reps, sp, stream):
            "immediate_over_layer_end": round(imm_us / del_us, 3),
            "retained_overlap_mean": round(float(ov.mean().item()), 4),
            "alg_bytes_per_layer": alg, "hbm_frac": round(alg / (imm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "fused_select_us_per_layer": round(fsel_us, 2) if fsel_us else None,
+           "fused_select_us_per_boundary": round(fsel_us / n_chunks, 2) if fsel_us else None,
            "entry_points": ["kvc_compress_chunked", "kvc_compress_layer"]}
     log(f"immediate eviction {name}: {imm_us:.1f} us/layer over {n_chunks} boundaries "
         f"({imm_us / n_chunks:.2f} us each; wall {imm_wall:.1f} us) vs layer-end {del_us:.1f} us "
-        f"({imm_us / del_us:.2f}x); retained-set overlap {out['retained_overlap_mean']:.3f}")
+        f"({imm_us / del_us:.2f}x); retained-set overlap {out['retained_overlap_mean']:.3f}; with the "
+        f"fused-selection flag " + (f"{fsel_us:.1f} us/layer ({fsel_us / n_chunks:.2f} us each)" if fsel_us else "n/a"))
     return out
 
 

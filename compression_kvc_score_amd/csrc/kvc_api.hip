@@ -327,6 +327,14 @@ int reject_fsel(const Layer& L, const char* what) {
   return fail(KVC_ERR_INVALID_ARG, "%s does not take KVC_FLAG_FUSED_SELECT (kvc_compress_layer does)", what);
 }
 
+// With KVC_FLAG_FUSED_SELECT a layer runs as one launch whose workgroups must
+// all be resident at once: checked before anything is enqueued.
+int check_fused_fits(const Layer& L) {
+  if (!L.fsel || use_fused_scans(L)) return KVC_OK;
+  return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: the %d workgroups of the fused launch do not fit "
+              "the device at once", L.hkv * L.n_split);
+}
+
 int check_ws(const Layer& L, const void* ws, size_t ws_bytes) {
   const size_t need = ws_layout(L).total;
   if (ws == nullptr) return fail(KVC_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
@@ -1088,7 +1096,6 @@ int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k
                     kvc_stream_t stream) {
   Layer Lc;
   KVC_TRY(normalize(desc, Lc));
-  KVC_TRY(reject_fsel(Lc, "kvc_evict_chunk"));
   if (budget < 0) return fail(KVC_ERR_INVALID_ARG, "budget=%d < 0", budget);
   if (n_kept < 0) return fail(KVC_ERR_INVALID_ARG, "n_kept=%lld < 0", (long long)n_kept);
   if (cap < n_kept + Lc.s || cap > kMaxPrompt)
@@ -1104,6 +1111,7 @@ int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k
     Layer La;
     KVC_TRY(arena_layer(desc, n_kept + Lc.s, cap, La));
     KVC_TRY(check_boundary(La, budget, cap));
+    KVC_TRY(check_fused_fits(La));
     KVC_TRY(check_arena(next, "next"));
     if (next.k == cur.k || next.v == cur.v || next.pos == cur.pos)
       return fail(KVC_ERR_INVALID_ARG, "the next arena must not be the current one");
@@ -1158,7 +1166,6 @@ int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* 
                          size_t ws_bytes, kvc_stream_t stream) {
   Layer L;
   KVC_TRY(normalize(desc, L));
-  KVC_TRY(reject_fsel(L, "kvc_compress_chunked"));
   ChunkedPlan p;
   KVC_TRY(chunked_plan(desc, chunk, budget, p));
   KVC_TRY(check_ptr(q_windows, 16, "q_windows"));
@@ -1196,7 +1203,8 @@ int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* 
     if (squeeze[(size_t)b]) {
       Layer La;
       KVC_TRY(arena_layer(&cd, s_acc, p.cap, La));
-      const int st = check_boundary(La, budget, p.cap);
+      int st = check_boundary(La, budget, p.cap);
+      if (st == KVC_OK) st = check_fused_fits(La);
       if (st != KVC_OK) return fail(st, "chunk %lld: %s", (long long)b, g_last_error.c_str());
       las.push_back(La);
     }

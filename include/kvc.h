@@ -142,7 +142,8 @@ typedef struct kvc_layer_desc {
 
 /*
  * KVC_FLAG_FUSED_SELECT: kvc_compress_layer (and its _noalloc variant and
- * kvc_compress_layers) run both scans, the selection and the gather as ONE
+ * kvc_compress_layers), and every evicting boundary of kvc_evict_chunk and
+ * kvc_compress_chunked, run both scans, the selection and the gather as ONE
  * launch in which every workgroup keeps its key segment's scores on chip, so
  * the workspace does not grow with s at all and no fp32 score vector goes to
  * device memory unless scores_out asks for it (TideKV, Fig. 3 caption:
@@ -154,8 +155,9 @@ typedef struct kvc_layer_desc {
  * last bits. Needs softmax scores, pool 1, G * W <= 128,
  * at most 4096 keys of a head per workgroup (s up to about 128K with 8 KV
  * heads on a 256-CU device) and a device whose compute units hold the whole
- * launch at once; else KVC_ERR_UNSUPPORTED. The staged entry points and the
- * chunk-boundary calls reject the flag (KVC_ERR_INVALID_ARG).
+ * launch at once; else KVC_ERR_UNSUPPORTED (the chunk-boundary calls check
+ * every boundary before they enqueue anything). The staged entry points
+ * reject the flag (KVC_ERR_INVALID_ARG).
  */
 #define KVC_FLAG_FUSED_SELECT 1
 

@@ -487,9 +487,9 @@ def test_fused_select_flag_is_validated():
 
 
 def test_staged_entry_points_reject_the_fused_select_flag():
-    """The staged calls and the chunk-boundary calls keep the s-length score
-    vector or the staged selection's bookkeeping in their contract: they
-    reject the flag before anything else touches the arguments."""
+    """The staged calls keep the s-length score vector or the staged
+    selection's bookkeeping in their contract: they reject the flag before
+    anything else touches the arguments."""
     lib = kvc.lib()
     d = base_desc(s=65536, flags=FSEL)
     dd = ctypes.byref(d)
@@ -504,3 +504,36 @@ def test_staged_entry_points_reject_the_fused_select_flag():
     for name, call in calls.items():
         assert call() == kvc.KVC_ERR_INVALID_ARG, name
         assert name in lib.kvc_last_error().decode() and "FUSED_SELECT" in lib.kvc_last_error().decode()
+
+
+def test_boundary_calls_take_the_fused_select_flag_and_check_the_launch_first():
+    """The chunk-boundary calls take the flag: a boundary's workspace then
+    holds no score vector, and each evicting boundary is checked to fit the
+    device as one launch before anything is enqueued (here, with no device,
+    it does not: KVC_ERR_UNSUPPORTED before any HIP call)."""
+    import os
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present: the launch could fit")
+    lib = kvc.lib()
+    chunk, budget = 2048, 4096
+    cap = budget + chunk
+    d = base_desc(s=chunk, flags=FSEL)
+    plain = base_desc(s=chunk)
+    n = kvc.kvc_chunk_workspace_size(d, cap)
+    assert n > 0
+    # the flagged boundary workspace grows with the arena by its index rows
+    # only; the unflagged one also by the score vector and the selection's
+    # per-key bookkeeping
+    grow = kvc.kvc_chunk_workspace_size(d, 4 * cap) - n
+    assert grow == 8 * 3 * cap * 4
+    assert kvc.kvc_chunk_workspace_size(plain, 4 * cap) - kvc.kvc_chunk_workspace_size(plain, cap) >= grow + 8 * 3 * cap * 4
+    P = _fake(0x10000)
+    st = lib.kvc_evict_chunk(ctypes.byref(d), P, P, P, budget, budget, cap, P, P, P,
+                             _fake(0x20000), _fake(0x30000), _fake(0x40000), P, n, None)
+    assert st == kvc.KVC_ERR_UNSUPPORTED and "FUSED_SELECT" in lib.kvc_last_error().decode()
+    # a boundary that does not evict is only an append: the flag changes nothing there
+    whole = base_desc(s=65536, flags=FSEL)
+    nw = kvc.kvc_chunked_workspace_size(whole, chunk, budget)
+    assert nw > 0
+    st = lib.kvc_compress_chunked(ctypes.byref(whole), chunk, P, P, P, budget, P, P, P, P, nw, None)
+    assert st == kvc.KVC_ERR_UNSUPPORTED and "chunk 2" in lib.kvc_last_error().decode()

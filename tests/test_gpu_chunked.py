@@ -31,6 +31,7 @@ from gpu_util import from_dev_bits, to_dev_bf16  # noqa: E402
 from parity import assert_scores_close, assert_selection_matches  # noqa: E402
 
 MODES = {"softmax": kvc.KVC_SCORE_SOFTMAX, "logit": kvc.KVC_SCORE_LOGIT, "int8": kvc.KVC_SCORE_LOGIT_INT8}
+FSEL = kvc.KVC_FLAG_FUSED_SELECT
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -44,11 +45,11 @@ def say(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-def chunk_desc(cfg, c, pos_offset, mode, pool):
+def chunk_desc(cfg, c, pos_offset, mode, pool, flags=0):
     hq, hkv, d = cfg.hq, cfg.hkv, cfg.d
     return kvc.make_desc(c, cfg.w, hq, hkv, d, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
                          pool=pool, pos_offset=pos_offset, score_mode=MODES[mode],
-                         q_strides=(hq * d, d), k_strides=(hkv * d, d), v_strides=(hkv * d, d))
+                         q_strides=(hq * d, d), k_strides=(hkv * d, d), v_strides=(hkv * d, d), flags=flags)
 
 
 def gpu_arena_scores(cfg, q_win, arena, s_acc, cap, mode):
@@ -120,15 +121,18 @@ def check_boundary_selection(cfg, mode, pool, budget, gs, ws_, err, k_acc, g):
     return got, not np.array_equal(got, want)
 
 
-def run_chain(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
+def run_chain(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0, flags=0):
     """kvc_evict_chunk boundary by boundary, each boundary checked; returns
     the final (K rows [hkv, n, d], V rows, positions [hkv, n]) and whether any
-    boundary's selection differed from the oracle's own."""
+    boundary's selection differed from the oracle's own. With the fused-
+    selection flag a boundary's scores stay on chip: its retained set is then
+    checked against the oracle's (tie band), rows and positions against the
+    arena."""
     chunk, s, w, hkv, d = cfg.chunk, cfg.s, cfg.w, cfg.hkv, cfg.d
     cap = min(budget + chunk, s)
     k_dev, v_dev, qw_dev = to_dev_bf16(x.k), to_dev_bf16(x.v), to_dev_bf16(qw_bits)
     arenas = [kvc.alloc_arena(hkv, cap, d), kvc.alloc_arena(hkv, cap, d)]
-    ws = torch.empty(kvc.kvc_chunk_workspace_size(chunk_desc(cfg, min(chunk, s), pos_offset, mode, pool), cap),
+    ws = torch.empty(kvc.kvc_chunk_workspace_size(chunk_desc(cfg, min(chunk, s), pos_offset, mode, pool, flags), cap),
                      dtype=torch.uint8, device="cuda")
     cur, n_kept, flipped = 0, 0, False
     kept_k = np.zeros((hkv, 0, d), np.uint16)
@@ -136,7 +140,7 @@ def run_chain(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
     kept_p = np.zeros((hkv, 0), np.int32)
     for b, (c0, c1) in enumerate(oracle.chunk_bounds(s, chunk)):
         c, s_acc = c1 - c0, n_kept + c1 - c0
-        desc = chunk_desc(cfg, c, pos_offset + c0, mode, pool)
+        desc = chunk_desc(cfg, c, pos_offset + c0, mode, pool, flags)
         q_win = qw_dev[b * w:(b + 1) * w]
         evict = s_acc > budget
         kvc.kvc_evict_chunk(desc, q_win, k_dev[c0:c1], v_dev[c0:c1], budget, n_kept, cap, arenas[cur],
@@ -171,7 +175,15 @@ def run_chain(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
         nv = from_dev_bits(arenas[1 - cur][1])[:, :budget]
         npos = arenas[1 - cur][2].cpu().numpy()[:, :budget]
         for g in range(hkv):
-            got, diff = check_boundary_selection(cfg, mode, pool, budget, gs, want, err, k_acc, g)
+            if flags & FSEL:
+                got = np.searchsorted(ap[g], npos[g])
+                assert np.all(got < s_acc) and np.array_equal(ap[g, np.minimum(got, s_acc - 1)], npos[g]), \
+                    f"chunk {b} head {g}: retained positions not among the accumulated keys"
+                own = oracle.select_head(want[g], budget, cfg.n_sink, cfg.n_recent)
+                assert_selection_matches(got, own, want[g], budget, cfg.n_sink, cfg.n_recent)
+                diff = not np.array_equal(got, own)
+            else:
+                got, diff = check_boundary_selection(cfg, mode, pool, budget, gs, want, err, k_acc, g)
             flipped |= diff
             np.testing.assert_array_equal(nk[g], ak[g, got], err_msg=f"chunk {b} head {g}: retained K rows")
             np.testing.assert_array_equal(nv[g], av[g, got])
@@ -181,10 +193,10 @@ def run_chain(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
     return kept_k, kept_v, kept_p, flipped
 
 
-def run_driver(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
+def run_driver(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0, flags=0):
     hq, hkv, d = cfg.hq, cfg.hkv, cfg.d
     desc = kvc.make_desc(cfg.s, cfg.w, hq, hkv, d, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
-                         pool=pool, pos_offset=pos_offset, score_mode=MODES[mode])
+                         pool=pool, pos_offset=pos_offset, score_mode=MODES[mode], flags=flags)
     rows = min(budget, cfg.s)
     k_out = torch.empty((hkv, rows, d), dtype=torch.bfloat16, device="cuda")
     v_out = torch.empty_like(k_out)
@@ -196,13 +208,13 @@ def run_driver(cfg, x, qw_bits, budget, mode="softmax", pool=1, pos_offset=0):
     return from_dev_bits(k_out), from_dev_bits(v_out), pos.cpu().numpy()
 
 
-def check_case(cfg, budget, mode="softmax", pool=1, pos_offset=0, layer=0):
+def check_case(cfg, budget, mode="softmax", pool=1, pos_offset=0, layer=0, flags=0):
     x = layer_inputs(cfg, layer)
     qw = chunk_windows(cfg, cfg.chunk, layer, q_last=x.q)
-    say(f"chunked {cfg.name} s={cfg.s} C={cfg.chunk} budget={budget} {mode} pool={pool}: chain")
-    ck, cv, cp, flipped = run_chain(cfg, x, qw, budget, mode, pool, pos_offset)
+    say(f"chunked {cfg.name} s={cfg.s} C={cfg.chunk} budget={budget} {mode} pool={pool} flags={flags}: chain")
+    ck, cv, cp, flipped = run_chain(cfg, x, qw, budget, mode, pool, pos_offset, flags)
     say("  driver")
-    dk, dv, dp = run_driver(cfg, x, qw, budget, mode, pool, pos_offset)
+    dk, dv, dp = run_driver(cfg, x, qw, budget, mode, pool, pos_offset, flags)
     np.testing.assert_array_equal(dk, ck, err_msg="driver K differs from the boundary chain")
     np.testing.assert_array_equal(dv, cv)
     np.testing.assert_array_equal(dp, cp)
@@ -279,3 +291,31 @@ def test_chunked_table8_setting_full_size():
     prompt, 512-token chunks, 1024 keys per head, every boundary checked."""
     cfg = get_config("llama8b_16k_imm")
     check_case(cfg, cfg.budget)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_chunk_over_budget", "gqa_3000"])
+def test_chunked_fused_select(name):
+    """With KVC_FLAG_FUSED_SELECT every evicting boundary is one launch
+    (scans, selection and gather, the scores kept on chip): each boundary's
+    retained set is the oracle's up to the tie band with rows and positions
+    carried from the arena, the whole-prompt driver equals the boundary chain
+    bit for bit, and with one KV head (one head per workgroup either way) the
+    result equals the unflagged path's bit for bit."""
+    c = SMALL[name]
+    base, kw = c["cfg"]
+    cfg = get_config(base).with_(**kw)
+    check_case(cfg, c["budget"], flags=FSEL)
+    if cfg.hkv == 1:
+        x = layer_inputs(cfg, 0)
+        qw = chunk_windows(cfg, cfg.chunk, 0, q_last=x.q)
+        plain = run_driver(cfg, x, qw, c["budget"])
+        fused = run_driver(cfg, x, qw, c["budget"], flags=FSEL)
+        for a, b in zip(plain, fused):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_chunked_fused_select_table8_setting_full_size():
+    """The Block-SnapKV setting the benchmark times, every boundary as one
+    launch with the scores on chip, every boundary checked."""
+    cfg = get_config("llama8b_16k_imm")
+    check_case(cfg, cfg.budget, flags=FSEL)
