@@ -327,3 +327,19 @@ def test_positions_at_the_int32_limit():
     np.testing.assert_array_equal(fu["pos"].astype(np.int64), idx + off)
     np.testing.assert_array_equal(st["pos"], fu["pos"])
     assert int(fu["pos"].max()) == (1 << 31) - 2  # head 1 keeps every key, the last at 2^31 - 2
+
+
+FSEL_CHUNKED = [i for i, c in enumerate(CHUNKED) if c["pool"] == 1 and c["mode"] == "softmax"]
+
+
+@pytest.mark.parametrize("i", FSEL_CHUNKED)
+def test_random_immediate_eviction_fused_select(i):
+    """The random softmax boundary chains again with KVC_FLAG_FUSED_SELECT
+    (every evicting boundary one launch, the scores kept on chip): every
+    boundary's retained set within the tie band of the oracle's, the
+    whole-prompt call equal to the chain."""
+    from test_gpu_chunked import FSEL, check_case
+    c = dict(CHUNKED[i])
+    budget, pool, pos_offset, mode, seed = c.pop("budget"), c.pop("pool"), c.pop("pos_offset"), c.pop("mode"), c.pop("seed")
+    cfg = get_config("tiny").with_(name=f"random_chunked_fsel_{i}", sink_scale=4.0, seed_base=seed, budget=budget, **c)
+    check_case(cfg, budget, mode=mode, pool=pool, pos_offset=pos_offset, flags=FSEL)
