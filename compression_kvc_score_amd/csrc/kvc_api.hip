@@ -207,16 +207,21 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   if (L.fsel) {
     if (L.score_mode != KVC_SCORE_SOFTMAX || L.pool != 1)
       return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT needs softmax scores and pool 1");
-    if (L.row_tiles > 4 || !stream_offsets_fit(L, 1))
-      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT needs G*W <= 128 and the streaming scans");
-    // the fused kernel's wavefronts split a head's row tiles into row groups
-    // of equal size, at most two tiles each: pad to that (padding rows are
-    // masked like the ones past G*W in the last tile)
+    const bool wide = L.d == 128 && L.row_tiles <= kStreamMaxRowTiles;
+    if ((L.row_tiles > 4 && !wide) || !stream_offsets_fit(L, 1))
+      return fail(KVC_ERR_UNSUPPORTED,
+                  "KVC_FLAG_FUSED_SELECT needs G*W <= 128 (192 with d=128) and the streaming scans");
+    // up to four tiles, the fused kernel's wavefronts split a head's row
+    // tiles into row groups of equal size, at most two tiles each: pad to
+    // that (padding rows are masked like the ones past G*W in the last
+    // tile); five and six take the three-tile loops as they are
     const int rs = stream_row_groups(L.d, 1);
-    L.row_tiles = (L.row_tiles + rs - 1) / rs * rs;
-    if (L.row_tiles / rs > 2)
-      return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: %d query rows per KV head > %d with d=%d",
-                  L.rows, 64 * rs, L.d);
+    if (L.row_tiles <= 4) {
+      L.row_tiles = (L.row_tiles + rs - 1) / rs * rs;
+      if (L.row_tiles / rs > 2)
+        return fail(KVC_ERR_UNSUPPORTED, "KVC_FLAG_FUSED_SELECT: %d query rows per KV head > %d with d=%d",
+                    L.rows, 64 * rs, L.d);
+    }
     L.stream_hg = 1;
   } else if ((L.row_tiles <= 4 || (L.d == 128 && L.row_tiles <= kStreamMaxRowTiles)) && stream_scans_enabled()) {
     if (L.hkv % 2 == 0 && stream_offsets_fit(L, 2)) L.stream_hg = 2;

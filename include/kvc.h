@@ -152,7 +152,7 @@ typedef struct kvc_layer_desc {
  * kvc_gather_retained make of the same call's scores; a workgroup scans one
  * KV head, so pass 1's partials merge in another order than the unflagged
  * path's when hkv is even and m, Z and the scores then differ from its in the
- * last bits. Needs softmax scores, pool 1, G * W <= 128,
+ * last bits. Needs softmax scores, pool 1, G * W <= 128 (192 with D = 128),
  * at most 4096 keys of a head per workgroup (s up to about 128K with 8 KV
  * heads on a 256-CU device) and a device whose compute units hold the whole
  * launch at once; else KVC_ERR_UNSUPPORTED (the chunk-boundary calls check

@@ -472,12 +472,15 @@ def test_fused_select_flag_is_validated():
     with pytest.raises(kvc.KvcError):
         kvc.kvc_plan_layer(d)
     for kw in (dict(pool=7), dict(score_mode=kvc.KVC_SCORE_LOGIT), dict(w=64),  # 256 rows per KV head
+               dict(hq=40, d=64),  # 160 rows per KV head take D = 128
                dict(s=1 << 20)):  # 32768 keys of a head per workgroup
         d = base_desc(**dict(dict(s=65536, flags=FSEL), **kw))
         with pytest.raises(kvc.KvcError) as e:
             kvc.kvc_plan_layer(d)
         assert e.value.status == kvc.KVC_ERR_UNSUPPORTED, kw
         assert "FUSED_SELECT" in str(e.value)
+    for hq in (40, 48):  # 160 and 192 rows per KV head at D = 128
+        assert kvc.kvc_plan_layer(base_desc(s=65536, hq=hq, flags=FSEL)).heads_per_wg == 1
     p = kvc.kvc_plan_layer(base_desc(s=131072, flags=FSEL))
     assert p.scan == kvc.KVC_SCAN_STREAM and p.heads_per_wg == 1 and p.keys_per_wg <= 4096
     assert p.hist_in_scan == 1

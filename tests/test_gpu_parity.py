@@ -589,6 +589,9 @@ FSEL_CASES = [
     ("llama8b_16k", {"s": 9000}, "mixed"),
     ("llama8b_64k", {}, None),
     ("llama8b_64k", {"s": 131072}, None),
+    # 160 and 192 query rows per KV head (five and six row tiles)
+    ("qwen14b_hetero_64k", {"s": 9000}, None),
+    ("llama8b_16k", {"s": 7001, "hq": 48, "hkv": 8, "w": 32}, "mixed"),
 ]
 
 
