@@ -357,28 +357,49 @@ def layer_sweep(kvc, torch, dev, name, sp, stream):
         preps.append(kvc.PreparedLayer(desc, q, k, v, budgets, o, ws))
     log(f"{name}: generated {cfg.layers} layers ({time.perf_counter() - t0:.0f} s)")
     arena = sum(p._keep[3].k_hat.nbytes + p._keep[3].v_hat.nbytes for p in preps)
-    preps[-1].kvc_compress_layer(sp)  # warm (the last layer; the sweep starts at the first)
-    torch.cuda.synchronize()
-    evs = []
-    for p in preps:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        p.kvc_compress_layer(sp)
-        e1.record(stream)
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+    def sweep(ps):
+        ps[-1].kvc_compress_layer(sp)  # warm (the last layer; the sweep starts at the first)
+        torch.cuda.synchronize()
+        evs = []
+        for p in ps:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            p.kvc_compress_layer(sp)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+    us = sweep(preps)
     med = float(np.median(us))
+    # the same layers with the fused-selection flag (scans, selection and
+    # gather as one launch), into the same retained-cache arena
+    fsel = None
+    try:
+        fpreps, fws = [], None
+        for p in preps:
+            q, k, v, o, _ = p._keep
+            fdesc = kvc.desc_for(q, k, v, block=cfg.block, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool,
+                                 flags=kvc.KVC_FLAG_FUSED_SELECT)
+            if fws is None:
+                fws = kvc.alloc_workspace(fdesc, dev)
+            fpreps.append(kvc.PreparedLayer(fdesc, q, k, v, p._b, o, fws))
+        fsel = _pct(sweep(fpreps))
+        del fpreps, fws
+    except kvc.KvcError as e:
+        log(f"{name} sweep with the fused-selection flag: {e}")
     alg = sum(algorithmic_bytes(cfg, max(rows)).values())
     out = {"s": cfg.s, "w": cfg.w, "hq": cfg.hq, "hkv": cfg.hkv, "layers": cfg.layers,
            "budgets": "inverse stability, total %d per layer" % cfg.total_budget if cfg.hetero else cfg.budget,
            "retained_arena_bytes": arena, "us_per_layer": _pct(us),
            "tokens_per_s": round(cfg.s / (med * 1e-6), 1), "alg_bytes": alg,
            "hbm_frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "scans": _scan_label(kvc, preps[0].desc)}
+           "scans": _scan_label(kvc, preps[0].desc), "fused_select_us_per_layer": fsel}
     log(f"{name} sweep over {cfg.layers} layers: median {med:.1f} us per layer (p10 {out['us_per_layer']['p10']:.1f}, "
         f"p90 {out['us_per_layer']['p90']:.1f}), retained arena {arena / 2**20:.0f} MiB, "
-        f"{out['hbm_frac'] * 100:.1f}% of the HBM peak")
+        f"{out['hbm_frac'] * 100:.1f}% of the HBM peak; with the fused-selection flag "
+        + (f"median {fsel['median']:.1f} us" if fsel else "n/a"))
     del preps, ws
     torch.cuda.empty_cache()
     return out
