@@ -53,15 +53,24 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Workgroups the scans aim for across all KV heads (two per CU on a
-// 256-CU part). Overridable for tuning sweeps.
-int score_wg_target() {
-  static const int v = [] {
+int device_cus();
+
+// Workgroups the per-head softmax scans aim for across all KV heads: as many
+// as the device holds at once (one round; on the 128K-key layer with 256 query
+// rows per KV head, one per CU took 206.8 against 220.8 us per layer for two
+// per CU in two rounds), or 512 where the device cannot be asked; 512 for the
+// raw inner-product scan. Overridable for tuning sweeps (KVC_SCORE_WGS).
+int score_wg_target(const Layer& L) {
+  static const int env = [] {
     const char* e = std::getenv("KVC_SCORE_WGS");
     const int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 512;
+    return x > 0 ? x : 0;
   }();
-  return v;
+  if (env > 0) return env;
+  if (L.score_mode != KVC_SCORE_SOFTMAX) return 512;
+  const int cus = device_cus();
+  const int per = cus > 0 ? per_head_wgs_per_cu(L) : 0;
+  return per > 0 ? cus * per : 512;
 }
 
 // Workgroups the streaming scans aim for (one per CU: each uses most of the LDS).
@@ -232,7 +241,7 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   // most kMaxSplit workgroups.
   const int unit = L.stream_hg ? stream_tokens(L.d, L.stream_hg) : L.block;
   const int groups = L.stream_hg ? L.hkv / L.stream_hg : L.hkv;
-  const int target = L.stream_hg ? stream_wg_target() : score_wg_target();
+  const int target = L.stream_hg ? stream_wg_target() : score_wg_target(L);
   L.n_blocks = (int)((L.s + unit - 1) / unit);
   const int64_t min_bpw = (L.n_blocks + kMaxSplit - 1) / kMaxSplit;
   const int64_t want_bpw = ((int64_t)L.n_blocks * groups + target - 1) / target;

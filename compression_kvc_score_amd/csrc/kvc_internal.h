@@ -164,6 +164,9 @@ hipError_t ensure_lds(const void* fn, size_t bytes);
 
 // Launchers (kernels in the .hip files). Each returns the launch status.
 hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st);
+// Workgroups of the per-head scans (the smaller of the two passes) that one
+// compute unit of the current device holds at once; 0 if it cannot be read.
+int per_head_wgs_per_cu(const Layer& L);
 hipError_t launch_combine(const Layer& L, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_pass2(const Layer& L, const ScoreArgs& a, hipStream_t st);
 // need_hist: clear and build the histogram (and pooled values) first;

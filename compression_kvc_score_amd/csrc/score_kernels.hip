@@ -465,6 +465,19 @@ size_t pass2_lds_bytes(const Layer& L) {
   return rows_pad * (L.d + 8) * 2 + rows_pad * sizeof(float) + kHistBins * sizeof(uint32_t);
 }
 
+int per_head_wgs_per_cu(const Layer& L) {
+  const void* f1 = L.d == 128 ? pass1_fn<128>(L.row_tiles) : pass1_fn<64>(L.row_tiles);
+  const void* f2 = L.d == 128 ? pass2_fn<128>(L.row_tiles) : pass2_fn<64>(L.row_tiles);
+  if (f1 == nullptr || f2 == nullptr) return 0;
+  const size_t l1 = pass1_lds_bytes(L), l2 = pass2_lds_bytes(L);
+  if (ensure_lds(f1, l1) != hipSuccess || ensure_lds(f2, l2) != hipSuccess) return 0;
+  const int threads = scan_waves(L) * kWave;
+  int b1 = 0, b2 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, f1, threads, l1) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b2, f2, threads, l2) != hipSuccess) return 0;
+  return std::min(b1, b2);
+}
+
 hipError_t launch_pass1(const Layer& L, const ScoreArgs& a, hipStream_t st) {
   const void* fn = L.d == 128 ? pass1_fn<128>(L.row_tiles) : pass1_fn<64>(L.row_tiles);
   return launch_scan(fn, L, a, pass1_lds_bytes(L), st);
