@@ -177,6 +177,9 @@ EDGE_CASES = {
                         [300, 52], {}),
     "stream_192_rows": (dict(s=2500, w=48, hq=4, hkv=1, d=128, n_sink=4, n_recent=48, n_heavy=12, budget=256),
                         None, {}),
+    # five row tiles with an odd KV-head count (one head per workgroup), a ragged last slot
+    "stream_160_rows_odd_hkv": (dict(s=5003, w=32, hq=15, hkv=3, d=128, n_sink=4, n_recent=32, n_heavy=20,
+                                     budget=700), [700, 37, 5003], {}),
 }
 
 
@@ -592,6 +595,7 @@ FSEL_CASES = [
     # 160 and 192 query rows per KV head (five and six row tiles)
     ("qwen14b_hetero_64k", {"s": 9000}, None),
     ("llama8b_16k", {"s": 7001, "hq": 48, "hkv": 8, "w": 32}, "mixed"),
+    ("llama8b_16k", {"s": 5003, "hq": 15, "hkv": 3, "w": 32}, None),
 ]
 
 
