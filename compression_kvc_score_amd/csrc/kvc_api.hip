@@ -233,7 +233,14 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
     }
     L.stream_hg = 1;
   } else if ((L.row_tiles <= 4 || (L.d == 128 && L.row_tiles <= kStreamMaxRowTiles)) && stream_scans_enabled()) {
-    if (L.hkv % 2 == 0 && stream_offsets_fit(L, 2)) L.stream_hg = 2;
+    // Head pairs (512-byte K segments per token) unless, at D = 128, one head
+    // per workgroup measured faster: five or six row tiles, or a short scan
+    // (at most 8 slots per workgroup), where the rendezvous inside the fused
+    // launch weighs more and a head's workgroups meet within one XCD.
+    const int64_t slots1 = (L.s + stream_tokens(L.d, 1) - 1) / stream_tokens(L.d, 1);
+    const bool short_scan = slots1 * L.hkv <= 8LL * stream_wg_target();
+    const bool prefer_one = L.d == 128 && (L.row_tiles > 4 || short_scan);
+    if (L.hkv % 2 == 0 && !prefer_one && stream_offsets_fit(L, 2)) L.stream_hg = 2;
     else if (stream_offsets_fit(L, 1)) L.stream_hg = 1;
   }
 
