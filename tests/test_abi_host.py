@@ -540,3 +540,19 @@ def test_boundary_calls_take_the_fused_select_flag_and_check_the_launch_first():
     assert nw > 0
     st = lib.kvc_compress_chunked(ctypes.byref(whole), chunk, P, P, P, budget, P, P, P, P, nw, None)
     assert st == kvc.KVC_ERR_UNSUPPORTED and "chunk 2" in lib.kvc_last_error().decode()
+
+
+def test_plan_heads_per_streaming_workgroup():
+    """Head pairs for long scans at D = 128 (the 64K and 128K layers); one head
+    per workgroup for short scans (at most 8 slots per workgroup: 16K, 32K),
+    for five or six row tiles, for an odd KV-head count, and head pairs
+    again at D = 64."""
+    def hpw(**kw):
+        p = kvc.kvc_plan_layer(base_desc(**kw))
+        assert p.scan == kvc.KVC_SCAN_STREAM, kw
+        return p.heads_per_wg
+    assert hpw(s=65536) == 2 and hpw(s=131072) == 2
+    assert hpw(s=16384) == 1 and hpw(s=32768) == 1 and hpw(s=32769) == 2
+    assert hpw(s=65536, hq=40) == 1 and hpw(s=65536, hq=48) == 1
+    assert hpw(s=65536, hq=12, hkv=3) == 1
+    assert hpw(s=16384, d=64) == 2
