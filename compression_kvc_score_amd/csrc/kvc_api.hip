@@ -73,14 +73,18 @@ int score_wg_target(const Layer& L) {
   return per > 0 ? cus * per : 512;
 }
 
-// Workgroups the streaming scans aim for (one per CU: each uses most of the LDS).
+// Workgroups the streaming scans aim for: one per CU of the current device
+// (each uses most of the LDS), 256 where the device cannot be asked.
+// Overridable for tuning sweeps (KVC_STREAM_WGS).
 int stream_wg_target() {
-  static const int v = [] {
+  static const int env = [] {
     const char* e = std::getenv("KVC_STREAM_WGS");
     const int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 256;
+    return x > 0 ? x : 0;
   }();
-  return v;
+  if (env > 0) return env;
+  const int cus = device_cus();
+  return cus > 0 ? cus : 256;
 }
 
 // KVC_STREAM=0 selects the per-head scans everywhere (for comparisons).
