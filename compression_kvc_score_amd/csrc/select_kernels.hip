@@ -212,6 +212,10 @@ constexpr int kSpecEntries = kSpecRounds * kWave - kSlotHdr;
 
 enum ResolveOutcome { kResolved = 0, kNeedLists = 1, kNeedRow = 2 };
 
+// Heads of at most this many chunks resolve with the chunk lists spread over
+// every wavefront slot (two or more 256-word segments per chunk).
+constexpr int kSpreadChunks = kCWaves * kGroupChunks / 2;
+
 // As resolve_from_lists, for heads of at most NG x 16 chunks whose lists all
 // fit in the first 256 words of their slots: the words stay in registers
 // (wavefront w holds chunks 16g + 4w + i, word 64r + lane) and the radix
@@ -320,6 +324,147 @@ __device__ int resolve_in_registers(const SelectArgs& a, const HeadGeom& h, int 
   gt_before = sums[1] + gq[0];
   eq_before = gq[1];
   return kResolved;
+}
+
+// As resolve_in_registers, for heads of few chunks (one group): the 16
+// wavefront slots spread over the head's chunks, slot u reading 256-word
+// segment u / nc of chunk u % nc (up to kMaxSegs per chunk), so that lists
+// longer than one segment stay in registers (at 16K keys the threshold bin's
+// lists run to about 500 entries per chunk). Returns kNeedLists if a list is
+// longer than its chunk's segments (nothing done yet) and kNeedRow if a slot
+// overflowed. It runs in a compaction kernel of its own: folded into the one
+// of the longer prompts, it made those 1-2 us slower.
+template <bool SIGNED, typename OnBstar, int NG = 1, bool SPREAD = true>
+__device__ int resolve_spread(const SelectArgs& a, const HeadGeom& h, int head, int sub,
+                                    const ResolveLds& m, uint32_t& thr, uint32_t& need_eq,
+                                    uint32_t& gt_before, uint32_t& eq_before, OnBstar on_bstar) {
+  using KF = KeyFmt<SIGNED>;
+  constexpr int NW = kCWaves;
+  constexpr int GC = NW * kGroupChunks;  // wavefront slots per group
+  constexpr int SEGW = kSpecRounds * kWave;        // words per segment
+  constexpr int kMaxSegs = kSlotStride / SEGW;     // whole segments inside a slot
+  __shared__ uint32_t s_cn[GC];                    // listed entries per chunk (one group)
+  const int nc = a.n_chunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t* slots = a.slots + (int64_t)head * nc * kSlotStride;
+  static_assert(!SPREAD || NG == 1, "segments spread over one group");
+  // chunk (nc for a slot without one) and segment of slot (g, i)
+#define KVC_SLOT_CHUNK(g, i)                                                                        \
+  (SPREAD ? ((wave * kGroupChunks + (i)) / nc < kMaxSegs ? (wave * kGroupChunks + (i)) % nc : nc) \
+          : ((g) * GC + wave * kGroupChunks + (i) < nc ? (g) * GC + wave * kGroupChunks + (i) : nc))
+#define KVC_SLOT_SEG(i) (SPREAD ? (wave * kGroupChunks + (i)) / nc : 0)
+  uint32_t v[NG][kGroupChunks][kSpecRounds];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = KVC_SLOT_CHUNK(g, i);
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r)
+        v[g][i][r] = c < nc ? slots[(int64_t)c * kSlotStride + KVC_SLOT_SEG(i) * SEGW + r * kWave + lane] : 0u;
+    }
+  // headers (wavefront-uniform, from each chunk's first segment): listed
+  // entries per chunk; candidates above b* in all sub-chunks and in those
+  // before this one; long lists; b* (chunk 0)
+  uint32_t n[NG][kGroupChunks];
+  uint32_t sums[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = KVC_SLOT_CHUNK(g, i);
+      n[g][i] = 0u;
+      if (c < nc && KVC_SLOT_SEG(i) == 0) {
+#pragma unroll
+        for (int q = 0; q < kSubsPerChunk; ++q) {
+          n[g][i] += (uint32_t)__builtin_amdgcn_readlane((int)v[g][i][0], q);
+          const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)v[g][i][0], kSubsPerChunk + q);
+          sums[0] += ab;
+          sums[1] += c * kSubsPerChunk + q < sub ? ab : 0u;
+        }
+        // the words this chunk's slots cover
+        const int segs = SPREAD ? min(kMaxSegs, (GC - 1 - c) / nc + 1) : 1;
+        if (n[g][i] > (uint32_t)(segs * SEGW - kSlotHdr)) sums[2] += n[g][i] > (uint32_t)kSlotCap ? 0x10000u : 1u;
+        if (SPREAD && lane == 0) s_cn[c] = n[g][i];
+      }
+    }
+  if (wave == 0) sums[3] = (uint32_t)__builtin_amdgcn_readlane((int)v[0][0][0], 2 * kSubsPerChunk);
+  if (lane != 0) {  // wavefront-uniform: count once per wavefront
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sums[i] = 0u;
+  }
+  block_sums<NW, 4, true>(sums, m.scratch);  // (its barrier also publishes s_cn)
+  if (sums[2] >= 0x10000u) return kNeedRow;
+  if (sums[2] != 0u) return kNeedLists;
+  const uint32_t bstar = sums[3];
+  on_bstar(bstar);
+  // every slot's entry count: its chunk's (spread: from LDS)
+  if constexpr (SPREAD) {
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i) {
+      const int c = KVC_SLOT_CHUNK(0, i);
+      n[0][i] = c < nc ? s_cn[c] : 0u;
+    }
+  }
+  // index of word (g, i, r) of this lane among its chunk's listed entries
+#define KVC_SLOT_ENTRY(g, i, r) (KVC_SLOT_SEG(i) * SEGW + (r) * kWave + lane - kSlotHdr)
+
+  // radix over the LOW key bits: the top 10, then the other R2 (the listed
+  // keys share the bits above LOW)
+  uint32_t rem = h.k_sel - sums[0];  // rank of the threshold inside the lists
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = KVC_SLOT_ENTRY(g, i, r);
+        if (e >= 0 && (uint32_t)e < n[g][i]) atomicAdd(&m.hist1[(v[g][i][r] >> KF::R2) & 1023u], 1u);
+      }
+  wg_sync<true>();
+  if (threadIdx.x < kWave) pick_digit_wave<1024>(m.hist1, rem, m.pick);
+  wg_sync<true>();
+  const uint32_t d1 = m.pick[0];
+  rem = m.pick[1];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = KVC_SLOT_ENTRY(g, i, r);
+        if (e >= 0 && (uint32_t)e < n[g][i] && ((v[g][i][r] >> KF::R2) & 1023u) == d1)
+          atomicAdd(&m.hist2[v[g][i][r] & (KF::R2_BINS - 1u)], 1u);
+      }
+  wg_sync<true>();
+  if (threadIdx.x < kWave) pick_digit_wave<KF::R2_BINS>(m.hist2, rem, m.pick);
+  wg_sync<true>();
+  const uint32_t low = (d1 << KF::R2) | m.pick[0];
+  need_eq = m.pick[1];
+  thr = (bstar << KF::LOW) | low;
+  // listed candidates of the sub-chunks before this one
+  uint32_t gq[2] = {0u, 0u};
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kGroupChunks; ++i)
+#pragma unroll
+      for (int r = 0; r < kSpecRounds; ++r) {
+        const int e = KVC_SLOT_ENTRY(g, i, r);
+        const uint32_t x = v[g][i][r];
+        if (e >= 0 && (uint32_t)e < n[g][i] && (int)(x >> KF::LOW) < sub) {
+          gq[0] += (x & KF::LOW_MASK) > low;
+          gq[1] += (x & KF::LOW_MASK) == low;
+        }
+      }
+  block_sums<NW, 2, true>(gq, m.scratch);
+  gt_before = sums[1] + gq[0];
+  eq_before = gq[1];
+  return kResolved;
+#undef KVC_SLOT_ENTRY
+#undef KVC_SLOT_SEG
+#undef KVC_SLOT_CHUNK
 }
 
 // Threshold of one head, resolved from the chunk lists: the pattern T of the
@@ -479,9 +624,10 @@ __device__ void resolve_from_row(const SelectArgs& a, const HeadGeom& h, int hea
 // ---------------------------------------------------------------------------
 // compact: per sub-chunk, resolve the head's threshold, then write the kept
 // indices (and positions) in ascending order from the sub-chunk's first
-// output row; with GATHER also copy their K and V rows.
+// output row; with GATHER also copy their K and V rows. SPREAD: the heads
+// have at most kSpreadChunks chunks, resolved by resolve_spread.
 // ---------------------------------------------------------------------------
-template <bool GATHER, bool SIGNED>
+template <bool GATHER, bool SIGNED, bool SPREAD>
 __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) {
   using KF = KeyFmt<SIGNED>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -555,10 +701,14 @@ __global__ void __launch_bounds__(kCompactThreads) compact_kernel(SelectArgs a) 
     uint32_t need_eq, gt_before, eq_before;
     constexpr int GC = kCWaves * kGroupChunks;
     int outcome = kNeedLists;
-    if (a.n_chunks <= GC)
-      outcome = resolve_in_registers<SIGNED, 1>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
-    else if (a.n_chunks <= 2 * GC)
-      outcome = resolve_in_registers<SIGNED, 2>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+    if constexpr (SPREAD) {
+      outcome = resolve_spread<SIGNED>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+    } else {
+      if (a.n_chunks <= GC)
+        outcome = resolve_in_registers<SIGNED, 1>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+      else if (a.n_chunks <= 2 * GC)
+        outcome = resolve_in_registers<SIGNED, 2>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch);
+    }
     if (outcome == kNeedLists)
       outcome = resolve_from_lists<SIGNED>(a, h, head, sub, m, thr, need_eq, gt_before, eq_before, prefetch)
                     ? kResolved
@@ -692,8 +842,12 @@ hipError_t launch_select_keys(const Layer& L, const SelectArgs& a, bool need_his
   const int want = kCompactTarget / subs;
   args.replicas = a.k == nullptr || want < 1 ? 1 : (want > kMaxReplicas ? kMaxReplicas : want);
   const size_t lds = select_lds_bytes(a.n_chunks, a.n_subs);
-  const void* compact = a.k != nullptr ? reinterpret_cast<const void*>(&compact_kernel<true, SIGNED>)
-                                       : reinterpret_cast<const void*>(&compact_kernel<false, SIGNED>);
+  const bool spread = a.n_chunks <= kSpreadChunks;
+  const void* compact =
+      a.k != nullptr ? (spread ? reinterpret_cast<const void*>(&compact_kernel<true, SIGNED, true>)
+                               : reinterpret_cast<const void*>(&compact_kernel<true, SIGNED, false>))
+                     : (spread ? reinterpret_cast<const void*>(&compact_kernel<false, SIGNED, true>)
+                               : reinterpret_cast<const void*>(&compact_kernel<false, SIGNED, false>));
   e = ensure_lds(compact, lds);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(compact, dim3((unsigned)(subs * args.replicas)), dim3(kCompactThreads), kargs, lds, st);
