@@ -212,9 +212,9 @@ int normalize(const kvc_layer_desc* d, Layer& L) {
   L.v_head = d->v_head_stride ? d->v_head_stride : d->d;
 
   // Streaming scans for up to four query-row tiles per KV head (six at
-  // D = 128); head pairs when the KV heads pair up and a slot's copy offsets
-  // stay in 32 bits. The selection inside the scan launch takes one head per
-  // workgroup.
+  // D = 128); head pairs or one head per workgroup as chosen below, where a
+  // slot's copy offsets stay in 32 bits. The selection inside the scan launch
+  // takes one head per workgroup.
   L.fsel = (d->flags & KVC_FLAG_FUSED_SELECT) != 0;
   L.stream_hg = 0;
   if (L.fsel) {
