@@ -2,8 +2,8 @@
 // counts G*W <= 128, and up to 192 at D = 128 (three row tiles per
 // wavefront): used whenever its register budget allows.
 //
-// A workgroup of 8 wavefronts owns HG KV heads (a head pair when Hkv is even)
-// and a contiguous token range. K flows through a ring of kRingSlots LDS
+// A workgroup of 8 wavefronts owns HG KV heads (a head pair, or one head as
+// the host chooses) and a contiguous token range. K flows through a ring of kRingSlots LDS
 // slots filled by direct global->LDS loads: a slot holds TOKS tokens x HG
 // heads (32 KiB), and every load instruction moves 1 KiB made of whole
 // HG*D*2-byte token segments, so DRAM sees long contiguous runs even though K
