@@ -177,6 +177,12 @@ EDGE_CASES = {
                         [300, 52], {}),
     "stream_192_rows": (dict(s=2500, w=48, hq=4, hkv=1, d=128, n_sink=4, n_recent=48, n_heavy=12, budget=256),
                         None, {}),
+    # the two sides of the head-grouping rule at D = 128: 8 slots of 128 keys per
+    # workgroup (one head each) and one key more (head pairs)
+    "stream_one_head_32768": (dict(s=32768, w=32, hq=32, hkv=8, d=128, n_sink=4, n_recent=32, n_heavy=40,
+                                   budget=2048), None, {}),
+    "stream_head_pairs_32769": (dict(s=32769, w=32, hq=32, hkv=8, d=128, n_sink=4, n_recent=32, n_heavy=40,
+                                     budget=2048), None, {}),
     # five row tiles with an odd KV-head count (one head per workgroup), a ragged last slot
     "stream_160_rows_odd_hkv": (dict(s=5003, w=32, hq=15, hkv=3, d=128, n_sink=4, n_recent=32, n_heavy=20,
                                      budget=700), [700, 37, 5003], {}),
@@ -197,6 +203,10 @@ def test_edge_shapes(name):
         assert plan.scan == kvc.KVC_SCAN_STREAM
         if name.startswith("stream_"):
             assert plan.fused_scans == 1  # the whole-layer call below runs both scans in one launch
+        if name == "stream_one_head_32768":
+            assert plan.heads_per_wg == 1
+        if name == "stream_head_pairs_32769":
+            assert plan.heads_per_wg == 2
     st = run_staged(desc, q, k, v, b)
     check_layer(x, st, b, scale=extra.get("scale"))
     fu = run_fused(desc, q, k, v, b)
