@@ -10,10 +10,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <random>
 #include <string>
-#include <unordered_map>
 #include <vector>
 
 #include "kvc_internal.h"
@@ -787,15 +787,21 @@ namespace kvc {
 
 int record_error(int status, const char* msg) { return fail(status, "%s", msg); }
 
+// Raise a kernel's dynamic LDS limit on the current device (the attribute
+// is set per device), once per (device, kernel) and size.
 hipError_t ensure_lds(const void* fn, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
+  int dev = 0;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return de;
   static std::mutex mu;
-  static std::unordered_map<const void*, size_t> done;
+  static std::map<std::pair<int, const void*>, size_t> done;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = done.find(fn);
+  const std::pair<int, const void*> key(dev, fn);
+  auto it = done.find(key);
   if (it != done.end() && it->second >= bytes) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done[fn] = bytes;
+  if (e == hipSuccess) done[key] = bytes;
   return e;
 }
 
