@@ -4,6 +4,8 @@
 // consecutive threads cover consecutive chunks of a row, so both the reads
 // (one contiguous row segment per key) and the writes are coalesced.
 
+#include <algorithm>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -30,7 +32,9 @@ __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
 // retained so far (TideKV, Fig. 1 caption, schedule (c)); the arena is
 // head-major, so one thread moves one 16-byte chunk of a K row and of the V
 // row, reading the token-major chunk and writing the arena tail coalesced.
-__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+// One launch serves up to two chunks (blockIdx.y picks the chunk).
+__global__ void __launch_bounds__(256) append_kernel(AppendJobs jobs) {
+  const AppendArgs& a = jobs.job[blockIdx.y];
   const int cpr = a.d / 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= a.n * a.hkv * cpr) return;
@@ -48,12 +52,18 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
-  if (a.n == 0) return hipSuccess;
-  AppendArgs args = a;
+hipError_t launch_append(const AppendArgs* jobs, int n_jobs, hipStream_t st) {
+  AppendJobs args{};
+  int n = 0;
+  int64_t threads = 0;
+  for (int i = 0; i < n_jobs && n < 2; ++i) {
+    if (jobs[i].n == 0) continue;
+    args.job[n++] = jobs[i];
+    threads = std::max<int64_t>(threads, jobs[i].n * jobs[i].hkv * (jobs[i].d / 8));
+  }
+  if (n == 0) return hipSuccess;
   void* kargs[] = {&args};
-  const int64_t threads = a.n * a.hkv * (a.d / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n);
   return hipLaunchKernel(reinterpret_cast<const void*>(&append_kernel), grid, dim3(256), kargs, 0, st);
 }
 

@@ -715,12 +715,10 @@ int check_boundary(const Layer& La, int32_t budget, int64_t cap) {
   return KVC_OK;
 }
 
-// Append the chunk to `cur` at row n_kept; with `compress`, score and select
-// the n_kept + c accumulated keys and write the retained rows (positions
-// carried from `cur`) to `out`, head g at row g * out_stride.
-int enqueue_boundary(const Layer& Lc, const kvc_layer_desc* chunk_desc, const void* q_win, const void* k_chunk,
-                     const void* v_chunk, int32_t budget, int64_t n_kept, int64_t cap, const Arena& cur,
-                     bool compress, const Arena& out, int64_t out_stride, void* ws, hipStream_t st) {
+// The append of a chunk (token-major rows of the prompt) to `cur` at row
+// n_kept of every head.
+AppendArgs append_args(const Layer& Lc, const void* k_chunk, const void* v_chunk, int64_t n_kept, int64_t cap,
+                       const Arena& cur) {
   AppendArgs ap{};
   ap.k = static_cast<const uint16_t*>(k_chunk);
   ap.v = static_cast<const uint16_t*>(v_chunk);
@@ -737,8 +735,21 @@ int enqueue_boundary(const Layer& Lc, const kvc_layer_desc* chunk_desc, const vo
   ap.pos0 = Lc.pos_offset;
   ap.hkv = Lc.hkv;
   ap.d = Lc.d;
-  const hipError_t e = launch_append(ap, st);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ap;
+}
+
+// With `append`, append the chunk to `cur` at row n_kept (otherwise the
+// caller has); with `compress`, score and select the n_kept + c accumulated
+// keys and write the retained rows (positions carried from `cur`) to `out`,
+// head g at row g * out_stride.
+int enqueue_boundary(const Layer& Lc, const kvc_layer_desc* chunk_desc, const void* q_win, const void* k_chunk,
+                     const void* v_chunk, int32_t budget, int64_t n_kept, int64_t cap, const Arena& cur,
+                     bool append, bool compress, const Arena& out, int64_t out_stride, void* ws, hipStream_t st) {
+  if (append) {
+    const AppendArgs ap = append_args(Lc, k_chunk, v_chunk, n_kept, cap, cur);
+    const hipError_t e = launch_append(&ap, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
   if (!compress) return KVC_OK;
   Layer La;
   KVC_TRY(arena_layer(chunk_desc, n_kept + Lc.s, cap, La));
@@ -1152,7 +1163,7 @@ int kvc_evict_chunk(const kvc_layer_desc* desc, const void* q_win, const void* k
     if (!aligned(ws, 256)) return fail(KVC_ERR_ALIGN, "workspace not 256-byte aligned");
     KVC_TRY(check_lds(La));
   }
-  return enqueue_boundary(Lc, desc, q_win, k_chunk, v_chunk, budget, n_kept, cap, cur, compress, next, cap, ws,
+  return enqueue_boundary(Lc, desc, q_win, k_chunk, v_chunk, budget, n_kept, cap, cur, true, compress, next, cap, ws,
                           static_cast<hipStream_t>(stream));
 }
 
@@ -1256,18 +1267,44 @@ int kvc_compress_chunked(const kvc_layer_desc* desc, int64_t chunk, const void* 
   const char* qb = static_cast<const char*>(q_windows);
   const char* kb = static_cast<const char*>(k);
   const char* vb = static_cast<const char*>(v);
-  int cur = 0;
-  n_kept = 0;
+  // Where each chunk is appended: the arena that holds the keys retained
+  // before it, behind them.
+  std::vector<int> tgt((size_t)p.n_chunks);
+  std::vector<int64_t> row((size_t)p.n_chunks);
+  {
+    int cur = 0;
+    int64_t kept = 0;
+    for (int64_t b = 0; b < p.n_chunks; ++b) {
+      tgt[(size_t)b] = cur;
+      row[(size_t)b] = kept;
+      if (squeeze[(size_t)b] && b + 1 < p.n_chunks) cur = 1 - cur;
+      kept = std::min<int64_t>(kept + lcs[(size_t)b].s, budget);
+    }
+  }
+  // Chunks 2i and 2i + 1 are appended by one launch before boundary 2i.
+  // Chunk 2i + 1's rows are neither read nor written by boundary 2i: when
+  // that boundary evicts, it reads the other arena and writes only rows
+  // [0, row of chunk 2i + 1) of this one; when it does not, it launches
+  // nothing. Every earlier boundary that read those rows precedes the launch.
   for (int64_t b = 0; b < p.n_chunks; ++b) {
     const Layer& Lc = lcs[(size_t)b];
     const int64_t c0 = b * chunk;
     const bool last = b + 1 == p.n_chunks;
+    if (b % 2 == 0) {
+      AppendArgs jobs[2];
+      int n_jobs = 0;
+      for (int64_t j = b; j < std::min<int64_t>(b + 2, p.n_chunks); ++j)
+        jobs[n_jobs++] = append_args(lcs[(size_t)j], kb + (size_t)(j * chunk * L.k_tok) * 2,
+                                     vb + (size_t)(j * chunk * L.v_tok) * 2, row[(size_t)j], p.cap,
+                                     arenas[tgt[(size_t)j]]);
+      const hipError_t e = launch_append(jobs, n_jobs, st);
+      if (e != hipSuccess) return hip_fail(e, "append launch");
+    }
+    const int cur = tgt[(size_t)b];
     const Arena& out = last ? final_out : arenas[1 - cur];
     KVC_TRY(enqueue_boundary(Lc, &cds[(size_t)b], qb + (size_t)(b * L.w * L.q_tok) * 2, kb + (size_t)(c0 * L.k_tok) * 2,
-                             vb + (size_t)(c0 * L.v_tok) * 2, budget, n_kept, p.cap, arenas[cur], squeeze[(size_t)b],
-                             out, last ? p.rows : p.cap, bws, st));
-    if (squeeze[(size_t)b] && !last) cur = 1 - cur;
-    n_kept = std::min<int64_t>(n_kept + Lc.s, budget);
+                             vb + (size_t)(c0 * L.v_tok) * 2, budget, row[(size_t)b], p.cap, arenas[cur], false,
+                             squeeze[(size_t)b], out, last ? p.rows : p.cap, bws, st));
   }
   return KVC_OK;
 }

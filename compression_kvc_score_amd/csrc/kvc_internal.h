@@ -191,7 +191,12 @@ struct AppendArgs {
   int64_t pos0;
   int hkv, d;
 };
-hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+struct AppendJobs {
+  AppendArgs job[2];
+};
+// Appends up to two chunks (n_jobs of them; jobs with n == 0 are skipped) in
+// one launch; the chunks must not write the same arena rows.
+hipError_t launch_append(const AppendArgs* jobs, int n_jobs, hipStream_t st);
 struct OverlapArgs {
   const int32_t* idx_a;
   const int32_t* idx_b;
