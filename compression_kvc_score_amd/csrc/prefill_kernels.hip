@@ -163,6 +163,18 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluArgs a) {
 // most tiles skip rescaling the output accumulators; lanes that do not raise
 // it scale by exactly 1. Workgroups with the most keys start first.
 // ---------------------------------------------------------------------------
+// x combined with x of lane l ^ 32 through one swap of the wavefront halves
+// in the VALU (a __shfl_xor is an LDS permute round trip); both orders of the
+// operands give the same bits.
+__device__ __forceinline__ float max_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -284,7 +296,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
     float tmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // finite: key 0 is seen by every query
+    tmax = max_other_half(tmax);               // finite: key 0 is seen by every query
     const bool up = tmax > m + thr;            // always on the first tile (m = -inf)
     if (__ballot(up) != 0) {
       const float corr = up ? __builtin_amdgcn_exp2f((m - tmax) * a.c) : 1.0f;
@@ -338,7 +350,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(1, 
     __syncthreads();
   }
 
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = add_other_half(l);
   const float inv = 1.0f / lt;
   if (t0 + l32 < a.n) {
     uint16_t* orow = a.o + ((t0 + l32) * a.hq + h) * D;
