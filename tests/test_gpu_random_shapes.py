@@ -154,6 +154,68 @@ def test_random_shape_score_modes(i, mode):
     np.testing.assert_array_equal(fu["pos"], pos)
 
 
+def random_long_cases(n=12, seed=20261205):
+    """Long prompts (20K-300K keys): several selection chunks per head, both
+    scan designs (up to 256 query rows per KV head), pooling, per-head budgets
+    up to 20K."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 5, 8]))
+        w = int(rng.choice([8, 16, 32, 64]))
+        if g * w > 256:
+            continue
+        s = int(rng.integers(20000, 300000))
+        n_sink = int(rng.integers(0, 9))
+        n_recent = int(rng.integers(0, 65))
+        n_mand = min(n_sink, s) + (s - max(s - n_recent, min(n_sink, s)))
+        budgets = [int(rng.integers(max(n_mand, 1), 20000)) for _ in range(hkv)]
+        cases.append(dict(s=s, w=w, hq=g * hkv, hkv=hkv, d=d, block=int(64 * rng.integers(1, 9)),
+                          n_sink=n_sink, n_recent=n_recent, n_heavy=int(rng.integers(0, 1 + s // 200)),
+                          pool=int(rng.choice([1, 1, 3, 7])), budgets=budgets, seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+LONG = random_long_cases()
+
+
+@pytest.mark.parametrize("i", range(len(LONG)))
+def test_random_long_prompt(i):
+    """A long random prompt through the whole-layer call against the oracle
+    on its first and last KV head (the fp64 dense softmax over every key);
+    where the plan allows the fused-selection flag, the flagged call's
+    retained set and rows equal the staged selection of its own scores bit
+    for bit and pass the same oracle check."""
+    from test_gpu_parity import _fused_select_run, _staged_select
+    c = dict(LONG[i])
+    budgets = np.asarray(c.pop("budgets"), dtype=np.int64)
+    seed = c.pop("seed")
+    cfg = get_config("tiny").with_(name=f"random_long_{i}", sink_scale=4.0, seed_base=seed, budget=int(budgets[0]), **c)
+    print(f"long prompt {i}: s={cfg.s} w={cfg.w} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} block={cfg.block} "
+          f"sink={cfg.n_sink} recent={cfg.n_recent} pool={cfg.pool} budgets={list(budgets)}", flush=True, file=sys.stderr)
+    x = layer_inputs(cfg, 0)
+    q, k, v = dev_inputs(x)
+    heads = sorted({0, cfg.hkv - 1})
+    desc = desc_from(cfg, q, k, v)
+    check_layer(x, run_fused(desc, q, k, v, budgets), budgets, heads=heads)
+    if cfg.pool != 1:
+        return
+    fdesc = desc_from(cfg, q, k, v, flags=kvc.KVC_FLAG_FUSED_SELECT)
+    try:
+        plan = kvc.kvc_plan_layer(fdesc)
+    except RuntimeError:
+        return  # the flag does not take this shape (the host says why)
+    if plan.fused_select != 1:
+        return
+    got, out = _fused_select_run(fdesc, q, k, v, budgets)
+    sel = _staged_select(desc, q, k, v, out.scores, budgets)
+    for key in ["idx", "k_hat", "v_hat", "pos"]:
+        np.testing.assert_array_equal(got[key], sel[key], err_msg=f"fused selection: {key}")
+    check_layer(x, got, budgets, heads=heads)
+
+
 def random_chunked_cases(n=10, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
